@@ -1,0 +1,183 @@
+"""CPU oracle for the SVDQuant W4A4 linear and the AWQ W4A16 linear.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check in __graft_entry__ and
+the cpu_baseline leg of bench.py may import this module.  The product path
+(the HIP library and its Python binding) never imports it.
+
+Every function here is a thin numpy <-> ctypes marshalling layer over
+svdq_oracle.cpp; the arithmetic, and its citations of the pages, live there.
+Arrays are numpy: bf16 and fp16 values travel as their uint16 bit patterns,
+E4M3 scales as uint8, 4-bit codes as packed uint8 [rows, K/2].
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+INT4, NVFP4 = 0, 1
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _LIB = ctypes.CDLL(_build.LIB)
+    return _LIB
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _i64(v):
+    return ctypes.c_int64(int(v))
+
+
+# ---- converters -------------------------------------------------------------
+def _vec(name, arr, out_dtype):
+    arr = np.ascontiguousarray(arr)
+    out = np.empty(arr.shape, dtype=out_dtype)
+    getattr(_lib(), name)(_p(arr), _p(out), _i64(arr.size))
+    return out
+
+
+def f32_to_f16_sat(x):
+    return _vec("orc_vec_f32_to_f16_sat", np.asarray(x, np.float32), np.uint16)
+
+
+def f32_to_bf16(x):
+    return _vec("orc_vec_f32_to_bf16", np.asarray(x, np.float32), np.uint16)
+
+
+def f32_to_e4m3_sat(x):
+    return _vec("orc_vec_f32_to_e4m3_sat", np.asarray(x, np.float32), np.uint8)
+
+
+def f32_to_e2m1_sat(x):
+    return _vec("orc_vec_f32_to_e2m1_sat", np.asarray(x, np.float32), np.uint8)
+
+
+def f16_to_f32(h):
+    return _vec("orc_vec_f16_to_f32", np.asarray(h, np.uint16), np.float32)
+
+
+def bf16_to_f32(h):
+    return _vec("orc_vec_bf16_to_f32", np.asarray(h, np.uint16), np.float32)
+
+
+def e4m3_to_f32(b):
+    return _vec("orc_vec_e4m3_to_f32", np.asarray(b, np.uint8), np.float32)
+
+
+def e2m1_to_f32(c):
+    return _vec("orc_vec_e2m1_to_f32", np.asarray(c, np.uint8), np.float32)
+
+
+# ---- the method ---------------------------------------------------------------
+def quantize_act(prec, x, lam=None, alpha=1.0, nthreads=0):
+    """Returns (codes u8 [M, K/2], scales) for bf16 bits x [M, K]."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    M, K = x.shape
+    lam = None if lam is None else np.ascontiguousarray(lam, dtype=np.uint16)
+    codes = np.zeros((M, K // 2), np.uint8)
+    if prec == INT4:
+        scales = np.zeros((M, K // 64), np.uint16)
+        _lib().orc_quantize_act_int4(_i64(M), _i64(K), _p(x), _p(lam), _p(codes), _p(scales),
+                                     ctypes.c_int(nthreads))
+    else:
+        scales = np.zeros((M, K // 16), np.uint8)
+        _lib().orc_quantize_act_nvfp4(_i64(M), _i64(K), _p(x), _p(lam), ctypes.c_float(alpha),
+                                      _p(codes), _p(scales), ctypes.c_int(nthreads))
+    return codes, scales
+
+
+def lowrank_down(x, l1t, nthreads=0):
+    """XL1 fp32 [M, r] from bf16 bits x [M, K] and l1t = L1^T [r, K]."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    l1t = np.ascontiguousarray(l1t, dtype=np.uint16)
+    M, K = x.shape
+    r = l1t.shape[0]
+    out = np.zeros((M, r), np.float32)
+    if r:
+        _lib().orc_lowrank_down(_i64(M), _i64(K), ctypes.c_int(r), _p(x), _p(l1t), _p(out),
+                                ctypes.c_int(nthreads))
+    return out
+
+
+def group_psums(prec, a_codes, w_codes, nthreads=0):
+    a_codes = np.ascontiguousarray(a_codes, dtype=np.uint8)
+    w_codes = np.ascontiguousarray(w_codes, dtype=np.uint8)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    G = 64 if prec == INT4 else 16
+    out = np.zeros((M, N, K // G), np.int32 if prec == INT4 else np.float32)
+    _lib().orc_group_psums(ctypes.c_int(prec), _i64(M), _i64(N), _i64(K), _p(a_codes),
+                           _p(w_codes), _p(out), ctypes.c_int(nthreads))
+    return out
+
+
+def w4a4_linear(prec, a_codes, a_scales, w_codes, w_scales, xl1=None, l2t=None, bias=None,
+                alpha_a=1.0, alpha_w=1.0, rows=None, cols=None, nthreads=0):
+    """Returns (y float64, y_bf16 uint16): full [M, N], or at (rows[i], cols[i])."""
+    a_codes = np.ascontiguousarray(a_codes, dtype=np.uint8)
+    w_codes = np.ascontiguousarray(w_codes, dtype=np.uint8)
+    a_scales = np.ascontiguousarray(a_scales)
+    w_scales = np.ascontiguousarray(w_scales)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    r = 0 if l2t is None else l2t.shape[1]
+    if r:
+        xl1 = np.ascontiguousarray(xl1, dtype=np.float32)
+        l2t = np.ascontiguousarray(l2t, dtype=np.uint16)
+        assert xl1.shape == (M, r) and l2t.shape == (N, r)
+    bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
+    if rows is None:
+        count = -1
+        y = np.zeros((M, N), np.float64)
+        yb = np.zeros((M, N), np.uint16)
+        ri = ci = None
+    else:
+        ri = np.ascontiguousarray(rows, dtype=np.int64)
+        ci = np.ascontiguousarray(cols, dtype=np.int64)
+        count = ri.size
+        y = np.zeros(count, np.float64)
+        yb = np.zeros(count, np.uint16)
+    _lib().orc_w4a4_linear(ctypes.c_int(prec), ctypes.c_int(r), _i64(M), _i64(N), _i64(K),
+                           _p(a_codes), _p(a_scales), ctypes.c_float(alpha_a),
+                           _p(w_codes), _p(w_scales), ctypes.c_float(alpha_w),
+                           _p(xl1 if r else None), _p(l2t if r else None), _p(bias),
+                           _i64(count), _p(ri), _p(ci), _p(y), _p(yb), ctypes.c_int(nthreads))
+    return y, yb
+
+
+def awq_linear(x, w_codes, w_scales, w_zeros, bias=None, rows=None, cols=None, nthreads=0):
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    w_codes = np.ascontiguousarray(w_codes, dtype=np.uint8)
+    w_scales = np.ascontiguousarray(w_scales, dtype=np.uint16)
+    w_zeros = np.ascontiguousarray(w_zeros, dtype=np.uint16)
+    bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
+    M, K = x.shape
+    N = w_codes.shape[0]
+    if rows is None:
+        count = -1
+        y = np.zeros((M, N), np.float64)
+        yb = np.zeros((M, N), np.uint16)
+        ri = ci = None
+    else:
+        ri = np.ascontiguousarray(rows, dtype=np.int64)
+        ci = np.ascontiguousarray(cols, dtype=np.int64)
+        count = ri.size
+        y = np.zeros(count, np.float64)
+        yb = np.zeros(count, np.uint16)
+    _lib().orc_awq_linear(_i64(M), _i64(N), _i64(K), _p(x), _p(w_codes), _p(w_scales),
+                          _p(w_zeros), _p(bias), _i64(count), _p(ri), _p(ci), _p(y), _p(yb),
+                          ctypes.c_int(nthreads))
+    return y, yb
