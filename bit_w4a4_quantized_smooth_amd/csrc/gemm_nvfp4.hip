@@ -1,0 +1,226 @@
+// W4A4 NVFP4 GEMM of the SVDQuant linear ("Nunchaku Lite", "Supported
+// quantization types": svdq_w4a4 nvfp4, group 16; low-rank up-projection and
+// bias fused into the epilogue as in the blog "Nunchaku 4-bit inference in
+// Diffusers", "Background: SVDQuant and Nunchaku"):
+//   y[m,n] = alpha_a*alpha_w * sum_g sa[m,g]*sw[n,g]*P[m,n,g] + XL1.L2 + bias
+//
+// gfx950's block-scaled matrix instructions scale 32 channels by a power of
+// two, while NVFP4 scales 16 channels by an E4M3 number, so the scales are not
+// folded into the matrix core.  Instead each operand is dequantized exactly:
+// an E2M1 value (at most 2 significant bits) times an E4M3 scale (at most 4)
+// has at most 6 significant bits, so e2m1(c) * s is exact in bf16.  The tile
+// is expanded to bf16 while staging to LDS and the whole K reduction runs on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation; there is no per-group
+// rescale on the vector ALUs (which would cost more than the matrix work at
+// 16-channel groups).  With unit scales the same path yields the exact group
+// products P (multiples of 1/4) for the partial-product test mode.
+//
+// Tiling: 128(n) x 128(m) per 256-thread workgroup, wave tiles of 64x64,
+// K steps of 64 channels (four NVFP4 groups) double buffered in LDS.
+#include "common.h"
+#include "launch.h"
+
+namespace svdq {
+
+namespace {
+constexpr int BM = 128, BN = 128;
+constexpr int ROW = 72;  // bf16 per LDS row: 64 channels + 8 padding
+
+// E2M1 nibble -> fp32 value (exact).  Magnitudes 2..7 are the fp32 numbers
+// with bit pattern (m + 252) << 22; 1 is 0.5 and 0 is 0.
+__device__ __forceinline__ float e2m1_val(u32 c) {
+  const u32 m = c & 7u;
+  const float mag = m >= 2u ? __uint_as_float((m + 252u) << 22) : 0.5f * (float)m;
+  return (c & 8u) ? -mag : mag;
+}
+
+// 8 codes of one dword (channels 0..7, even channel in the low nibble) times
+// scale s -> 8 bf16 (exact; the product's low 16 bits are zero).
+__device__ __forceinline__ uint4 dequant8(u32 w, float s) {
+  u32 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float f0 = e2m1_val((w >> (8 * i)) & 0xFu) * s;
+    const float f1 = e2m1_val((w >> (8 * i + 4)) & 0xFu) * s;
+    o[i] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+  }
+  return uint4{o[0], o[1], o[2], o[3]};
+}
+}  // namespace
+
+template <int MODE>  // 0: Y; 1: fp32 partial products per 16-channel group
+__global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
+    int M, int N, int K, int rank, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
+    float alpha, const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+    const float* __restrict__ xl1, const uint16_t* __restrict__ l2t,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, float* __restrict__ psums) {
+  __shared__ __align__(16) uint16_t sW[2][BN * ROW];
+  __shared__ __align__(16) uint16_t sX[2][BM * ROW];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m_tiles = (M + BM - 1) / BM;
+  const int mt = blockIdx.x % m_tiles, nt = blockIdx.x / m_tiles;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int wn = (wave >> 1) * 64, wm = (wave & 1) * 64;
+  const int steps = K >> 6, G = K >> 4;
+  const size_t rowb = (size_t)(K >> 1);
+
+  // staging: thread -> (row, 16-byte half = 32 channels = two NVFP4 groups)
+  const int srow = tid >> 1, shalf = tid & 1;
+  const bool xvalid = (m0 + srow) < M;
+  const uint8_t* wsrc = wc + (size_t)(n0 + srow) * rowb + shalf * 16;
+  const uint8_t* xsrc = ac + (size_t)(xvalid ? m0 + srow : 0) * rowb + shalf * 16;
+  const uint8_t* wssrc = MODE == 0 ? ws + (size_t)(n0 + srow) * G + 2 * shalf : nullptr;
+  const uint8_t* xssrc = MODE == 0 ? as + (size_t)(xvalid ? m0 + srow : 0) * G + 2 * shalf : nullptr;
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  uint4 wv, xv;
+  u32 wsb = 0x3838u, xsb = 0x3838u;  // two E4M3 scales (1.0, 1.0 in test mode)
+  auto gload = [&](int st) {
+    wv = *(const uint4*)(wsrc + st * 32);
+    xv = xvalid ? *(const uint4*)(xsrc + st * 32) : uint4{0u, 0u, 0u, 0u};
+    if constexpr (MODE == 0) {
+      wsb = *(const uint16_t*)(wssrc + st * 4);
+      xsb = xvalid ? *(const uint16_t*)(xssrc + st * 4) : 0u;
+    }
+  };
+  auto sstore = [&](int buf) {
+    const float w0 = e4m3_to_f32(wsb & 0xFFu), w1 = e4m3_to_f32(wsb >> 8);
+    const float x0 = e4m3_to_f32(xsb & 0xFFu), x1 = e4m3_to_f32(xsb >> 8);
+    uint16_t* dw = &sW[buf][srow * ROW + shalf * 32];
+    *(uint4*)(dw + 0) = dequant8(wv.x, w0);
+    *(uint4*)(dw + 8) = dequant8(wv.y, w0);
+    *(uint4*)(dw + 16) = dequant8(wv.z, w1);
+    *(uint4*)(dw + 24) = dequant8(wv.w, w1);
+    uint16_t* dx = &sX[buf][srow * ROW + shalf * 32];
+    *(uint4*)(dx + 0) = dequant8(xv.x, x0);
+    *(uint4*)(dx + 8) = dequant8(xv.y, x0);
+    *(uint4*)(dx + 16) = dequant8(xv.z, x1);
+    *(uint4*)(dx + 24) = dequant8(xv.w, x1);
+  };
+
+  const int lr = lane & 31, lh = lane >> 5;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+
+  for (int st = 0; st < steps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < steps) gload(st + 1);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {  // one NVFP4 group per 16-channel MFMA step
+      v8bf a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *(const v8bf*)&sW[buf][(wn + 32 * i + lr) * ROW + 16 * kk + 8 * lh];
+        b[i] = *(const v8bf*)&sX[buf][(wm + 32 * i + lr) * ROW + 16 * kk + 8 * lh];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if constexpr (MODE == 1) {
+            v16f d;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) d[v] = 0.0f;
+            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], d, 0, 0, 0);
+            const int m = m0 + wm + 32 * j + lr;
+            if (m < M) {
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const int n = n0 + wn + 32 * i + 8 * (v >> 2) + 4 * lh + (v & 3);
+                psums[((size_t)m * N + n) * G + 4 * st + kk] = d[v];
+              }
+            }
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          }
+        }
+    }
+    if (st + 1 < steps) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if constexpr (MODE == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] *= alpha;
+    for (int jb = 0; jb < rank; jb += 16) {
+      v8bf al[2], bl[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        al[i] = *(const v8bf*)(l2t + (size_t)(n0 + wn + 32 * i + lr) * rank + jb + 8 * lh);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int m = m0 + wm + 32 * j + lr;
+        uint4 pk = {0u, 0u, 0u, 0u};
+        if (m < M) {
+          const float4* src = (const float4*)(xl1 + (size_t)m * rank + jb + 8 * lh);
+          const float4 f0 = src[0], f1 = src[1];
+          pk.x = f32_to_bf16_bits(f0.x) | (f32_to_bf16_bits(f0.y) << 16);
+          pk.y = f32_to_bf16_bits(f0.z) | (f32_to_bf16_bits(f0.w) << 16);
+          pk.z = f32_to_bf16_bits(f1.x) | (f32_to_bf16_bits(f1.y) << 16);
+          pk.w = f32_to_bf16_bits(f1.z) | (f32_to_bf16_bits(f1.w) << 16);
+        }
+        bl[j] = __builtin_bit_cast(v8bf, pk);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bl[j], acc[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int m = m0 + wm + 32 * j + lr;
+        if (m >= M) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn + 32 * i + 8 * q + 4 * lh;
+          float bv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (bias) {
+            const uint2 bb = *(const uint2*)(bias + n);
+            bv[0] = bf16_bits_to_f32(bb.x & 0xFFFFu);
+            bv[1] = bf16_bits_to_f32(bb.x >> 16);
+            bv[2] = bf16_bits_to_f32(bb.y & 0xFFFFu);
+            bv[3] = bf16_bits_to_f32(bb.y >> 16);
+          }
+          uint2 o;
+          o.x = f32_to_bf16_bits(acc[i][j][4 * q] + bv[0]) | (f32_to_bf16_bits(acc[i][j][4 * q + 1] + bv[1]) << 16);
+          o.y = f32_to_bf16_bits(acc[i][j][4 * q + 2] + bv[2]) | (f32_to_bf16_bits(acc[i][j][4 * q + 3] + bv[3]) << 16);
+          *(uint2*)(y + (size_t)m * N + n) = o;
+        }
+      }
+  }
+}
+
+hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st) {
+  const int m_tiles = (int)((a.M + BM - 1) / BM);
+  const int blocks = m_tiles * (int)(a.N / BN);
+  if (a.psums) {
+    hipLaunchKernelGGL(gemm_nvfp4_kernel<1>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
+                       (int)a.K, 0, (const uint8_t*)a.act_codes, nullptr, 1.0f,
+                       (const uint8_t*)a.w_codes, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       (float*)a.psums);
+  } else {
+    hipLaunchKernelGGL(gemm_nvfp4_kernel<0>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
+                       (int)a.K, a.rank, (const uint8_t*)a.act_codes, (const uint8_t*)a.act_scales,
+                       a.alpha_a * a.alpha_w, (const uint8_t*)a.w_codes, (const uint8_t*)a.w_scales,
+                       a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace svdq

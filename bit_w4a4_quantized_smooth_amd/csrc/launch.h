@@ -1,0 +1,53 @@
+// Internal launch interface between the C-ABI layer (svdq_api.hip) and the
+// kernel files.  Arguments arrive already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace svdq {
+
+struct QuantArgs {
+  int precision, rank;
+  int64_t M, K;
+  const void* x;
+  const void* smooth;
+  const void* l1t;
+  float alpha;
+  void* codes;
+  void* scales;
+  float* xl1;
+};
+
+struct GemmArgs {
+  int precision, rank;
+  int64_t M, N, K;
+  const void* act_codes;
+  const void* act_scales;
+  float alpha_a;
+  const void* w_codes;
+  const void* w_scales;
+  float alpha_w;
+  const float* xl1;
+  const void* l2t;
+  const void* bias;
+  void* y;       // bf16 [M, N] (GEMM) ...
+  void* psums;   // ... or [M, N, K/G] partial products (test support)
+};
+
+struct AwqArgs {
+  int64_t M, N, K;
+  const void* x;
+  const void* w_codes;
+  const void* w_scales;
+  const void* w_zeros;
+  const void* bias;
+  void* y;
+};
+
+hipError_t launch_quantize_act(const QuantArgs& a, hipStream_t st);
+hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st);
+hipError_t launch_awq(const AwqArgs& a, hipStream_t st);
+
+}  // namespace svdq

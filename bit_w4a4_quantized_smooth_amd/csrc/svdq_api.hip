@@ -1,0 +1,251 @@
+// C ABI of libsvdq.so (declared in include/svdq.h): argument validation, the
+// device architecture check and dispatch to the gfx950 kernels.  Nothing here
+// allocates device memory.
+//
+// The accepted (method, precision, group) triples are the table in "Nunchaku
+// Lite", "Supported quantization types": svdq_w4a4 nvfp4 16, svdq_w4a4 int4
+// 64, awq_w4a16 int4 64.  A device that is not gfx950 is rejected with an
+// error before any launch, never run into wrong results (blog "Nunchaku 4-bit
+// inference in Diffusers", "Hardware support": the capability check at load).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "../../include/svdq.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::mutex g_arch_mu;
+std::string g_arch_override;
+bool g_has_override = false;
+int g_arch_ok[64];  // per device: 0 unknown, 1 gfx950, 2 other
+
+svdq_status fail(svdq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+svdq_status ok() {
+  g_last_error.clear();
+  return SVDQ_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+svdq_status check_arch() {
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (g_has_override) {
+    if (g_arch_override.rfind("gfx950", 0) != 0)
+      return fail(SVDQ_ERR_UNSUPPORTED, "device architecture %s is not supported (gfx950 required)",
+                  g_arch_override.c_str());
+    return SVDQ_OK;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SVDQ_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(SVDQ_ERR_DEVICE, "device index %d out of range", dev);
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(SVDQ_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    g_arch_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (g_arch_ok[dev] != 1)
+      return fail(SVDQ_ERR_UNSUPPORTED, "device architecture %s is not supported (gfx950 required)",
+                  prop.gcnArchName);
+  }
+  if (g_arch_ok[dev] != 1) return fail(SVDQ_ERR_UNSUPPORTED, "device is not gfx950");
+  return SVDQ_OK;
+}
+
+// Reports a fault left by an earlier launch, before anything new is enqueued.
+svdq_status check_sticky() {
+  hipError_t e = hipPeekAtLastError();
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SVDQ_ERR_DEVICE, "earlier HIP error: %s", hipGetErrorString(e));
+  }
+  return SVDQ_OK;
+}
+
+svdq_status launched(hipError_t e) {
+  if (e != hipSuccess) return fail(SVDQ_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+bool valid_rank(int r) { return r >= 0 && r <= 128 && r % 16 == 0; }
+
+svdq_status check_precision(int precision, int group) {
+  if (precision == SVDQ_INT4 && group == 64) return SVDQ_OK;
+  if (precision == SVDQ_NVFP4 && group == 16) return SVDQ_OK;
+  return fail(SVDQ_ERR_UNSUPPORTED,
+              "svdq_w4a4 supports (int4, group 64) and (nvfp4, group 16); got precision %d group %d",
+              precision, group);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+}  // namespace
+
+extern "C" {
+
+int svdq_abi_version(void) { return 1; }
+
+const char* svdq_last_error(void) { return g_last_error.c_str(); }
+
+void svdq_test_set_arch_override(const char* arch) {
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  g_has_override = arch != nullptr;
+  g_arch_override = arch ? arch : "";
+}
+
+svdq_status svdq_quantize_act(int precision, int group_size, int rank, int64_t M, int64_t K,
+                              const void* x, const void* smooth, const void* l1t,
+                              float act_global_scale, void* act_codes, void* act_scales,
+                              float* xl1, void* stream) {
+  svdq_status s;
+  if ((s = check_precision(precision, group_size)) != SVDQ_OK) return s;
+  if (!valid_rank(rank)) return fail(SVDQ_ERR_UNSUPPORTED, "rank %d not in {0, 16, ..., 128}", rank);
+  if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxDim) return fail(SVDQ_ERR_INVALID_ARG, "bad shape M=%lld K=%lld", (long long)M, (long long)K);
+  if (K % 64 != 0) return fail(SVDQ_ERR_UNSUPPORTED, "K=%lld must be a multiple of 64", (long long)K);
+  if (K > 32768) return fail(SVDQ_ERR_UNSUPPORTED, "K=%lld above the supported 32768", (long long)K);
+  if (M * K > ((int64_t)1 << 31)) return fail(SVDQ_ERR_UNSUPPORTED, "M*K above 2^31");
+  if (M == 0) return ok();  // empty call: nothing to read or write
+  if (!x || !act_codes || !act_scales) return fail(SVDQ_ERR_INVALID_ARG, "x, act_codes and act_scales are required");
+  if ((rank > 0) != (l1t != nullptr)) return fail(SVDQ_ERR_INVALID_ARG, "l1t must be given iff rank > 0");
+  if ((rank > 0) != (xl1 != nullptr)) return fail(SVDQ_ERR_INVALID_ARG, "xl1 must be given iff rank > 0");
+  if (precision == SVDQ_NVFP4 && !(act_global_scale > 0.0f && act_global_scale < 3.0e38f))
+    return fail(SVDQ_ERR_INVALID_ARG, "act_global_scale must be finite and > 0 for nvfp4");
+  if (!aligned16(x) || !aligned16(smooth) || !aligned16(l1t) || !aligned16(act_codes) ||
+      !aligned16(act_scales) || !aligned16(xl1))
+    return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
+  const size_t nx = (size_t)M * K * 2, nc = (size_t)M * K / 2;
+  const size_t ns = precision == SVDQ_INT4 ? (size_t)M * (K / 64) * 2 : (size_t)M * (K / 16);
+  const size_t nl = (size_t)M * rank * 4;
+  if (overlaps(x, nx, act_codes, nc) || overlaps(x, nx, act_scales, ns) || overlaps(x, nx, xl1, nl) ||
+      overlaps(act_codes, nc, act_scales, ns) || overlaps(act_codes, nc, xl1, nl) ||
+      overlaps(act_scales, ns, xl1, nl))
+    return fail(SVDQ_ERR_INVALID_ARG, "outputs must not overlap each other or x");
+  if ((s = check_arch()) != SVDQ_OK) return s;
+  if (M == 0) return ok();
+  if ((s = check_sticky()) != SVDQ_OK) return s;
+  svdq::QuantArgs a{precision, rank, M, K, x, smooth, l1t, act_global_scale, act_codes, act_scales, xl1};
+  return launched(svdq::launch_quantize_act(a, (hipStream_t)stream));
+}
+
+static svdq_status gemm_common(int precision, int group_size, int rank, int64_t M, int64_t N,
+                               int64_t K, const void* act_codes, const void* w_codes) {
+  svdq_status s;
+  if ((s = check_precision(precision, group_size)) != SVDQ_OK) return s;
+  if (!valid_rank(rank)) return fail(SVDQ_ERR_UNSUPPORTED, "rank %d not in {0, 16, ..., 128}", rank);
+  if (M < 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(SVDQ_ERR_INVALID_ARG, "bad shape M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
+  if (K % 64 != 0) return fail(SVDQ_ERR_UNSUPPORTED, "K=%lld must be a multiple of 64", (long long)K);
+  if (N % 128 != 0) return fail(SVDQ_ERR_UNSUPPORTED, "N=%lld must be a multiple of 128", (long long)N);
+  if (M * K > ((int64_t)1 << 31) || N * K > ((int64_t)1 << 31) || M * N > ((int64_t)1 << 31))
+    return fail(SVDQ_ERR_UNSUPPORTED, "operand above 2^31 elements");
+  if (M > 0 && !act_codes) return fail(SVDQ_ERR_INVALID_ARG, "act_codes is required");
+  if (!w_codes) return fail(SVDQ_ERR_INVALID_ARG, "w_codes is required");
+  return SVDQ_OK;
+}
+
+svdq_status svdq_w4a4_gemm(int precision, int group_size, int rank, int64_t M, int64_t N,
+                           int64_t K, const void* act_codes, const void* act_scales,
+                           float act_global_scale, const void* w_codes, const void* w_scales,
+                           float w_global_scale, const float* xl1, const void* l2t,
+                           const void* bias, void* y, void* stream) {
+  svdq_status s;
+  if ((s = gemm_common(precision, group_size, rank, M, N, K, act_codes, w_codes)) != SVDQ_OK) return s;
+  if (M == 0) return ok();  // empty call: nothing to read or write
+  if (!act_scales || !w_scales || !y) return fail(SVDQ_ERR_INVALID_ARG, "act_scales, w_scales and y are required");
+  if ((rank > 0) != (xl1 != nullptr) || (rank > 0) != (l2t != nullptr))
+    return fail(SVDQ_ERR_INVALID_ARG, "xl1 and l2t must be given iff rank > 0");
+  if (precision == SVDQ_NVFP4 && !(act_global_scale > 0.0f && w_global_scale > 0.0f &&
+                                   act_global_scale < 3.0e38f && w_global_scale < 3.0e38f))
+    return fail(SVDQ_ERR_INVALID_ARG, "global scales must be finite and > 0 for nvfp4");
+  if (!aligned16(act_codes) || !aligned16(act_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(xl1) || !aligned16(l2t) || !aligned16(bias) || !aligned16(y))
+    return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
+  const size_t ny = (size_t)M * N * 2;
+  const size_t ns_a = precision == SVDQ_INT4 ? (size_t)M * (K / 64) * 2 : (size_t)M * (K / 16);
+  const size_t ns_w = precision == SVDQ_INT4 ? (size_t)N * (K / 64) * 2 : (size_t)N * (K / 16);
+  if (overlaps(y, ny, act_codes, (size_t)M * K / 2) || overlaps(y, ny, w_codes, (size_t)N * K / 2) ||
+      overlaps(y, ny, act_scales, ns_a) || overlaps(y, ny, w_scales, ns_w) ||
+      overlaps(y, ny, xl1, (size_t)M * rank * 4) || overlaps(y, ny, l2t, (size_t)N * rank * 2) ||
+      overlaps(y, ny, bias, (size_t)N * 2))
+    return fail(SVDQ_ERR_INVALID_ARG, "y must not overlap an input");
+  if ((s = check_arch()) != SVDQ_OK) return s;
+  if (M == 0) return ok();
+  if ((s = check_sticky()) != SVDQ_OK) return s;
+  svdq::GemmArgs a{precision, rank, M, N, K, act_codes, act_scales, act_global_scale, w_codes,
+                   w_scales, w_global_scale, xl1, l2t, bias, y, nullptr};
+  return launched(precision == SVDQ_INT4 ? svdq::launch_gemm_int4(a, (hipStream_t)stream)
+                                         : svdq::launch_gemm_nvfp4(a, (hipStream_t)stream));
+}
+
+svdq_status svdq_w4a4_group_psums(int precision, int group_size, int64_t M, int64_t N, int64_t K,
+                                  const void* act_codes, const void* w_codes, void* psums,
+                                  void* stream) {
+  svdq_status s;
+  if ((s = gemm_common(precision, group_size, 0, M, N, K, act_codes, w_codes)) != SVDQ_OK) return s;
+  if (M == 0) return ok();  // empty call: nothing to read or write
+  if (!psums) return fail(SVDQ_ERR_INVALID_ARG, "psums is required");
+  if (!aligned16(act_codes) || !aligned16(w_codes) || !aligned16(psums))
+    return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
+  const size_t np = (size_t)M * N * (K / group_size) * 4;
+  if (overlaps(psums, np, act_codes, (size_t)M * K / 2) || overlaps(psums, np, w_codes, (size_t)N * K / 2))
+    return fail(SVDQ_ERR_INVALID_ARG, "psums must not overlap an input");
+  if ((s = check_arch()) != SVDQ_OK) return s;
+  if (M == 0) return ok();
+  if ((s = check_sticky()) != SVDQ_OK) return s;
+  svdq::GemmArgs a{precision, 0, M, N, K, act_codes, nullptr, 1.0f, w_codes, nullptr, 1.0f,
+                   nullptr, nullptr, nullptr, nullptr, psums};
+  return launched(precision == SVDQ_INT4 ? svdq::launch_gemm_int4(a, (hipStream_t)stream)
+                                         : svdq::launch_gemm_nvfp4(a, (hipStream_t)stream));
+}
+
+svdq_status awq_w4a16_gemv(int group_size, int64_t M, int64_t N, int64_t K, const void* x,
+                           const void* w_codes, const void* w_scales, const void* w_zeros,
+                           const void* bias, void* y, void* stream) {
+  if (group_size != 64)
+    return fail(SVDQ_ERR_UNSUPPORTED, "awq_w4a16 supports int4 with group 64; got group %d", group_size);
+  if (M < 0 || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
+    return fail(SVDQ_ERR_INVALID_ARG, "bad shape M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
+  if (M > 64) return fail(SVDQ_ERR_UNSUPPORTED, "M=%lld above 64 (weight-only path is for small M)", (long long)M);
+  if (K % 64 != 0) return fail(SVDQ_ERR_UNSUPPORTED, "K=%lld must be a multiple of 64", (long long)K);
+  if (N % 64 != 0) return fail(SVDQ_ERR_UNSUPPORTED, "N=%lld must be a multiple of 64", (long long)N);
+  if (N * K > ((int64_t)1 << 31)) return fail(SVDQ_ERR_UNSUPPORTED, "N*K above 2^31");
+  if (M == 0) return ok();  // empty call: nothing to read or write
+  if (!x || !w_codes || !w_scales || !w_zeros || !y)
+    return fail(SVDQ_ERR_INVALID_ARG, "x, w_codes, w_scales, w_zeros and y are required");
+  if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(w_zeros) ||
+      !aligned16(bias) || !aligned16(y))
+    return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
+  const size_t ny = (size_t)M * N * 2, ng = (size_t)N * (K / 64) * 2;
+  if (overlaps(y, ny, x, (size_t)M * K * 2) || overlaps(y, ny, w_codes, (size_t)N * K / 2) ||
+      overlaps(y, ny, w_scales, ng) || overlaps(y, ny, w_zeros, ng) || overlaps(y, ny, bias, (size_t)N * 2))
+    return fail(SVDQ_ERR_INVALID_ARG, "y must not overlap an input");
+  svdq_status s;
+  if ((s = check_arch()) != SVDQ_OK) return s;
+  if (M == 0) return ok();
+  if ((s = check_sticky()) != SVDQ_OK) return s;
+  svdq::AwqArgs a{M, N, K, x, w_codes, w_scales, w_zeros, bias, y};
+  return launched(svdq::launch_awq(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,165 @@
+/*
+ * svdq.h -- C ABI of libsvdq.so: the SVDQuant W4A4 linear layer and the AWQ
+ * W4A16 weight-only linear, as hand-written HIP kernels for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What the layer computes (sources: the "Nunchaku Lite" Diffusers docs and the
+ * blog "Nunchaku 4-bit inference in Diffusers"):
+ *   Y = Q(X / lambda) . Q(W_res)^T  with per-group dequantization
+ *     + (X . L1) . L2                16-bit low-rank branch
+ *     + bias
+ *   - smoothing moves activation outliers into the weights; a low-rank branch
+ *     carries the hardest part of each weight; the residual runs as 4-bit
+ *     weights x 4-bit activations (blog, "Background: SVDQuant and Nunchaku");
+ *   - the low-rank down-projection X.L1 is computed by the activation quantizer
+ *     and the up-projection (X.L1).L2 inside the 4-bit GEMM, so the 16-bit
+ *     branch adds no extra pass over X or Y (same section);
+ *   - precisions: svdq_w4a4 int4 with group 64, svdq_w4a4 nvfp4 with group 16,
+ *     awq_w4a16 int4 weight-only with group 64 ("Nunchaku Lite", table in
+ *     "Supported quantization types"); the layer's float buffers are bfloat16
+ *     ("NunchakuLiteQuantizationConfig", compute_dtype);
+ *   - an unsupported GPU is reported as an error, never as wrong output (blog,
+ *     "Hardware support").
+ *
+ * Conventions shared by every entry point
+ *   - All buffers are caller-owned DEVICE pointers, contiguous, row-major,
+ *     16-byte aligned.  The library allocates nothing and keeps no state apart
+ *     from a per-device architecture check.
+ *   - bf16 / fp16 values are IEEE bit patterns in uint16; E4M3 values are OCP
+ *     E4M3 "FN" bytes; 4-bit codes are packed two per byte, even channel k in
+ *     the low nibble.  int4 codes are two's complement in [-8, 7]; NVFP4 codes
+ *     are E2M1 (sign in bit 3); AWQ codes are unsigned 0..15.
+ *   - Weights follow the nn.Linear layout: W codes [N, K/2], L1 given as
+ *     l1t = L1^T [rank, K], L2 given as l2t = L2^T [N, rank].
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; nothing synchronizes.  A device fault
+ *     of an earlier launch is reported by the next call as SVDQ_ERR_DEVICE.
+ *   - Every argument is checked before anything is launched; on a non-OK
+ *     status nothing was enqueued and svdq_last_error() describes the cause.
+ *   - M == 0 is a valid empty call: nothing is launched and the buffers whose
+ *     size is proportional to M may be NULL.
+ */
+#ifndef SVDQ_H_
+#define SVDQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_ERR_INVALID_ARG = 1,  /* NULL required pointer, negative or inconsistent size */
+  SVDQ_ERR_UNSUPPORTED = 2,  /* not gfx950, precision/group/rank outside the table, shape limits */
+  SVDQ_ERR_ALIGNMENT = 3,    /* a pointer is not 16-byte aligned */
+  SVDQ_ERR_DEVICE = 4        /* a HIP runtime error (launch failure or an earlier fault) */
+} svdq_status;
+
+typedef enum { SVDQ_INT4 = 0, SVDQ_NVFP4 = 1 } svdq_precision;
+
+/*
+ * svdq_quantize_act -- smoothing, 4-bit activation quantization and the fused
+ * low-rank down-projection, reading X once (blog, "Background: SVDQuant and
+ * Nunchaku"; precisions from "Supported quantization types").
+ *
+ * For every row m and group g of `group_size` channels:
+ *   xh_k = fl32(x_k * fl32(1 / lambda_k))                  (smoothing)
+ *   int4 (group 64):  s = fp16_sat(fl32(max|xh| / 7)),
+ *                     q_k = clamp(rne(fl32(xh_k * fl32(1/s))), -8, 7), 0 if s == 0
+ *   nvfp4 (group 16): s = e4m3_sat(fl32(max|xh| / fl32(6 * alpha))),
+ *                     c_k = e2m1_sat(fl32(xh_k * fl32(1 / fl32(s * alpha)))), 0 if s == 0
+ *   xl1[m, j] = sum_k x[m, k] * L1[k, j]   (raw X, fp32 accumulation)
+ *
+ *   precision   SVDQ_INT4 (group_size must be 64) or SVDQ_NVFP4 (16)
+ *   rank        0, 16, 32, ..., 128; 0 disables the low-rank branch
+ *   M, K        rows and channels; K % 64 == 0, K <= 32768
+ *   x           bf16 [M, K]
+ *   smooth      bf16 [K] smoothing factors lambda (finite, > 0), or NULL for 1
+ *   l1t         bf16 [rank, K] (L1 transposed); NULL iff rank == 0
+ *   act_global_scale  NVFP4 per-tensor scale alpha > 0 (static); ignored for int4
+ *   act_codes   out u8 [M, K/2]
+ *   act_scales  out int4: fp16 [M, K/64]; nvfp4: E4M3 u8 [M, K/16]
+ *   xl1         out fp32 [M, rank]; NULL iff rank == 0
+ */
+svdq_status svdq_quantize_act(int precision, int group_size, int rank, int64_t M, int64_t K,
+                              const void* x, const void* smooth, const void* l1t,
+                              float act_global_scale, void* act_codes, void* act_scales,
+                              float* xl1, void* stream);
+
+/*
+ * svdq_w4a4_gemm -- the 4-bit GEMM with per-group dequantization and the
+ * low-rank up-projection and bias fused into its epilogue (blog, "Background:
+ * SVDQuant and Nunchaku"):
+ *   int4:  y[m,n] = sum_g sa[m,g] * sw[n,g] * P[m,n,g]
+ *   nvfp4: y[m,n] = alpha_a * alpha_w * sum_g sa[m,g] * sw[n,g] * P[m,n,g]
+ *          + sum_j xl1[m,j] * L2[j,n] + bias[n];   Y = bf16(y)
+ * where P[m,n,g] = sum over the group's channels of act code x weight code.
+ *
+ *   precision, group_size   as for svdq_quantize_act
+ *   rank        0, 16, ..., 128
+ *   M, N, K     M >= 0; N % 128 == 0; K % 64 == 0
+ *   act_codes, act_scales   as written by svdq_quantize_act
+ *   act_global_scale, w_global_scale   NVFP4 alpha_a, alpha_w; ignored for int4
+ *   w_codes     u8 [N, K/2] (same nibble order and encoding as act_codes)
+ *   w_scales    int4: fp16 [N, K/64]; nvfp4: E4M3 u8 [N, K/16]
+ *   xl1         fp32 [M, rank]; NULL iff rank == 0
+ *   l2t         bf16 [N, rank] (L2 transposed); NULL iff rank == 0
+ *   bias        bf16 [N] or NULL
+ *   y           out bf16 [M, N]; must not overlap any input
+ */
+svdq_status svdq_w4a4_gemm(int precision, int group_size, int rank, int64_t M, int64_t N,
+                           int64_t K, const void* act_codes, const void* act_scales,
+                           float act_global_scale, const void* w_codes, const void* w_scales,
+                           float w_global_scale, const float* xl1, const void* l2t,
+                           const void* bias, void* y, void* stream);
+
+/*
+ * awq_w4a16_gemv -- AWQ-style int4 weight-only linear for memory-bound
+ * modulation projections ("Supported quantization types": awq_w4a16, int4,
+ * group 64; blog, "Introducing Nunchaku Lite"):
+ *   y[m,n] = sum_g sum_{k in g} x[m,k] * (q[n,k] - z[n,g]) * s[n,g] + bias[n]
+ *
+ *   group_size  64
+ *   M, N, K     0 <= M <= 64; N % 64 == 0; K % 64 == 0
+ *   x           bf16 [M, K]
+ *   w_codes     u8 [N, K/2], unsigned codes 0..15
+ *   w_scales    fp16 [N, K/64]
+ *   w_zeros     fp16 [N, K/64] (zero-points, in code units)
+ *   bias        bf16 [N] or NULL
+ *   y           out bf16 [M, N]
+ */
+svdq_status awq_w4a16_gemv(int group_size, int64_t M, int64_t N, int64_t K, const void* x,
+                           const void* w_codes, const void* w_scales, const void* w_zeros,
+                           const void* bias, void* y, void* stream);
+
+/*
+ * svdq_w4a4_group_psums -- test support: the per-group partial products of
+ * the 4-bit GEMM, P[m,n,g] = sum_{k in g} a_code * w_code, computed by the
+ * same unpack and matrix-core path as svdq_w4a4_gemm.  int4: int32 (exact);
+ * nvfp4: fp32 (exact: multiples of 1/4, |P| <= 576).  Layout [M, N, K/G],
+ * g fastest.  Crops of larger operands are taken by pointer offsets (rows of
+ * the code buffers are contiguous).  Shape limits as for svdq_w4a4_gemm.
+ */
+svdq_status svdq_w4a4_group_psums(int precision, int group_size, int64_t M, int64_t N,
+                                  int64_t K, const void* act_codes, const void* w_codes,
+                                  void* psums, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* svdq_last_error(void);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int svdq_abi_version(void);
+
+/*
+ * Test hook: when `arch` is non-NULL every later architecture check sees this
+ * gcnArchName instead of the device's; NULL restores the real check.  Lets a
+ * test prove that a non-gfx950 device gets SVDQ_ERR_UNSUPPORTED and no launch.
+ */
+void svdq_test_set_arch_override(const char* arch);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H_ */

@@ -1,0 +1,132 @@
+"""The C ABI on a host without a GPU: libsvdq.so loads, exports every function
+that include/svdq.h declares, and rejects bad arguments and non-gfx950
+devices before anything is launched (no compute call is made here: every
+call below fails validation or the architecture check first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_w4a4_quantized_smooth_amd as sq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, DEVICE = 0, 1, 2, 3, 4
+A = 1 << 20  # a fake, 16-byte aligned "device address"; never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svdq_\w+|awq_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return sq.lib()
+
+
+@pytest.fixture(autouse=True)
+def gfx942(L):
+    # every call that gets past validation meets a non-gfx950 architecture
+    L.svdq_test_set_arch_override(b"gfx942")
+    yield
+    L.svdq_test_set_arch_override(None)
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"svdq_quantize_act", "svdq_w4a4_gemm", "awq_w4a16_gemv", "svdq_w4a4_group_psums",
+            "svdq_last_error", "svdq_abi_version", "svdq_test_set_arch_override"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(sq.EXPORTS) == set(names)
+    assert L.svdq_abi_version() == 1
+
+
+def q(L, prec=0, G=64, r=16, M=256, K=512, x=A, smooth=A, l1t=A, alpha=1.0, codes=2 * A,
+      scales=3 * A, xl1=4 * A):
+    return L.svdq_quantize_act(prec, G, r, M, K, x, smooth, l1t, alpha, codes, scales, xl1, None)
+
+
+def gemm(L, prec=0, G=64, r=16, M=256, N=512, K=512, ac=A, as_=2 * A, aa=1.0, wc=3 * A, ws=4 * A,
+         aw=1.0, xl1=5 * A, l2t=6 * A, bias=7 * A, y=8 * A):
+    return L.svdq_w4a4_gemm(prec, G, r, M, N, K, ac, as_, aa, wc, ws, aw, xl1, l2t, bias, y, None)
+
+
+def awq(L, G=64, M=2, N=512, K=512, x=A, wc=2 * A, ws=3 * A, wz=4 * A, bias=5 * A, y=6 * A):
+    return L.awq_w4a16_gemv(G, M, N, K, x, wc, ws, wz, bias, y, None)
+
+
+def test_valid_arguments_reach_the_arch_check(L):
+    assert q(L) == UNSUPPORTED
+    assert b"gfx942" in L.svdq_last_error()
+    assert q(L, prec=1, G=16, alpha=0.01) == UNSUPPORTED
+    assert gemm(L) == UNSUPPORTED
+    assert gemm(L, prec=1, G=16) == UNSUPPORTED
+    assert awq(L) == UNSUPPORTED
+    assert L.svdq_w4a4_group_psums(0, 64, 256, 512, 512, A, 2 * A, 3 * A, None) == UNSUPPORTED
+
+
+def test_precision_group_table(L):
+    # the supported (method, precision, group) triples only
+    assert q(L, prec=0, G=16) == UNSUPPORTED
+    assert q(L, prec=1, G=64) == UNSUPPORTED
+    assert q(L, prec=2, G=64) == UNSUPPORTED
+    assert gemm(L, prec=0, G=32) == UNSUPPORTED
+    assert awq(L, G=16) == UNSUPPORTED
+    assert awq(L, G=128) == UNSUPPORTED
+
+
+def test_rank_and_shape_limits(L):
+    for r in (8, 24, 144, -16):
+        assert q(L, r=r) == UNSUPPORTED
+    assert q(L, K=96) == UNSUPPORTED          # not a multiple of 64
+    assert q(L, M=-1) == INVALID
+    assert q(L, K=0) == INVALID
+    assert gemm(L, N=500) == UNSUPPORTED      # N % 128
+    assert gemm(L, N=0) == INVALID
+    assert awq(L, M=65) == UNSUPPORTED
+    assert awq(L, N=96) == UNSUPPORTED
+
+
+def test_required_pointers(L):
+    assert q(L, x=None) == INVALID
+    assert q(L, codes=None) == INVALID
+    assert q(L, r=16, l1t=None) == INVALID
+    assert q(L, r=0, l1t=A, xl1=None) == INVALID
+    assert q(L, r=16, xl1=None) == INVALID
+    assert q(L, r=0, l1t=None, xl1=None) == UNSUPPORTED  # valid: reaches the arch check
+    assert q(L, smooth=None) == UNSUPPORTED              # smoothing is optional
+    assert gemm(L, y=None) == INVALID
+    assert gemm(L, r=16, l2t=None) == INVALID
+    assert gemm(L, bias=None) == UNSUPPORTED             # bias is optional
+    assert awq(L, wz=None) == INVALID
+    assert q(L, prec=1, G=16, alpha=0.0) == INVALID
+    assert q(L, prec=1, G=16, alpha=float("inf")) == INVALID
+
+
+def test_alignment(L):
+    assert q(L, x=A + 8) == ALIGN
+    assert gemm(L, y=8 * A + 2) == ALIGN
+    assert awq(L, ws=3 * A + 4) == ALIGN
+
+
+def test_overlapping_outputs(L):
+    assert q(L, codes=A) == INVALID  # codes alias x
+    assert gemm(L, y=A) == INVALID   # y aliases act_codes
+
+
+def test_empty_call_is_valid(L):
+    L.svdq_test_set_arch_override(b"gfx950")
+    assert q(L, M=0) == OK
+    assert gemm(L, M=0) == OK
+    assert awq(L, M=0) == OK
+
+
+def test_python_binding_raises_loudly(L):
+    with pytest.raises(sq.SvdqError) as e:
+        sq._check(q(L))
+    assert e.value.status == UNSUPPORTED

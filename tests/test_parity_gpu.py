@@ -1,0 +1,232 @@
+"""Parity of the gfx950 HIP path with the CPU oracle, through the C ABI.
+
+Bar: 4-bit codes, scales and per-group partial products bit-exact; XL1 within
+1e-4 of the oracle's double result (normalized by its max |value|); Y within
+1e-2 max-abs-rel, max |Y_gpu - y| / max |y| against the oracle's double y
+before bf16 rounding.  Small workloads are compared element by element in
+full; the DiT-sized ones are compared in full where the oracle is cheap
+(codes, scales, XL1, AWQ at M = 2) and on sampled outputs otherwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import bit_w4a4_quantized_smooth_amd as sq
+from bit_w4a4_quantized_smooth_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 1e-2
+XL1_TOL = 1e-4
+
+
+def dev(a, dtype=None):
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def bf16_dev(bits):
+    return dev(np.asarray(bits, np.uint16).view(np.int16), torch.bfloat16)
+
+
+def f16_dev(bits):
+    return dev(np.asarray(bits, np.uint16).view(np.int16), torch.float16)
+
+
+def host_bits(t):
+    t = t.cpu()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def bf16_to_f64(bits):
+    return synth.bf16_bits_to_f64(bits)
+
+
+def max_abs_rel(y_bits, y_ref):
+    y = bf16_to_f64(y_bits)
+    return float(np.max(np.abs(y - y_ref)) / max(np.max(np.abs(y_ref)), 1e-30))
+
+
+def scales_dev(prec, s):
+    return f16_dev(s) if prec == sq.SVDQ_INT4 else dev(s)
+
+
+def run_quant(d, smooth=True):
+    lam = d["lam"] if smooth else None
+    codes, scales, xl1 = sq.quantize_act(d["prec"], bf16_dev(d["x"]), bf16_dev(lam) if lam is not None else None,
+                                         bf16_dev(d["l1t"]) if d["rank"] else None, d["alpha_a"])
+    torch.cuda.synchronize()
+    return (host_bits(codes), host_bits(scales), None if xl1 is None else xl1.cpu().numpy())
+
+
+def check_quant(d, smooth=True):
+    codes, scales, xl1 = run_quant(d, smooth)
+    lam = d["lam"] if smooth else None
+    oc, os_ = oracle.quantize_act(d["prec"], d["x"], lam, alpha=d["alpha_a"])
+    assert np.array_equal(scales, os_), f"scales differ at {np.argwhere(scales != os_)[:5]}"
+    assert np.array_equal(codes, oc), f"codes differ at {np.argwhere(codes != oc)[:5]}"
+    if d["rank"]:
+        ox = oracle.lowrank_down(d["x"], d["l1t"])
+        err = np.max(np.abs(xl1 - ox)) / max(np.max(np.abs(ox)), 1e-30)
+        assert err <= XL1_TOL, err
+    return codes, scales, xl1
+
+
+def run_gemm(d, codes, scales, xl1, with_bias=True):
+    y = sq.w4a4_gemm(d["prec"], dev(codes), scales_dev(d["prec"], scales), dev(d["w_codes"]),
+                     scales_dev(d["prec"], d["w_scales"]), dev(xl1) if d["rank"] else None,
+                     bf16_dev(d["l2t"]) if d["rank"] else None,
+                     bf16_dev(d["bias"]) if (with_bias and d["bias"] is not None) else None,
+                     d["alpha_a"], d["alpha_w"])
+    torch.cuda.synchronize()
+    return host_bits(y)
+
+
+def oracle_y(d, codes, scales, xl1, rows=None, cols=None, with_bias=True):
+    y, _ = oracle.w4a4_linear(d["prec"], codes, scales, d["w_codes"], d["w_scales"],
+                              xl1 if d["rank"] else None, d["l2t"] if d["rank"] else None,
+                              d["bias"] if with_bias else None, alpha_a=d["alpha_a"],
+                              alpha_w=d["alpha_w"], rows=rows, cols=cols)
+    return y
+
+
+# --------------------------------------------------------------------------- small, full
+SMALL = {
+    "int4_256x512x512_r16": lambda: synth.svdq_layer(1001, 256, 512, 512, 16, synth.INT4, 0.01, 20.0),
+    "nvfp4_256x512x512_r32": lambda: synth.svdq_layer(1004, 256, 512, 512, 32, synth.NVFP4, 0.01, 20.0),
+    "int4_ragged_200x256x1024_r32": lambda: synth.svdq_layer(7, 200, 256, 1024, 32, synth.INT4, 0.02, 30.0),
+    "nvfp4_ragged_37x128x768_r16": lambda: synth.svdq_layer(8, 37, 128, 768, 16, synth.NVFP4, 0.02, 30.0),
+    "int4_rank0_130x384x320": lambda: synth.svdq_layer(9, 130, 384, 320, 0, synth.INT4, 0.01, 20.0),
+    "int4_rank128_64x128x256": lambda: synth.svdq_layer(10, 64, 128, 256, 128, synth.INT4, 0.01, 20.0),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(SMALL))
+def small(request):
+    print(f"[parity] case {request.param}", flush=True)
+    return SMALL[request.param]()
+
+
+def test_quantize_small(small):
+    check_quant(small)
+
+
+def test_quantize_without_smoothing(small):
+    check_quant(small, smooth=False)
+
+
+def test_group_psums_small(small):
+    d = small
+    codes, _ = oracle.quantize_act(d["prec"], d["x"], d["lam"], alpha=d["alpha_a"])
+    P = sq.group_psums(d["prec"], dev(codes), dev(d["w_codes"]))
+    torch.cuda.synchronize()
+    ref = oracle.group_psums(d["prec"], codes, d["w_codes"])
+    got = P.cpu().numpy()
+    assert got.dtype == ref.dtype
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_gemm_small(small):
+    d = small
+    codes, scales = oracle.quantize_act(d["prec"], d["x"], d["lam"], alpha=d["alpha_a"])
+    xl1 = oracle.lowrank_down(d["x"], d["l1t"]) if d["rank"] else None
+    y = run_gemm(d, codes, scales, xl1)
+    ref = oracle_y(d, codes, scales, xl1)
+    assert max_abs_rel(y, ref) <= Y_TOL
+    yn = run_gemm(d, codes, scales, xl1, with_bias=False)
+    refn = oracle_y(d, codes, scales, xl1, with_bias=False)
+    assert max_abs_rel(yn, refn) <= Y_TOL
+
+
+def test_linear_end_to_end_small(small):
+    d = small
+    codes, scales, xl1 = check_quant(d)
+    y = run_gemm(d, codes, scales, xl1)
+    oc, os_ = oracle.quantize_act(d["prec"], d["x"], d["lam"], alpha=d["alpha_a"])
+    ox = oracle.lowrank_down(d["x"], d["l1t"]) if d["rank"] else None
+    ref = oracle_y(d, oc, os_, ox)
+    assert max_abs_rel(y, ref) <= Y_TOL
+
+
+# --------------------------------------------------------------------------- quantizer edge cases
+def _bits(a):
+    return synth.to_bf16_bits(np.asarray(a, np.float64))
+
+
+def _edge_case(prec, kind):
+    G = 64 if prec == sq.SVDQ_INT4 else 16
+    M, K = 48, 256
+    rng = np.random.default_rng(11)
+    if kind == "ties":
+        # x = (q + 1/2) * s with s a power of two: exact midpoints of the code grid
+        s = 2.0 ** rng.integers(-8, 4, size=(M, K // G))
+        q = rng.integers(-7, 7, size=(M, K)) + 0.5
+        x = q * np.repeat(s, G, axis=1)
+        x[:, ::G] = 7.0 * np.repeat(s, G, axis=1)[:, ::G]
+    elif kind == "tiny":
+        x = rng.standard_normal((M, K)) * 1e-6  # fp16-subnormal / E4M3-underflow scales
+    elif kind == "huge":
+        x = rng.standard_normal((M, K)) * 3e5  # fp16 scale saturates at 65504
+    elif kind == "zeros":
+        x = np.zeros((M, K))
+        x[1::2, :G] = rng.standard_normal((M // 2, G))
+    return dict(prec=prec, x=_bits(x), lam=None, rank=0, alpha_a=1.0 if prec == sq.SVDQ_INT4 else
+                synth.nvfp4_act_global_scale(_bits(x), None), l1t=np.zeros((0, K), np.uint16))
+
+
+@pytest.mark.parametrize("prec", [sq.SVDQ_INT4, sq.SVDQ_NVFP4])
+@pytest.mark.parametrize("kind", ["ties", "tiny", "huge", "zeros"])
+def test_quantize_edge_cases(prec, kind):
+    print(f"[parity] quantize edge {kind} prec {prec}", flush=True)
+    check_quant(_edge_case(prec, kind), smooth=False)
+
+
+def test_empty_inputs():
+    d = synth.svdq_layer(1, 0, 128, 256, 16, synth.INT4)
+    codes, scales, xl1 = sq.quantize_act(0, bf16_dev(np.zeros((0, 256), np.uint16)), None,
+                                         bf16_dev(d["l1t"]), 1.0)
+    y = sq.w4a4_gemm(0, codes, scales, dev(d["w_codes"]), f16_dev(d["w_scales"]), xl1,
+                     bf16_dev(d["l2t"]), None)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 128)
+
+
+# --------------------------------------------------------------------------- AWQ
+AWQ = {
+    "awq_2x18432x3072": lambda: synth.awq_layer(1005, 2, 18432, 3072),
+    "awq_1x512x512": lambda: synth.awq_layer(21, 1, 512, 512),
+    "awq_5x1024x1024_nobias": lambda: synth.awq_layer(22, 5, 1024, 1024, with_bias=False),
+    "awq_64x1024x3072": lambda: synth.awq_layer(23, 64, 1024, 3072),
+    "awq_2x256x5120": lambda: synth.awq_layer(24, 2, 256, 5120),
+}
+
+
+@pytest.mark.parametrize("name", sorted(AWQ))
+def test_awq(name):
+    print(f"[parity] {name}", flush=True)
+    d = AWQ[name]()
+    y = sq.awq_gemv(bf16_dev(d["x"]), dev(d["w_codes"]), f16_dev(d["w_scales"]), f16_dev(d["w_zeros"]),
+                    bf16_dev(d["bias"]) if d["bias"] is not None else None)
+    torch.cuda.synchronize()
+    ref, _ = oracle.awq_linear(d["x"], d["w_codes"], d["w_scales"], d["w_zeros"], d["bias"])
+    assert max_abs_rel(host_bits(y), ref) <= Y_TOL
+
+
+def test_awq_modulation_m64_sampled():
+    d = synth.awq_layer(1005, 64, 18432, 3072)
+    y = sq.awq_gemv(bf16_dev(d["x"]), dev(d["w_codes"]), f16_dev(d["w_scales"]), f16_dev(d["w_zeros"]),
+                    bf16_dev(d["bias"]))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = rng.integers(0, 64, 4096)
+    cols = rng.integers(0, 18432, 4096)
+    ref, _ = oracle.awq_linear(d["x"], d["w_codes"], d["w_scales"], d["w_zeros"], d["bias"], rows=rows, cols=cols)
+    yb = host_bits(y)[rows, cols]
+    assert max_abs_rel(yb, ref) <= Y_TOL
