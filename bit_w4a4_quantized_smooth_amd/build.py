@@ -1,6 +1,7 @@
 """Builds libsvdq.so (the gfx950 HIP kernels and their C ABI) in-tree.
 
 Every HIP source is compiled for gfx950 only, with
+  * matrix-core instructions in their VGPR form,
   * packed-fp32 instructions disabled (the compiler would otherwise form
     v_pk_*_f32 from plain float code),
   * IEEE-correct fp32 division and fp32 denormals kept, because the
@@ -19,6 +20,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
+    # matrix-core results land in VGPRs, where the vector ALU reads them
+    # directly (the AGPR form would need a v_accvgpr_read per element)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

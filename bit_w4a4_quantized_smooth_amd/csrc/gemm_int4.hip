@@ -6,26 +6,84 @@
 //   y[m,n] = sum_g sa[m,g] * sw[n,g] * P[m,n,g] + sum_j XL1[m,j] L2[j,n] + bias[n]
 //   P[m,n,g] = sum_{k in g} qa[m,k] * qw[n,k]                    (exact int32)
 //
-// Tiling: a 256-thread workgroup computes a 128(n) x 128(m) tile of Y^T; each
-// wave64 owns 64x64 = 2x2 blocks of v_mfma_i32_32x32x32_i8.  The matrix-core
-// A operand is the weight tile (rows n) and B the activation tile (columns m),
-// so every lane ends up holding one output row m and runs of four adjacent n:
-// the bf16 epilogue writes 8-byte pieces of Y rows.
-//
-// Per 64-channel group the workgroup stages both 128x64 code tiles through
-// LDS (double buffered).  Nibbles are expanded while staging: the two's
-// complement nibble placed in the high half of a byte is the int8 value 16*q,
-// obtained with a mask (odd channels) or a shift and mask (even channels), no
-// sign extension.  Both operands get the same channel permutation, so the
-// group dot product is unchanged and the matrix core returns 256*P exactly.
+// gfx950 design
+// -------------
+// * Workgroup = 8 wave64 (two per SIMD, so one wave's matrix-core work
+//   overlaps the other's vector ALU work) computing a 256(n) x 128(m) tile of
+//   Y^T; each wave owns 64x64 = 2x2 blocks of 32x32.  The matrix-core A operand
+//   is the weight tile (rows n) and B the activation tile (columns m): every
+//   lane ends up with one output row m and runs of four adjacent n, so the
+//   bf16 epilogue writes 8-byte pieces of Y rows.
+// * Two 64-channel groups per pipeline stage: each row contributes a 64-byte
+//   segment of packed codes (four 16-byte loads per row, consecutive lanes).
+//   While staging to LDS the nibbles are expanded to int8 16*q: the two's
+//   complement nibble in the high half of a byte is 16*q exactly (one mask for
+//   odd channels, one shift and mask for even ones, no sign extension).  Both
+//   operands get the same channel permutation, so P is unchanged and the
+//   matrix core (v_mfma_i32_32x32x32_i8) returns 256*P.
+// * int32 -> fp32 without a conversion instruction: each group's MFMA chain
+//   starts from the accumulator bit pattern of c0 = 1/(2 pi) (an inline
+//   constant, so no registers), whose mantissa leaves more than 2^20 of
+//   head-room on both sides; the integer sum bits(c0) + 256*P is therefore the
+//   float c0 + P*2^-18 exactly.
+// * The per-group scale product S = sw (x) sa is an outer product; it is
+//   computed on the matrix core by v_mfma_f32_32x32x1_2b_f32, which takes the
+//   two 32-lane halves as two independent blocks (one fp32 per lane: two
+//   32-row weight blocks against one 32-column activation block), leaving one
+//   VALU FMA per output per group: acc += S * (c0 + P*2^-18).  The epilogue
+//   removes the constant: y = 2^18 * (acc - c0 * sum_g S), where
+//   sum_g S = Sw . Sa^T is one small K = #groups fp16 GEMM on the matrix core
+//   (fp16 x fp16 products are exact in fp32).
+// * Operand loads are raw buffer loads: rows past the end of a tensor read as
+//   zero in hardware, so the M and N tails need no per-lane predication.
+// * Tiles are ordered so that each XCD (own L2) works on a contiguous range:
+//   neighbouring tiles share weight panels in that XCD's L2.
 #include "common.h"
 #include "launch.h"
 
 namespace svdq {
 
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v32f __attribute__((ext_vector_type(32)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+
+// Tile configuration: WAVES_N x WAVES_M waves, each owning a (16*BI) x (16*BJ)
+// tile of 16x16 blocks; KG 64-channel groups per pipeline stage.
+#ifndef SVDQ_INT4_CFG
+#define SVDQ_INT4_CFG 0
+#endif
+#if SVDQ_INT4_CFG == 0
+constexpr int WAVES_N = 2, WAVES_M = 2, BI = 4, BJ = 4, KG = 2;
+#elif SVDQ_INT4_CFG == 1
+constexpr int WAVES_N = 2, WAVES_M = 2, BI = 8, BJ = 4, KG = 2;
+#elif SVDQ_INT4_CFG == 2
+constexpr int WAVES_N = 2, WAVES_M = 2, BI = 4, BJ = 8, KG = 2;
+#elif SVDQ_INT4_CFG == 3
+constexpr int WAVES_N = 4, WAVES_M = 2, BI = 4, BJ = 4, KG = 2;
+#endif
+
 namespace {
-constexpr int BM = 128, BN = 128;
-constexpr int LDS_ROW = 80;  // 64 int8 channels + 16 bytes of padding per row
+constexpr int BN = WAVES_N * BI * 16, BM = WAVES_M * BJ * 16;
+constexpr int NT = WAVES_N * WAVES_M * 64;
+constexpr int PARTS = 2 * KG;                       // 16-byte code parts per row per stage
+constexpr int ROWB = 64 * KG + 16;                  // LDS bytes per operand row (int8) incl. padding
+constexpr int NROWS = BN + BM;                      // W rows then X rows in one LDS stage
+constexpr int CHUNKS = NROWS * PARTS / NT;          // 16-byte loads per thread per stage
+constexpr int SROWS = (NROWS + NT - 1) / NT;        // scale rows per thread
+constexpr int STAGE = NROWS * ROWB;                 // bytes of one stage of operands
+constexpr int SC_STAGE = NROWS * KG;                // fp32 scales of one stage
+constexpr size_t LDS_BYTES = 2 * (size_t)STAGE + 2 * (size_t)SC_STAGE * 4;
+// The integer accumulator starts from the bit pattern of the fp32 number
+// c0 = 0x3E22F983 (the inline constant 1/(2 pi)), whose mantissa leaves more
+// than 2^20 of head-room on both sides: the integer sum c0_bits + 256*P is the
+// float c0 + P * 2^-18 exactly (|256 P| <= 2^20).
+constexpr int kMagicBits = 0x3E22F983;
+constexpr float kMagicScale = 262144.0f;            // 2^18
+constexpr uint32_t kBufDword3 = 0x00020000u;        // raw buffer, 32-bit data format
+static_assert(NROWS * PARTS % NT == 0, "stage loads must divide evenly");
+static_assert(BN % 128 == 0, "weight tile in halves of 128 rows");
+static_assert(BI % 2 == 0 && BJ % 2 == 0, "scale outer products cover 2x2 quads of blocks");
 
 __device__ __forceinline__ uint4 nib_lo16(uint4 v) {  // 16*q of even channels
   return uint4{(v.x << 4) & 0xF0F0F0F0u, (v.y << 4) & 0xF0F0F0F0u, (v.z << 4) & 0xF0F0F0F0u,
@@ -34,181 +92,387 @@ __device__ __forceinline__ uint4 nib_lo16(uint4 v) {  // 16*q of even channels
 __device__ __forceinline__ uint4 nib_hi16(uint4 v) {  // 16*q of odd channels
   return uint4{v.x & 0xF0F0F0F0u, v.y & 0xF0F0F0F0u, v.z & 0xF0F0F0F0u, v.w & 0xF0F0F0F0u};
 }
+
+// 8 fp16 scales of one row starting at group kb (zero past the last group).
+// Rows of 8k groups are 16-byte aligned: one vector load.
+__device__ __forceinline__ v8h load_scales8(const uint16_t* row, int kb, int G) {
+  if ((G & 7) == 0) return kb < G ? *(const v8h*)(row + kb) : __builtin_bit_cast(v8h, uint4{0u, 0u, 0u, 0u});
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = kb + 2 * i < G ? row[kb + 2 * i] : 0u;
+    const uint32_t hi = kb + 2 * i + 1 < G ? row[kb + 2 * i + 1] : 0u;
+    w[i] = lo | (hi << 16);
+  }
+  return __builtin_bit_cast(v8h, uint4{w[0], w[1], w[2], w[3]});
+}
 }  // namespace
 
 template <int MODE>  // 0: Y = bf16 linear output; 1: int32 partial products
-__global__ __launch_bounds__(256) void gemm_int4_kernel(
+__global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
     int M, int N, int K, int rank, const uint8_t* __restrict__ ac, const uint16_t* __restrict__ as,
     const uint8_t* __restrict__ wc, const uint16_t* __restrict__ ws, const float* __restrict__ xl1,
     const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
     int32_t* __restrict__ psums) {
-  __shared__ __align__(16) uint8_t sW[2][BN * LDS_ROW];
-  __shared__ __align__(16) uint8_t sX[2][BM * LDS_ROW];
-  __shared__ __align__(16) float sSW[2][BN];
-  __shared__ __align__(16) float sSA[2][BM];
+  extern __shared__ __align__(16) uint8_t smem[];
+  float* ssc = (float*)(smem + 2 * STAGE);  // [2][KG][NROWS] fp32 scales
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int m_tiles = (M + BM - 1) / BM;
-  const int mt = blockIdx.x % m_tiles, nt = blockIdx.x / m_tiles;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const int wn = (wave >> 1) * 64, wm = (wave & 1) * 64;
+  const int l16 = lane & 15, lg = lane >> 4;  // lane within a 16-lane group, group 0..3
+
+  // XCD-aware tile order: consecutive workgroup ids go round-robin over the 8
+  // XCDs; give each XCD a contiguous block of tiles (m fastest).
+  const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;  // N % 128 == 0
+  const int tiles = m_tiles * n_tiles;
+  int t = blockIdx.x;
+  if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
+  const int m0 = (t % m_tiles) * BM, n0 = (t / m_tiles) * BN;
+  const int wn = (wave / WAVES_M) * (BI * 16), wm = (wave % WAVES_M) * (BJ * 16);
   const int G = K >> 6;
-  const size_t rowb = (size_t)(K >> 1);
+  const int stages = (G + KG - 1) / KG;
+  const int rowb = K >> 1;
 
-  // staging: thread -> (row, 16-byte half of the 32-byte group slice)
-  const int srow = tid >> 1, shalf = tid & 1;
-  const uint8_t* wsrc = wc + (size_t)(n0 + srow) * rowb + shalf * 16;
-  const bool xvalid = (m0 + srow) < M;
-  const uint8_t* xsrc = ac + (size_t)(xvalid ? m0 + srow : 0) * rowb + shalf * 16;
-  const int srow_s = tid & 127;
-  const bool s_is_w = tid < 128;
-  const bool s_valid = s_is_w || (m0 + srow_s) < M;
-  const uint16_t* ssrc = MODE == 1 ? nullptr
-                         : s_is_w ? ws + (size_t)(n0 + srow_s) * G
-                                  : as + (size_t)(s_valid ? m0 + srow_s : 0) * G;
+  // Buffer resources: reads past the last row return zeros (the M and N tails).
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wc, (short)0, N * rowb, kBufDword3);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)ac, (short)0, M * rowb, kBufDword3);
+  const __amdgpu_buffer_rsrc_t wsres = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, MODE == 0 ? N * G * 2 : 0, kBufDword3);
+  const __amdgpu_buffer_rsrc_t asres = __builtin_amdgcn_make_buffer_rsrc((void*)as, (short)0, MODE == 0 ? M * G * 2 : 0, kBufDword3);
 
-  v16f acc[2][2];
+  // staging: chunk c = tid + NT*r -> (row c / PARTS, 16-byte part c % PARTS);
+  // rows [0, BN) are weight rows n0+row, rows [BN, NROWS) activation rows.
+  const int part = tid % PARTS;  // the same for every chunk of this thread (NT % PARTS == 0)
+  int coff[CHUNKS];              // byte offset of the chunk in its tensor at stage 0
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int r = 0; r < CHUNKS; ++r) {
+    const int row = (tid + NT * r) / PARTS;
+    coff[r] = row < BN ? (n0 + row) * rowb + part * 16 : (m0 + row - BN) * rowb + part * 16;
+  }
+  int soff[SROWS];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  for (int r = 0; r < SROWS; ++r) {
+    const int row = tid + NT * r;
+    soff[r] = row < BN ? (n0 + row) * G * 2 : (m0 + row - BN) * G * 2;
+  }
 
-  uint4 wv, xv;
-  float sv = 0.0f;
-  auto gload = [&](int g) {
-    wv = *(const uint4*)(wsrc + g * 32);
-    xv = xvalid ? *(const uint4*)(xsrc + g * 32) : uint4{0u, 0u, 0u, 0u};
-    if constexpr (MODE == 0) sv = s_valid ? f16_bits_to_f32(ssrc[g]) : 0.0f;
+  uint4 rc[CHUNKS];
+  uint32_t rs[SROWS][KG];  // raw fp16 bits: converted only at the LDS store, so
+                           // no instruction waits on these loads before then
+  auto gload = [&](int s) {
+    // channel bytes of this stage; a partial last stage (odd number of
+    // groups) skips its missing group with a wave-uniform test
+    const int kbyte = s * 32 * KG;
+    const bool full = kbyte + 32 * KG <= rowb;
+#pragma unroll
+    for (int r = 0; r < CHUNKS; ++r) {
+      const bool is_w = (tid + NT * r) / PARTS < BN;
+      if (full || kbyte + part * 16 < rowb)
+        rc[r] = __builtin_bit_cast(uint4, is_w ? __builtin_amdgcn_raw_buffer_load_b128(wres, coff[r] + kbyte, 0, 0)
+                                               : __builtin_amdgcn_raw_buffer_load_b128(xres, coff[r] + kbyte, 0, 0));
+      else
+        rc[r] = uint4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (MODE == 0) {
+#pragma unroll
+      for (int r = 0; r < SROWS; ++r) {
+        const int row = tid + NT * r;
+#pragma unroll
+        for (int gg = 0; gg < KG; ++gg) {
+          const int g = s * KG + gg;
+          uint32_t h = 0u;
+          if (row < NROWS && g < G)
+            h = row < BN ? __builtin_amdgcn_raw_buffer_load_b16(wsres, soff[r] + 2 * g, 0, 0)
+                         : __builtin_amdgcn_raw_buffer_load_b16(asres, soff[r] + 2 * g, 0, 0);
+          rs[r][gg] = h;
+        }
+      }
+    }
   };
   auto sstore = [&](int buf) {
-    uint8_t* dw = &sW[buf][srow * LDS_ROW + shalf * 32];
-    *(uint4*)dw = nib_lo16(wv);
-    *(uint4*)(dw + 16) = nib_hi16(wv);
-    uint8_t* dx = &sX[buf][srow * LDS_ROW + shalf * 32];
-    *(uint4*)dx = nib_lo16(xv);
-    *(uint4*)(dx + 16) = nib_hi16(xv);
+    uint8_t* base = smem + buf * STAGE;
+#pragma unroll
+    for (int r = 0; r < CHUNKS; ++r) {
+      const int row = (tid + NT * r) / PARTS;
+      uint8_t* dst = base + row * ROWB + part * 32;
+      *(uint4*)dst = nib_lo16(rc[r]);
+      *(uint4*)(dst + 16) = nib_hi16(rc[r]);
+    }
     if constexpr (MODE == 0) {
-      if (s_is_w) sSW[buf][srow_s] = sv;
-      else sSA[buf][srow_s] = sv * (1.0f / 256.0f);  // undo the 16*16 code scaling
+#pragma unroll
+      for (int r = 0; r < SROWS; ++r) {
+        const int row = tid + NT * r;
+        if (row < NROWS) {
+#pragma unroll
+          for (int gg = 0; gg < KG; ++gg) ssc[buf * SC_STAGE + gg * NROWS + row] = f16_bits_to_f32(rs[r][gg]);
+        }
+      }
     }
   };
 
-  const int lr = lane & 31, lh = lane >> 5;
+  v4f acc[BI][BJ];
+#pragma unroll
+  for (int i = 0; i < BI; ++i)
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4i cinit;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) cinit[v] = MODE == 0 ? kMagicBits : 0;
+  const v16f zero16 = {};
+
+  // Pipeline buffers: the 2x2 quads of 16x16 blocks alternate between two
+  // sets of (four group products 256*P + c0 bits, one 4-block scale product).
+  constexpr int NQ = BI * BJ / 4;
+  static_assert(NQ % 2 == 0, "quads alternate between two buffer sets");
+  v4i dbuf[2][4];
+  v16f sbuf[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dbuf[h][q] = v4i{0, 0, 0, 0};
+    sbuf[h] = zero16;
+  }
+
   gload(0);
   sstore(0);
   __syncthreads();
 
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    if (g + 1 < G) gload(g + 1);
-
-    v4i a[2][2], b[2][2];
+  for (int s = 0; s < stages; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < stages) gload(s + 1);
+    const uint8_t* base = smem + buf * STAGE;
+#pragma unroll 1
+    for (int gg = 0; gg < KG; ++gg) {
+      const int g = s * KG + gg;
+      // operand fragments of v_mfma_i32_16x16x64_i8: lane = (row l16 of the
+      // block, channels 16*lg .. +16 of the group)
+      v4i a[BI], b[BJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < BI; ++i)
+        a[i] = *(const v4i*)(base + (wn + 16 * i + l16) * ROWB + 64 * gg + 16 * lg);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        a[i][h] = *(const v4i*)&sW[buf][(wn + 32 * i + lr) * LDS_ROW + 32 * h + 16 * lh];
-        b[i][h] = *(const v4i*)&sX[buf][(wm + 32 * i + lr) * LDS_ROW + 32 * h + 16 * lh];
-      }
-
+      for (int j = 0; j < BJ; ++j)
+        b[j] = *(const v4i*)(base + (BN + wm + 16 * j + l16) * ROWB + 64 * gg + 16 * lg);
+      if constexpr (MODE == 1) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      float swv[16];
+        for (int i = 0; i < BI; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(float4*)&swv[4 * q] = *(const float4*)&sSW[buf][wn + 32 * i + 8 * q + 4 * lh];
+          for (int j = 0; j < BJ; ++j) {
+            const v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], cinit, 0, 0, 0);
+            const int m = m0 + wm + 16 * j + l16;
+            if (m < M && g < G && n0 + wn < N) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        v16i d = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-        d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i][0], b[j][0], d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i][1], b[j][1], d, 0, 0, 0);
-        if constexpr (MODE == 1) {
-          const int m = m0 + wm + 32 * j + lr;
-          if (m < M) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int n = n0 + wn + 32 * i + 8 * (v >> 2) + 4 * lh + (v & 3);
-              psums[((size_t)m * N + n) * G + g] = d[v] >> 8;
+              for (int v = 0; v < 4; ++v) {
+                const int n = n0 + wn + 16 * i + 4 * lg + v;
+                psums[((size_t)m * N + n) * G + g] = d[v] >> 8;
+              }
             }
           }
-        } else {
-          const float sa = sSA[buf][wm + 32 * j + lr];
+      } else {
+        // Quads Q = (qi, qj) of 2x2 blocks: lane group b of the 4-block scale
+        // product v_mfma_f32_16x16x1_4b_f32 is block (2qi + b/2, 2qj + b%2), so
+        // this lane supplies the weight scale of row l16 of block row 2qi + lg/2
+        // and the activation scale of column l16 of block column 2qj + lg%2.
+        // Step Q issues the quad's five matrix instructions and retires quad
+        // Q-1 (16 FMAs, independent of what was just issued); the last quad of
+        // a group retires at the first step of the next group (the buffers
+        // start at zero, so the first retire adds 0 * 0).
+        const float* sc = ssc + buf * SC_STAGE + gg * NROWS;
+        float swq[BI / 2], saq[BJ / 2];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf((float)d[v], swv[v] * sa, acc[i][j][v]);
+        for (int qi = 0; qi < BI / 2; ++qi) swq[qi] = sc[wn + 16 * (2 * qi + (lg >> 1)) + l16];
+#pragma unroll
+        for (int qj = 0; qj < BJ / 2; ++qj) saq[qj] = sc[BN + wm + 16 * (2 * qj + (lg & 1)) + l16];
+#pragma unroll
+        for (int Q = 0; Q < NQ; ++Q) {
+          const int qi = Q / (BJ / 2), qj = Q % (BJ / 2);
+          sbuf[Q & 1] = __builtin_amdgcn_mfma_f32_16x16x1f32(swq[qi], saq[qj], zero16, 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dbuf[Q & 1][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[2 * qi + (q >> 1)], b[2 * qj + (q & 1)], cinit, 0, 0, 0);
+          const int Qp = Q == 0 ? NQ - 1 : Q - 1;
+          const int pi = Qp / (BJ / 2), pj = Qp % (BJ / 2);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[2 * pi + (q >> 1)][2 * pj + (q & 1)][v] =
+                  fmaf(sbuf[Qp & 1][4 * q + v], __int_as_float(dbuf[Qp & 1][q][v]),
+                       acc[2 * pi + (q >> 1)][2 * pj + (q & 1)][v]);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-
-    if (g + 1 < G) sstore(buf ^ 1);
+    if (s + 1 < stages) sstore(buf ^ 1);
     __syncthreads();
   }
 
   if constexpr (MODE == 0) {
-    // low-rank up-projection on the bf16 matrix cores: acc += L2^T[n, :] . XL1[m, :]
-    for (int jb = 0; jb < rank; jb += 16) {
-      v8bf al[2], bl[2];
+    {  // retire the last quad of the last group
+      constexpr int Qp = NQ - 1;
+      constexpr int pi = Qp / (BJ / 2), pj = Qp % (BJ / 2);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        al[i] = *(const v8bf*)(l2t + (size_t)(n0 + wn + 32 * i + lr) * rank + jb + 8 * lh);
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int m = m0 + wm + 32 * j + lr;
-        uint4 pk = {0u, 0u, 0u, 0u};
-        if (m < M) {
-          const float4* src = (const float4*)(xl1 + (size_t)m * rank + jb + 8 * lh);
-          const float4 f0 = src[0], f1 = src[1];
-          pk.x = f32_to_bf16_bits(f0.x) | (f32_to_bf16_bits(f0.y) << 16);
-          pk.y = f32_to_bf16_bits(f0.z) | (f32_to_bf16_bits(f0.w) << 16);
-          pk.z = f32_to_bf16_bits(f1.x) | (f32_to_bf16_bits(f1.y) << 16);
-          pk.w = f32_to_bf16_bits(f1.z) | (f32_to_bf16_bits(f1.w) << 16);
+        for (int v = 0; v < 4; ++v)
+          acc[2 * pi + (q >> 1)][2 * pj + (q & 1)][v] =
+              fmaf(sbuf[Qp & 1][4 * q + v], __int_as_float(dbuf[Qp & 1][q][v]),
+                   acc[2 * pi + (q >> 1)][2 * pj + (q & 1)][v]);
+    }
+    // Epilogue.  Every global load it needs (bias, the scale rows of the
+    // sum_g S product, the first low-rank slices) is issued before any of them
+    // is consumed, so the workgroup pays one memory latency here, not several.
+    uint2 bb[BI];
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int n = n0 + wn + 16 * i + 4 * lg;
+      bb[i] = (bias && n < N) ? *(const uint2*)(bias + n) : uint2{0u, 0u};
+    }
+    auto load_ts = [&](int kb, v8h* aw, v8h* bx) {
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const int n = n0 + wn + 16 * i + l16;
+        aw[i] = n < N ? load_scales8(ws + (size_t)n * G, kb + 8 * lg, G)
+                      : __builtin_bit_cast(v8h, uint4{0u, 0u, 0u, 0u});
+      }
+#pragma unroll
+      for (int j = 0; j < BJ; ++j) {
+        const int m = m0 + wm + 16 * j + l16;
+        bx[j] = m < M ? load_scales8(as + (size_t)m * G, kb + 8 * lg, G)
+                      : __builtin_bit_cast(v8h, uint4{0u, 0u, 0u, 0u});
+      }
+    };
+    auto load_lr = [&](int jb, v8bf* al, float4* xf) {
+      const bool live = jb + 8 * lg < rank;  // rank 16 leaves lane groups 2, 3 empty
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const int n = n0 + wn + 16 * i + l16;
+        al[i] = (live && n < N) ? *(const v8bf*)(l2t + (size_t)n * rank + jb + 8 * lg)
+                                : __builtin_bit_cast(v8bf, uint4{0u, 0u, 0u, 0u});
+      }
+#pragma unroll
+      for (int j = 0; j < BJ; ++j) {
+        const int m = m0 + wm + 16 * j + l16;
+        if (live && m < M) {
+          const float4* src4 = (const float4*)(xl1 + (size_t)m * rank + jb + 8 * lg);
+          xf[2 * j] = src4[0];
+          xf[2 * j + 1] = src4[1];
+        } else {
+          xf[2 * j] = float4{0.f, 0.f, 0.f, 0.f};
+          xf[2 * j + 1] = float4{0.f, 0.f, 0.f, 0.f};
         }
+      }
+    };
+    v8h aw[2][BI], bx[2][BJ];
+    v8bf al[BI];
+    float4 xf[2 * BJ];
+    load_ts(0, aw[0], bx[0]);
+    if (G > 32) load_ts(32, aw[1], bx[1]);
+    if (rank > 0) load_lr(0, al, xf);
+
+    // sum_g S = Sw . Sa^T on the matrix core (v_mfma_f32_16x16x32_f16, K = 32
+    // groups per instruction), then y = 2^18 * (acc - c0 * sum_g S)
+    const float c0 = __int_as_float(kMagicBits);
+    const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < G; kb += 64) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (kb + 32 * h >= G) break;
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+#pragma unroll
+          for (int j = 0; j < BJ; ++j) {
+            const v4f T = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[h][i], bx[h][j], zero4, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(-c0, T[v], acc[i][j][v]);
+          }
+      }
+      if (kb + 64 < G) load_ts(kb + 64, aw[0], bx[0]);
+      if (kb + 96 < G) load_ts(kb + 96, aw[1], bx[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+#pragma unroll
+      for (int j = 0; j < BJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][v] *= kMagicScale;
+
+    // low-rank up-projection on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16):
+    // acc += L2^T[n, :] . XL1[m, :]; lane = (row l16, rank entries 8*lg .. +8)
+    for (int jb = 0; jb < rank; jb += 32) {
+      if (jb > 0) load_lr(jb, al, xf);
+      v8bf bl[BJ];
+#pragma unroll
+      for (int j = 0; j < BJ; ++j) {
+        const float4 f0 = xf[2 * j], f1 = xf[2 * j + 1];
+        uint4 pk;
+        pk.x = f32_to_bf16_bits(f0.x) | (f32_to_bf16_bits(f0.y) << 16);
+        pk.y = f32_to_bf16_bits(f0.z) | (f32_to_bf16_bits(f0.w) << 16);
+        pk.z = f32_to_bf16_bits(f1.x) | (f32_to_bf16_bits(f1.y) << 16);
+        pk.w = f32_to_bf16_bits(f1.z) | (f32_to_bf16_bits(f1.w) << 16);
         bl[j] = __builtin_bit_cast(v8bf, pk);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < BI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bl[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < BJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bl[j], acc[i][j], 0, 0, 0);
     }
-    // bias, bf16 rounding, 8-byte stores of four adjacent n
+
+    // bias, bf16 rounding, then the wave's tile goes through LDS (free after
+    // the main loop) so that each store instruction writes whole 128-byte row
+    // segments of Y: lane l of a store covers row l/8, bytes 16*(l%8) .. +16.
+    constexpr int TROW = BI * 16 * 2 + 16;  // bytes per LDS row of the wave tile (+ pad)
+    uint8_t* tile = smem + wave * (BJ * 16) * TROW;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < BI; ++i) {
+      const float b0 = bf16_bits_to_f32(bb[i].x & 0xFFFFu), b1 = bf16_bits_to_f32(bb[i].x >> 16);
+      const float b2 = bf16_bits_to_f32(bb[i].y & 0xFFFFu), b3 = bf16_bits_to_f32(bb[i].y >> 16);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int m = m0 + wm + 32 * j + lr;
-        if (m >= M) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn + 32 * i + 8 * q + 4 * lh;
-          float bv[4] = {0.f, 0.f, 0.f, 0.f};
-          if (bias) {
-            const uint2 bb = *(const uint2*)(bias + n);
-            bv[0] = bf16_bits_to_f32(bb.x & 0xFFFFu);
-            bv[1] = bf16_bits_to_f32(bb.x >> 16);
-            bv[2] = bf16_bits_to_f32(bb.y & 0xFFFFu);
-            bv[3] = bf16_bits_to_f32(bb.y >> 16);
-          }
-          uint2 o;
-          o.x = f32_to_bf16_bits(acc[i][j][4 * q] + bv[0]) | (f32_to_bf16_bits(acc[i][j][4 * q + 1] + bv[1]) << 16);
-          o.y = f32_to_bf16_bits(acc[i][j][4 * q + 2] + bv[2]) | (f32_to_bf16_bits(acc[i][j][4 * q + 3] + bv[3]) << 16);
-          *(uint2*)(y + (size_t)m * N + n) = o;
-        }
+      for (int j = 0; j < BJ; ++j) {
+        uint2 o;
+        o.x = f32_to_bf16_bits(acc[i][j][0] + b0) | (f32_to_bf16_bits(acc[i][j][1] + b1) << 16);
+        o.y = f32_to_bf16_bits(acc[i][j][2] + b2) | (f32_to_bf16_bits(acc[i][j][3] + b3) << 16);
+        *(uint2*)(tile + (16 * j + l16) * TROW + (16 * i + 4 * lg) * 2) = o;
       }
+    }
+    if (n0 + wn < N) {
+      constexpr int LPR = BI * 16 * 2 / 16;  // lanes per tile row (16 bytes each)
+      constexpr int RPI = 64 / LPR;          // tile rows per store instruction
+#pragma unroll
+      for (int r0 = 0; r0 < BJ * 16; r0 += RPI) {
+        const int r = r0 + lane / LPR, c = lane % LPR;
+        const uint4 v = *(const uint4*)(tile + r * TROW + c * 16);
+        const int m = m0 + wm + r;
+        if (m < M) *(uint4*)(y + (size_t)m * N + n0 + wn + c * 8) = v;
+      }
+    }
   }
 }
 
 hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
   const int m_tiles = (int)((a.M + BM - 1) / BM);
-  const int blocks = m_tiles * (int)(a.N / BN);
+  const int blocks = m_tiles * (int)((a.N + BN - 1) / BN);
+  auto k0 = gemm_int4_kernel<0>;
+  auto k1 = gemm_int4_kernel<1>;
+  hipError_t e = hipFuncSetAttribute((const void*)(a.psums ? k1 : k0),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+  if (e != hipSuccess) return e;
   if (a.psums) {
-    hipLaunchKernelGGL(gemm_int4_kernel<1>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
-                       (int)a.K, 0, (const uint8_t*)a.act_codes, nullptr, (const uint8_t*)a.w_codes,
-                       nullptr, nullptr, nullptr, nullptr, nullptr, (int32_t*)a.psums);
+    hipLaunchKernelGGL(k1, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, 0,
+                       (const uint8_t*)a.act_codes, nullptr, (const uint8_t*)a.w_codes, nullptr, nullptr,
+                       nullptr, nullptr, nullptr, (int32_t*)a.psums);
   } else {
-    hipLaunchKernelGGL(gemm_int4_kernel<0>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
-                       (int)a.K, a.rank, (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
+    hipLaunchKernelGGL(k0, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
+                       (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
                        (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
                        (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr);
   }
