@@ -6,143 +6,156 @@
 // which equals sum_k x * (q - z) * s (the weight dequantized per group).
 //
 // Two kernels:
-//  * M <= 2 (the decode-like case that is bound by streaming the 4-bit
-//    weights): a 32-lane team owns one weight row; lane i reads the 16-byte
-//    chunks i, i+32, i+64, ... so every load instruction of the team covers
-//    512 contiguous bytes.  The lane's slice of x stays in registers for the
-//    whole kernel as bf16 pairs.  Codes become bf16 pairs with one AND-OR
-//    each: (nibble | 0x4300) is the bf16 number 128 + q, so v_dot2_f32_bf16
-//    accumulates sum x*(128+q) and the 128*sum(x) term is folded into the
-//    zero-point, z' = z + 128.
-//  * 2 < M <= 64: matrix-core kernel, see awq_gemm_mfma_kernel.
+//  * M <= 4 (the decode-like case, bound by streaming the 4-bit weights):
+//    v_mfma_f32_4x4x4_16b_bf16, whose sixteen independent 4x4 blocks fit a
+//    handful of activation rows.  Lane l = 4b + c of a wave owns weight row
+//    n0 + c and the 16-byte chunks b, b+16, b+32, ... of it (the 16 lanes of
+//    a row read 256 contiguous bytes per load), and holds activation row c
+//    of block b as the A operand.  Each 16-byte chunk (32 codes, half a
+//    group) is eight MFMAs whose block result is that chunk's partial dot
+//    product for all activation rows, scaled right away by its group's scale
+//    and zero-point.  Codes become bf16 pairs with one AND-OR each:
+//    (nibble | 0x4300) is the bf16 number 128 + q, taking the channels of a
+//    32-bit word in the order (k0,k4) (k1,k5) (k2,k6) (k3,k7); x is staged
+//    once per workgroup in LDS in that same pair order, with its per-chunk
+//    sums, and the 128*sum(x) term is folded into the zero-point, z' = z + 128.
+//  * 4 < M <= 64: matrix-core kernel, see awq_gemm_mfma_kernel.
 #include "common.h"
 #include "launch.h"
 
 namespace svdq {
 
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 
 namespace {
-constexpr int AWQ_RP = 4;   // row pairs per wave
-constexpr int AWQ_CPL = 4;  // 32-channel chunks per lane per pass (pass = 4096 channels)
+constexpr uint32_t kBufDword3 = 0x00020000u;  // raw buffer, 32-bit data format
+constexpr int kOut = 0x7FFFFFF0;              // offset past num_records: the load returns 0
+constexpr int AWQ_WAVES = 8;                  // small-M kernel: waves per workgroup
+constexpr int AWQ_ROWS = 4 * AWQ_WAVES;       // weight rows per workgroup
+constexpr int AWQ_PT = 6;                     // 512-channel blocks whose loads are issued together
 
-__device__ __forceinline__ float dot2bf(u32 a, u32 b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a), __builtin_bit_cast(v2bf, b), c, false);
+__device__ __forceinline__ v4bf as_v4bf(u32 lo, u32 hi) {
+  return __builtin_bit_cast(v4bf, uint2{lo, hi});
+}
+
+// LDS bytes of the small-M kernel: pair-permuted x and per-chunk sums.
+__host__ __device__ constexpr int awq_small_lds(int K, int MR) {
+  return ((K / 32 + 15) / 16) * MR * (64 * 16 + 16 * 4);
 }
 }  // namespace
 
 template <int MR>
-__global__ __launch_bounds__(256) void awq_gemv_kernel(
+__global__ __launch_bounds__(64 * AWQ_WAVES) void awq_gemv_kernel(
     int M, int N, int K, const uint16_t* __restrict__ x, const uint8_t* __restrict__ wc,
     const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wz,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y) {
+  extern __shared__ __align__(16) uint4 lds4[];
+  const int nchunks = K >> 5, TB = (nchunks + 15) >> 4, G = K >> 6, rowb = K >> 1;
+  uint4* xl = lds4;                        // [TB][4 words][16 blocks][MR] x pairs
+  float* xsl = (float*)(lds4 + TB * 64 * MR);  // [TB*16 chunks][MR] sums of x per chunk
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int team = lane >> 5, li = lane & 31;
-  const int n_base = (blockIdx.x * 4 + wave) * (2 * AWQ_RP);
-  const int G = K >> 6, nchunks = K >> 5;
-  const size_t rowb = (size_t)(K >> 1);
+  const int b = lane >> 2, c = lane & 3;
+  const int n = blockIdx.x * AWQ_ROWS + wave * 4 + c;  // N is a multiple of AWQ_ROWS
+  const int arow = c % MR;  // A rows past MR only feed D rows that are never read
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * K * 2, kBufDword3);
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wc, (short)0, N * rowb, kBufDword3);
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, N * G * 2, kBufDword3);
+  const __amdgpu_buffer_rsrc_t zres = __builtin_amdgcn_make_buffer_rsrc((void*)wz, (short)0, N * G * 2, kBufDword3);
 
-  float acc[AWQ_RP][MR];
+  float acc[MR];
 #pragma unroll
-  for (int p = 0; p < AWQ_RP; ++p)
-#pragma unroll
-    for (int m = 0; m < MR; ++m) acc[p][m] = 0.0f;
+  for (int v = 0; v < MR; ++v) acc[v] = 0.0f;
 
-  for (int cbase = 0; cbase < nchunks; cbase += 32 * AWQ_CPL) {
-    // this lane's x slice as (k, k+4) bf16 pairs, plus the fp32 sum per chunk
-    u32 xp[AWQ_CPL][MR][16];
-    float xs[AWQ_CPL][MR];
+  for (int t0 = 0; t0 < TB; t0 += AWQ_PT) {
+    // codes, scales and zero-points of this lane's chunks in the next AWQ_PT
+    // blocks, all in flight at once; chunks past K read as zeros
+    uint4 cv[AWQ_PT];
+    u32 sv[AWQ_PT], zv[AWQ_PT];
 #pragma unroll
-    for (int t = 0; t < AWQ_CPL; ++t) {
-      const int c = cbase + li + 32 * t;
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        xs[t][m] = 0.0f;
-#pragma unroll
-        for (int b = 0; b < 16; ++b) xp[t][m][b] = 0u;
-        if (c < nchunks && m < M) {
-          const uint4* src = (const uint4*)(x + (size_t)m * K + 32 * c);
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {  // 8 channels: words (k0,k1) (k2,k3) (k4,k5) (k6,k7)
-            const uint4 w = src[b];
-            xp[t][m][4 * b + 0] = __builtin_amdgcn_perm(w.z, w.x, 0x05040100u);  // (k0, k4)
-            xp[t][m][4 * b + 1] = __builtin_amdgcn_perm(w.z, w.x, 0x07060302u);  // (k1, k5)
-            xp[t][m][4 * b + 2] = __builtin_amdgcn_perm(w.w, w.y, 0x05040100u);  // (k2, k6)
-            xp[t][m][4 * b + 3] = __builtin_amdgcn_perm(w.w, w.y, 0x07060302u);  // (k3, k7)
-            const u32 ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              xs[t][m] += bf16_bits_to_f32(ww[q] & 0xFFFFu) + bf16_bits_to_f32(ww[q] >> 16);
-          }
-        }
-      }
+    for (int u = 0; u < AWQ_PT; ++u) {
+      const int ch = 16 * (t0 + u) + b;
+      const bool ok = ch < nchunks;
+      cv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, ok ? n * rowb + 16 * ch : kOut, 0, 0));
+      const int go = ok ? (n * G + (ch >> 1)) * 2 : kOut;
+      sv[u] = __builtin_amdgcn_raw_buffer_load_b16(sres, go, 0, 0);
+      zv[u] = __builtin_amdgcn_raw_buffer_load_b16(zres, go, 0, 0);
     }
 
-    // stream the weight rows: all loads of the wave's rows are issued first
-    uint4 wv[AWQ_RP][AWQ_CPL];
+    if (t0 == 0) {
+      // stage x while the first codes are in flight: item = (row m, chunk, word i)
+      const int items = MR * TB * 64;
+      for (int it = tid; it < items; it += 64 * AWQ_WAVES) {
+        const int i = it & 3, ch = (it >> 2) % (TB * 16), m = it / (TB * 64);
+        const bool ok = m < M && ch < nchunks;
+        const uint4 w = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, ok ? (m * K + 32 * ch + 8 * i) * 2 : kOut, 0, 0));
+        uint4 pr;
+        pr.x = __builtin_amdgcn_perm(w.z, w.x, 0x05040100u);  // (k0, k4)
+        pr.y = __builtin_amdgcn_perm(w.z, w.x, 0x07060302u);  // (k1, k5)
+        pr.z = __builtin_amdgcn_perm(w.w, w.y, 0x05040100u);  // (k2, k6)
+        pr.w = __builtin_amdgcn_perm(w.w, w.y, 0x07060302u);  // (k3, k7)
+        xl[(((ch >> 4) * 4 + i) * 16 + (ch & 15)) * MR + m] = pr;
+        const u32 ww[4] = {w.x, w.y, w.z, w.w};
+        float sm = 0.0f;
 #pragma unroll
-    for (int p = 0; p < AWQ_RP; ++p) {
-      const int n = n_base + 2 * p + team;
-#pragma unroll
-      for (int t = 0; t < AWQ_CPL; ++t) {
-        const int c = cbase + li + 32 * t;
-        wv[p][t] = (n < N && c < nchunks) ? *(const uint4*)(wc + (size_t)n * rowb + 16 * c)
-                                           : uint4{0u, 0u, 0u, 0u};
+        for (int q = 0; q < 4; ++q) sm += bf16_bits_to_f32(ww[q] & 0xFFFFu) + bf16_bits_to_f32(ww[q] >> 16);
+        sm += __shfl_xor(sm, 1, 64);  // the four words of a chunk are adjacent items
+        sm += __shfl_xor(sm, 2, 64);
+        if (i == 0) xsl[ch * MR + m] = sm;
       }
+      __syncthreads();
     }
+
 #pragma unroll
-    for (int p = 0; p < AWQ_RP; ++p) {
-      const int n = n_base + 2 * p + team;
+    for (int u = 0; u < AWQ_PT; ++u) {
+      const int t = t0 + u;
+      if (t >= TB) break;  // wave-uniform
+      const uint4* ap = xl + (t * 64 + b) * MR + arow;
+      uint4 a[4];
 #pragma unroll
-      for (int t = 0; t < AWQ_CPL; ++t) {
-        const int c = cbase + li + 32 * t;
-        if (n >= N || c >= nchunks) continue;
-        const int g = c >> 1;
-        const float s = f16_bits_to_f32(ws[(size_t)n * G + g]);
-        const float zp = f16_bits_to_f32(wz[(size_t)n * G + g]) + 128.0f;
-        const u32 d4[4] = {wv[p][t].x, wv[p][t].y, wv[p][t].z, wv[p][t].w};
-        float dot[MR];
+      for (int i = 0; i < 4; ++i) a[i] = ap[i * 16 * MR];
+      float xs[MR];
 #pragma unroll
-        for (int m = 0; m < MR; ++m) dot[m] = 0.0f;
+      for (int v = 0; v < MR; ++v) xs[v] = xsl[(16 * t + b) * MR + v];
+      const u32 d4[4] = {cv[u].x, cv[u].y, cv[u].z, cv[u].w};
+      v4f d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const u32 d = d4[b];
-          const u32 q0 = (d & 0x000F000Fu) | 0x43004300u;          // (k0, k4)
-          const u32 q1 = ((d >> 4) & 0x000F000Fu) | 0x43004300u;   // (k1, k5)
-          const u32 q2 = ((d >> 8) & 0x000F000Fu) | 0x43004300u;   // (k2, k6)
-          const u32 q3 = ((d >> 12) & 0x000F000Fu) | 0x43004300u;  // (k3, k7)
-#pragma unroll
-          for (int m = 0; m < MR; ++m) {
-            dot[m] = dot2bf(q0, xp[t][m][4 * b + 0], dot[m]);
-            dot[m] = dot2bf(q1, xp[t][m][4 * b + 1], dot[m]);
-            dot[m] = dot2bf(q2, xp[t][m][4 * b + 2], dot[m]);
-            dot[m] = dot2bf(q3, xp[t][m][4 * b + 3], dot[m]);
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < MR; ++m) acc[p][m] = fmaf(s, fmaf(-zp, xs[t][m], dot[m]), acc[p][m]);
+      for (int i = 0; i < 4; ++i) {
+        const u32 w = d4[i];
+        const u32 q0 = (w & 0x000F000Fu) | 0x43004300u;          // (k0, k4)
+        const u32 q1 = ((w >> 4) & 0x000F000Fu) | 0x43004300u;   // (k1, k5)
+        const u32 q2 = ((w >> 8) & 0x000F000Fu) | 0x43004300u;   // (k2, k6)
+        const u32 q3 = ((w >> 12) & 0x000F000Fu) | 0x43004300u;  // (k3, k7)
+        d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(as_v4bf(a[i].x, a[i].y), as_v4bf(q0, q1), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(as_v4bf(a[i].z, a[i].w), as_v4bf(q2, q3), d, 0, 0, 0);
       }
+      // a chunk past K read a zero scale (and x is zero there): it adds 0
+      const float s = f16_bits_to_f32(sv[u]);
+      const float zp = f16_bits_to_f32(zv[u]) + 128.0f;
+#pragma unroll
+      for (int v = 0; v < MR; ++v) acc[v] = fmaf(s, fmaf(-zp, xs[v], d[v]), acc[v]);
     }
   }
 
-  // team reduction and store
+  // sum over the 16 blocks (lanes c, c+4, ..., c+60), then lanes 0..3 store
 #pragma unroll
-  for (int p = 0; p < AWQ_RP; ++p) {
-    const int n = n_base + 2 * p + team;
+  for (int v = 0; v < MR; ++v) {
+    float r = acc[v];
+    r += __shfl_xor(r, 4, 64);
+    r += __shfl_xor(r, 8, 64);
+    r += __shfl_xor(r, 16, 64);
+    r += __shfl_xor(r, 32, 64);
+    acc[v] = r;
+  }
+  if (b == 0) {
+    const float bv = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      float v = acc[p][m];
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-      if (li == 0 && n < N && m < M) {
-        if (bias) v += bf16_bits_to_f32(bias[n]);
-        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
-      }
-    }
+    for (int v = 0; v < MR; ++v)
+      if (v < M) y[(size_t)v * N + n] = (uint16_t)f32_to_bf16_bits(acc[v] + bv);
   }
 }
 
-// 2 < M <= 64: D[m][n] = sum_k x[m,k] * q[n,k] per 64-channel group on the bf16
+// 4 < M <= 64 (or a K too long for the small kernel's LDS): D[m][n] = sum_k x[m,k] * q[n,k] per 64-channel group on the bf16
 // matrix cores (both operands exact in bf16), then in fp32
 //   acc[m][n] += s[n,g] * (P[m][n] - z[n,g] * xsum[m,g]).
 // Workgroup: 64 weight rows x all (<= 64, zero padded) activation rows; wave w
@@ -235,11 +248,11 @@ __global__ __launch_bounds__(256) void awq_gemm_mfma_kernel(
 
 hipError_t launch_awq(const AwqArgs& a, hipStream_t st) {
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
-  if (M <= 2) {
-    const int rows_per_block = 4 * 2 * AWQ_RP;
-    const int blocks = (N + rows_per_block - 1) / rows_per_block;
-    auto kern = M == 1 ? awq_gemv_kernel<1> : awq_gemv_kernel<2>;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, st, M, N, K, (const uint16_t*)a.x,
+  const int MR = M <= 1 ? 1 : M <= 2 ? 2 : 4;
+  const int lds = awq_small_lds(K, MR);
+  if (M <= 4 && lds <= 64 * 1024) {
+    auto kern = MR == 1 ? awq_gemv_kernel<1> : MR == 2 ? awq_gemv_kernel<2> : awq_gemv_kernel<4>;
+    hipLaunchKernelGGL(kern, dim3(N / AWQ_ROWS), dim3(64 * AWQ_WAVES), lds, st, M, N, K, (const uint16_t*)a.x,
                        (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales,
                        (const uint16_t*)a.w_zeros, (const uint16_t*)a.bias, (uint16_t*)a.y);
   } else {

@@ -5,13 +5,16 @@
 // Precisions and group sizes from "Nunchaku Lite", "Supported quantization
 // types": int4 / group 64 and nvfp4 / group 16.
 //
-// Work split: one workgroup (4 wave64) owns 16 rows of X and all K.  Wave w
-// takes the 64-channel steps s = w, w+4, ...; within a step lane l holds row
+// Work split: one workgroup (16 wave64, or 8 for ranks above 32) owns 16 rows
+// of X and all K.  Wave w takes the 64-channel steps s = w, w+WAVES, ..., and
+// issues the loads of up to four of its steps (X and the L1^T slices) before
+// consuming any of them, as branch-free buffer loads (rows past M read as
+// zero).  Within a step lane l holds row
 // l % 16 and channels 16*(l/16) .. +16 (two 16-byte loads, 512 contiguous
 // bytes per row per workgroup step).  That is also the operand layout of
 // v_mfma_f32_16x16x32_bf16, so the raw bf16 X registers feed the matrix core
-// for X.L1 directly; the four waves' partial XL1 tiles are summed in LDS in a
-// fixed order.
+// for X.L1 directly; the waves' partial XL1 tiles are summed in LDS in a
+// fixed order (deterministic).
 //
 // Numerics: every quantization decision is taken in fp32 with the operations
 // written out one by one (no contraction), so codes and scales are bit-exact
@@ -27,122 +30,159 @@
 
 namespace svdq {
 
+// Eight waves per workgroup; with at most 128 VGPRs (ranks up to 32) two
+// workgroups share a CU, so a DiT-sized call (a few hundred workgroups) is
+// resident at once.  SPP steps' loads are issued together per pass; it shrinks
+// as the rank grows because each step also carries RB*2 L1^T fragments.
+template <int RB>
+struct QuantCfg {
+  static constexpr int WAVES = 8;
+  static constexpr int NT = WAVES * 64;
+  static constexpr int SPP = RB <= 1 ? 4 : RB <= 2 ? 3 : RB <= 4 ? 2 : 1;
+};
+
 template <int PREC, int RB>
-__global__ __launch_bounds__(256) void quant_act_kernel(
+__global__ __launch_bounds__(QuantCfg<RB>::NT) void quant_act_kernel(
     int M, int K, const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
     const uint16_t* __restrict__ l1t, float alpha, uint8_t* __restrict__ codes,
     void* __restrict__ scales, float* __restrict__ xl1) {
+  constexpr int WAVES = QuantCfg<RB>::WAVES, NT = QuantCfg<RB>::NT, SPP = QuantCfg<RB>::SPP;
+  constexpr int RBX = RB > 0 ? RB : 1;
   extern __shared__ __align__(16) float smem[];
-  float* rl = smem;      // [K] fp32 reciprocals of lambda
-  float* red = smem + K; // [4 waves][16 rows][RB*16] partial XL1
+  float* rl = smem;   // [K] fp32 reciprocals of lambda (main loop)
+  float* red = smem;  // [WAVES][16 rows][RB*16] partial XL1 (after it, same space)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row0 = blockIdx.x * 16;
 
-  for (int k = tid; k < K; k += 256) rl[k] = lam ? 1.0f / bf16_bits_to_f32(lam[k]) : 1.0f;
+  for (int k = tid; k < K; k += NT) rl[k] = lam ? 1.0f / bf16_bits_to_f32(lam[k]) : 1.0f;
   __syncthreads();
 
   const int r = lane & 15, c = lane >> 4;
   const int m = row0 + r;
   const bool valid = m < M;
-  const uint16_t* xrow = x + (size_t)(valid ? m : 0) * K;
   const int nsteps = K >> 6;
+  // Raw buffer loads: rows past M read as zeros, no branches in the load phase.
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t lres = __builtin_amdgcn_make_buffer_rsrc((void*)l1t, (short)0, RB * 16 * K * 2, 0x00020000);
+  const int xrow = m * K * 2;  // byte offset of this lane's row (past the end when m >= M)
 
-  v4f acc[RB > 0 ? RB : 1];
+  v4f acc[RBX];
 #pragma unroll
-  for (int i = 0; i < (RB > 0 ? RB : 1); ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < RBX; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const float d6 = 6.0f * alpha;
 
-  for (int s = wave; s < nsteps; s += 4) {
-    const int k0 = (s << 6) + (c << 4);
-    uint4 xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
-    if (valid) {
-      xa = *(const uint4*)(xrow + k0);
-      xb = *(const uint4*)(xrow + k0 + 8);
-    }
-    const u32 xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-    float rk[16];
-    *(float4*)&rk[0] = *(const float4*)&rl[k0];
-    *(float4*)&rk[4] = *(const float4*)&rl[k0 + 4];
-    *(float4*)&rk[8] = *(const float4*)&rl[k0 + 8];
-    *(float4*)&rk[12] = *(const float4*)&rl[k0 + 12];
-    float xh[16];
-    float amax = 0.0f;
+  for (int s0 = wave; s0 < nsteps; s0 += WAVES * SPP) {
+    // loads of this pass: steps s0, s0 + WAVES, ... (up to SPP of them)
+    uint4 xa[SPP], xb[SPP];
+    uint4 lb[SPP][RBX][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xh[2 * i] = bf16_bits_to_f32(xw[i] & 0xFFFFu) * rk[2 * i];
-      xh[2 * i + 1] = bf16_bits_to_f32(xw[i] >> 16) * rk[2 * i + 1];
-      amax = fmaxf(amax, fmaxf(fabsf(xh[2 * i]), fabsf(xh[2 * i + 1])));
-    }
-
-    u32 pk0 = 0u, pk1 = 0u;
-    if constexpr (PREC == 0) {
-      // one 64-channel group = this lane and the lanes 16 and 32 apart
-      amax = fmaxf(amax, shfl_xor_f(amax, 16));
-      amax = fmaxf(amax, shfl_xor_f(amax, 32));
-      const u32 sb = f32_to_f16_sat_bits(amax / 7.0f);
-      const float sf = f16_bits_to_f32(sb);
-      const float t = sf == 0.0f ? 0.0f : 1.0f / sf;
+    for (int u = 0; u < SPP; ++u) {
+      const int st = s0 + u * WAVES;
+      const int k0 = (st << 6) + (c << 4);
+      const bool live = st < nsteps;
+      const int xo = live ? xrow + k0 * 2 : 0x7FFFFFF0;
+      xa[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, xo, 0, 0));
+      xb[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, xo, 16, 0));
+      if constexpr (RB > 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float q = __builtin_rintf(xh[i] * t);
-        q = fminf(fmaxf(q, -8.0f), 7.0f);
-        const u32 nib = (u32)(int)q & 0xFu;
-        if (i < 8) pk0 |= nib << (4 * i);
-        else pk1 |= nib << (4 * (i - 8));
-      }
-      if (valid) {
-        *(uint2*)(codes + (size_t)m * (K >> 1) + (k0 >> 1)) = uint2{pk0, pk1};
-        if (c == 0) ((uint16_t*)scales)[(size_t)m * (K >> 6) + s] = (uint16_t)sb;
-      }
-    } else {
-      // one 16-channel group = this lane's 16 channels
-      const u32 sb = f32_to_e4m3_sat_pos(amax / d6);
-      const float sf = e4m3_to_f32(sb);
-      float t = 0.0f;
-      if (sf != 0.0f) {
-        const float sa = sf * alpha;
-        t = 1.0f / sa;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const u32 nib = sf == 0.0f ? 0u : f32_to_e2m1_sat(xh[i] * t);
-        if (i < 8) pk0 |= nib << (4 * i);
-        else pk1 |= nib << (4 * (i - 8));
-      }
-      if (valid) {
-        *(uint2*)(codes + (size_t)m * (K >> 1) + (k0 >> 1)) = uint2{pk0, pk1};
-        ((uint8_t*)scales)[(size_t)m * (K >> 4) + (s << 2) + c] = (uint8_t)sb;
+        for (int rb = 0; rb < RB; ++rb) {
+          const int lo = live ? ((rb * 16 + r) * K + k0) * 2 : 0x7FFFFFF0;
+          lb[u][rb][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lres, lo, 0, 0));
+          lb[u][rb][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lres, lo, 16, 0));
+        }
       }
     }
 
-    if constexpr (RB > 0) {
-      // XL1 += X[16 rows, these 64 channels] . L1[these channels, 16*RB]
-      const v8bf a0 = __builtin_bit_cast(v8bf, xa);
-      const v8bf a1 = __builtin_bit_cast(v8bf, xb);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const uint16_t* lrow = l1t + (size_t)(rb * 16 + r) * K + k0;
-        const uint4 b0 = *(const uint4*)lrow;
-        const uint4 b1 = *(const uint4*)(lrow + 8);
-        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, b0), acc[rb], 0, 0, 0);
-        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, b1), acc[rb], 0, 0, 0);
+    for (int u = 0; u < SPP; ++u) {
+      const int st = s0 + u * WAVES;
+      if (st >= nsteps) break;  // wave-uniform
+      const int k0 = (st << 6) + (c << 4);
+      const u32 xw[8] = {xa[u].x, xa[u].y, xa[u].z, xa[u].w, xb[u].x, xb[u].y, xb[u].z, xb[u].w};
+      float rk[16];
+      *(float4*)&rk[0] = *(const float4*)&rl[k0];
+      *(float4*)&rk[4] = *(const float4*)&rl[k0 + 4];
+      *(float4*)&rk[8] = *(const float4*)&rl[k0 + 8];
+      *(float4*)&rk[12] = *(const float4*)&rl[k0 + 12];
+      float xh[16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xh[2 * i] = bf16_bits_to_f32(xw[i] & 0xFFFFu) * rk[2 * i];
+        xh[2 * i + 1] = bf16_bits_to_f32(xw[i] >> 16) * rk[2 * i + 1];
+        amax = fmaxf(amax, fmaxf(fabsf(xh[2 * i]), fabsf(xh[2 * i + 1])));
+      }
+
+      u32 pk0 = 0u, pk1 = 0u;
+      if constexpr (PREC == 0) {
+        // one 64-channel group = this lane and the lanes 16 and 32 apart
+        amax = fmaxf(amax, shfl_xor_f(amax, 16));
+        amax = fmaxf(amax, shfl_xor_f(amax, 32));
+        const u32 sb = f32_to_f16_sat_bits(amax / 7.0f);
+        const float sf = f16_bits_to_f32(sb);
+        const float t = sf == 0.0f ? 0.0f : 1.0f / sf;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float q = __builtin_rintf(xh[i] * t);
+          q = fminf(fmaxf(q, -8.0f), 7.0f);
+          const u32 nib = (u32)(int)q & 0xFu;
+          if (i < 8) pk0 |= nib << (4 * i);
+          else pk1 |= nib << (4 * (i - 8));
+        }
+        if (valid) {
+          *(uint2*)(codes + (size_t)m * (K >> 1) + (k0 >> 1)) = uint2{pk0, pk1};
+          if (c == 0) ((uint16_t*)scales)[(size_t)m * (K >> 6) + st] = (uint16_t)sb;
+        }
+      } else {
+        // one 16-channel group = this lane's 16 channels
+        const u32 sb = f32_to_e4m3_sat_pos(amax / d6);
+        const float sf = e4m3_to_f32(sb);
+        float t = 0.0f;
+        if (sf != 0.0f) {
+          const float sa = sf * alpha;
+          t = 1.0f / sa;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const u32 nib = sf == 0.0f ? 0u : f32_to_e2m1_sat(xh[i] * t);
+          if (i < 8) pk0 |= nib << (4 * i);
+          else pk1 |= nib << (4 * (i - 8));
+        }
+        if (valid) {
+          *(uint2*)(codes + (size_t)m * (K >> 1) + (k0 >> 1)) = uint2{pk0, pk1};
+          ((uint8_t*)scales)[(size_t)m * (K >> 4) + (st << 2) + c] = (uint8_t)sb;
+        }
+      }
+
+      if constexpr (RB > 0) {
+        // XL1 += X[16 rows, these 64 channels] . L1[these channels, 16*RB]
+        const v8bf a0 = __builtin_bit_cast(v8bf, xa[u]);
+        const v8bf a1 = __builtin_bit_cast(v8bf, xb[u]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, lb[u][rb][0]), acc[rb], 0, 0, 0);
+          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, lb[u][rb][1]), acc[rb], 0, 0, 0);
+        }
       }
     }
   }
 
   if constexpr (RB > 0) {
     constexpr int R = RB * 16;
-    // lane holds D[row 4*(lane/16) + v][col lane%16] of each 16x16 block
+    // lane holds D[row 4*(lane/16) + v][col lane%16] of each 16x16 block;
+    // the partial tiles overwrite the reciprocal table once every wave is done
+    __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * c + v) * R + rb * 16 + r] = acc[rb][v];
     __syncthreads();
-    for (int idx = tid; idx < 16 * R; idx += 256) {
+    for (int idx = tid; idx < 16 * R; idx += NT) {
       const int rr = idx / R, col = idx - rr * R;
-      const float sum = ((red[rr * R + col] + red[(16 + rr) * R + col]) + red[(32 + rr) * R + col]) +
-                        red[(48 + rr) * R + col];
+      float sum = red[rr * R + col];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) sum += red[(w * 16 + rr) * R + col];  // fixed order
       if (row0 + rr < M) xl1[(size_t)(row0 + rr) * R + col] = sum;
     }
   }
@@ -150,14 +190,15 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
 
 template <int PREC, int RB>
 static hipError_t launch_quant(const QuantArgs& a, hipStream_t st) {
-  const size_t lds = sizeof(float) * ((size_t)a.K + (RB > 0 ? 4 * 16 * RB * 16 : 0));
+  const size_t red = RB > 0 ? (size_t)QuantCfg<RB>::WAVES * 16 * RB * 16 : 0;
+  const size_t lds = sizeof(float) * ((size_t)a.K > red ? (size_t)a.K : red);
   auto kern = quant_act_kernel<PREC, RB>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   const int blocks = (int)((a.M + 15) / 16);
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, st, (int)a.M, (int)a.K,
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(QuantCfg<RB>::NT), lds, st, (int)a.M, (int)a.K,
                      (const uint16_t*)a.x, (const uint16_t*)a.smooth, (const uint16_t*)a.l1t,
                      a.alpha, (uint8_t*)a.codes, a.scales, a.xl1);
   return hipGetLastError();
