@@ -36,8 +36,9 @@
 //   (fp16 x fp16 products are exact in fp32).
 // * Operand loads are raw buffer loads: rows past the end of a tensor read as
 //   zero in hardware, so the M and N tails need no per-lane predication.
-// * Tiles are ordered so that each XCD (own L2) works on a contiguous range:
-//   neighbouring tiles share weight panels in that XCD's L2.
+// * Tiles are ordered so that each XCD (own L2) works on a contiguous range
+//   of a banded order: the tiles resident on one XCD at a time share a few
+//   activation and weight panels in that XCD's L2.
 #include "common.h"
 #include "launch.h"
 
@@ -120,13 +121,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;  // lane within a 16-lane group, group 0..3
 
-  // XCD-aware tile order: consecutive workgroup ids go round-robin over the 8
-  // XCDs; give each XCD a contiguous block of tiles (m fastest).
+  // Tile order.  Consecutive workgroup ids go round-robin over the 8 XCDs
+  // (each with its own L2): first give each XCD a contiguous range of the
+  // order, then walk the tile grid in bands of kBandM row tiles (m fastest
+  // inside a band), so the tiles an XCD runs at once share a few activation
+  // and weight panels that fit its L2 instead of sweeping all of M per column.
   const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;  // N % 128 == 0
   const int tiles = m_tiles * n_tiles;
   int t = blockIdx.x;
   if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
-  const int m0 = (t % m_tiles) * BM, n0 = (t / m_tiles) * BN;
+  constexpr int kBandM = 12;
+  const int band = t / (kBandM * n_tiles), in_band = t - band * (kBandM * n_tiles);
+  const int band_m0 = band * kBandM;
+  const int band_h = m_tiles - band_m0 < kBandM ? m_tiles - band_m0 : kBandM;
+  const int m0 = (band_m0 + in_band % band_h) * BM, n0 = (in_band / band_h) * BN;
   const int wn = (wave / WAVES_M) * (BI * 16), wm = (wave % WAVES_M) * (BJ * 16);
   const int G = K >> 6;
   const int stages = (G + KG - 1) / KG;
@@ -140,48 +148,52 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
 
   // staging: chunk c = tid + NT*r -> (row c / PARTS, 16-byte part c % PARTS);
   // rows [0, BN) are weight rows n0+row, rows [BN, NROWS) activation rows.
-  const int part = tid % PARTS;  // the same for every chunk of this thread (NT % PARTS == 0)
-  int coff[CHUNKS];              // byte offset of the chunk in its tensor at stage 0
+  // Chunks r < WCH hold weight rows for every thread (NT % PARTS == 0), so the
+  // buffer resource of each load is known at compile time; the stage's byte
+  // offset goes in the scalar offset.  A group past the end of K (odd number
+  // of groups) reads the next row's bytes or zeros: its scales are zero, so it
+  // adds nothing.
+  constexpr int WCH = BN * PARTS / NT;
+  static_assert(BN * PARTS % NT == 0, "weight rows fill whole chunk rounds");
+  const int part = tid % PARTS;
+  int coff[CHUNKS];  // byte offset of the chunk in its tensor at stage 0
 #pragma unroll
   for (int r = 0; r < CHUNKS; ++r) {
     const int row = (tid + NT * r) / PARTS;
-    coff[r] = row < BN ? (n0 + row) * rowb + part * 16 : (m0 + row - BN) * rowb + part * 16;
+    coff[r] = r < WCH ? (n0 + row) * rowb + part * 16 : (m0 + row - BN) * rowb + part * 16;
   }
+  // scale rows: row = tid + NT*r; each wave lies wholly in the weight rows or
+  // in the activation rows (BN % 64 == 0), so the choice is wave-uniform
+  static_assert(BN % 64 == 0, "scale rows split on a wave boundary");
   int soff[SROWS];
+  bool s_is_w[SROWS], s_live[SROWS];
 #pragma unroll
   for (int r = 0; r < SROWS; ++r) {
     const int row = tid + NT * r;
-    soff[r] = row < BN ? (n0 + row) * G * 2 : (m0 + row - BN) * G * 2;
+    const int row0 = __builtin_amdgcn_readfirstlane(row - lane);  // first row of this wave
+    s_is_w[r] = row0 < BN;
+    s_live[r] = row0 < NROWS;
+    soff[r] = s_is_w[r] ? (n0 + row) * G * 2 : (m0 + row - BN) * G * 2;
   }
 
   uint4 rc[CHUNKS];
   uint32_t rs[SROWS][KG];  // raw fp16 bits: converted only at the LDS store, so
                            // no instruction waits on these loads before then
   auto gload = [&](int s) {
-    // channel bytes of this stage; a partial last stage (odd number of
-    // groups) skips its missing group with a wave-uniform test
     const int kbyte = s * 32 * KG;
-    const bool full = kbyte + 32 * KG <= rowb;
 #pragma unroll
-    for (int r = 0; r < CHUNKS; ++r) {
-      const bool is_w = (tid + NT * r) / PARTS < BN;
-      if (full || kbyte + part * 16 < rowb)
-        rc[r] = __builtin_bit_cast(uint4, is_w ? __builtin_amdgcn_raw_buffer_load_b128(wres, coff[r] + kbyte, 0, 0)
-                                               : __builtin_amdgcn_raw_buffer_load_b128(xres, coff[r] + kbyte, 0, 0));
-      else
-        rc[r] = uint4{0u, 0u, 0u, 0u};
-    }
+    for (int r = 0; r < CHUNKS; ++r)
+      rc[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r < WCH ? wres : xres, coff[r], kbyte, 0));
     if constexpr (MODE == 0) {
 #pragma unroll
       for (int r = 0; r < SROWS; ++r) {
-        const int row = tid + NT * r;
 #pragma unroll
         for (int gg = 0; gg < KG; ++gg) {
           const int g = s * KG + gg;
           uint32_t h = 0u;
-          if (row < NROWS && g < G)
-            h = row < BN ? __builtin_amdgcn_raw_buffer_load_b16(wsres, soff[r] + 2 * g, 0, 0)
-                         : __builtin_amdgcn_raw_buffer_load_b16(asres, soff[r] + 2 * g, 0, 0);
+          if (s_live[r] && g < G)  // wave-uniform
+            h = s_is_w[r] ? __builtin_amdgcn_raw_buffer_load_b16(wsres, soff[r], 2 * g, 0)
+                          : __builtin_amdgcn_raw_buffer_load_b16(asres, soff[r], 2 * g, 0);
           rs[r][gg] = h;
         }
       }
@@ -200,7 +212,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
 #pragma unroll
       for (int r = 0; r < SROWS; ++r) {
         const int row = tid + NT * r;
-        if (row < NROWS) {
+        if (s_live[r]) {
 #pragma unroll
           for (int gg = 0; gg < KG; ++gg) ssc[buf * SC_STAGE + gg * NROWS + row] = f16_bits_to_f32(rs[r][gg]);
         }
