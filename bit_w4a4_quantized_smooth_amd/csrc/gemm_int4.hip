@@ -149,10 +149,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
   // staging: chunk c = tid + NT*r -> (row c / PARTS, 16-byte part c % PARTS);
   // rows [0, BN) are weight rows n0+row, rows [BN, NROWS) activation rows.
   // Chunks r < WCH hold weight rows for every thread (NT % PARTS == 0), so the
-  // buffer resource of each load is known at compile time; the stage's byte
-  // offset goes in the scalar offset.  A group past the end of K (odd number
-  // of groups) reads the next row's bytes or zeros: its scales are zero, so it
-  // adds nothing.
+  // buffer resource of each load is known at compile time.  Offsets stay in
+  // the vector operand, which the hardware range-checks: a group past the end
+  // of K (odd number of groups) reads the next row's bytes, or zeros past the
+  // tensor; its scales are zero, so it adds nothing.
   constexpr int WCH = BN * PARTS / NT;
   static_assert(BN * PARTS % NT == 0, "weight rows fill whole chunk rounds");
   const int part = tid % PARTS;
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
     const int kbyte = s * 32 * KG;
 #pragma unroll
     for (int r = 0; r < CHUNKS; ++r)
-      rc[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r < WCH ? wres : xres, coff[r], kbyte, 0));
+      rc[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r < WCH ? wres : xres, coff[r] + kbyte, 0, 0));
     if constexpr (MODE == 0) {
 #pragma unroll
       for (int r = 0; r < SROWS; ++r) {
@@ -192,8 +192,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
           const int g = s * KG + gg;
           uint32_t h = 0u;
           if (s_live[r] && g < G)  // wave-uniform
-            h = s_is_w[r] ? __builtin_amdgcn_raw_buffer_load_b16(wsres, soff[r], 2 * g, 0)
-                          : __builtin_amdgcn_raw_buffer_load_b16(asres, soff[r], 2 * g, 0);
+            h = s_is_w[r] ? __builtin_amdgcn_raw_buffer_load_b16(wsres, soff[r] + 2 * g, 0, 0)
+                          : __builtin_amdgcn_raw_buffer_load_b16(asres, soff[r] + 2 * g, 0, 0);
           rs[r][gg] = h;
         }
       }

@@ -5,11 +5,10 @@
 // Precisions and group sizes from "Nunchaku Lite", "Supported quantization
 // types": int4 / group 64 and nvfp4 / group 16.
 //
-// Work split: one workgroup (16 wave64, or 8 for ranks above 32) owns 16 rows
-// of X and all K.  Wave w takes the 64-channel steps s = w, w+WAVES, ..., and
-// issues the loads of up to four of its steps (X and the L1^T slices) before
-// consuming any of them, as branch-free buffer loads (rows past M read as
-// zero).  Within a step lane l holds row
+// Work split: one workgroup (8 wave64) owns 16 rows of X and all K.  Wave w
+// takes the 64-channel steps s = w, w+8, ..., keeping a few of them in flight
+// in a ring of register slots (X and the L1^T slices, as branch-free buffer
+// loads; rows past M read as zero).  Within a step lane l holds row
 // l % 16 and channels 16*(l/16) .. +16 (two 16-byte loads, 512 contiguous
 // bytes per row per workgroup step).  That is also the operand layout of
 // v_mfma_f32_16x16x32_bf16, so the raw bf16 X registers feed the matrix core
@@ -32,74 +31,95 @@ namespace svdq {
 
 // Eight waves per workgroup; with at most 128 VGPRs (ranks up to 32) two
 // workgroups share a CU, so a DiT-sized call (a few hundred workgroups) is
-// resident at once.  SPP steps' loads are issued together per pass; it shrinks
-// as the rank grows because each step also carries RB*2 L1^T fragments.
+// resident at once.  Each wave keeps W of its 64-channel steps in flight in a
+// ring of register slots (a step also carries RB*2 fragments of L1^T, so W
+// shrinks as the rank grows): step j is computed while steps j+1 .. j+W-1
+// are loading, and its slot is refilled with step j+W right after.
 template <int RB>
 struct QuantCfg {
   static constexpr int WAVES = 8;
   static constexpr int NT = WAVES * 64;
-  static constexpr int SPP = RB <= 1 ? 4 : RB <= 2 ? 3 : RB <= 4 ? 2 : 1;
+  static constexpr int W = RB <= 1 ? 3 : RB <= 4 ? 2 : 1;
 };
+
+// Max over lanes l, l^16, l^32 and l^48: the four 16-channel slices of one
+// row's 64-channel group.  The permlane swaps move whole 16-lane rows without
+// going through LDS.
+__device__ __forceinline__ float max_over_rows(float v) {
+  u32 bv = __float_as_uint(v);
+  auto p = __builtin_amdgcn_permlane16_swap(bv, bv, false, false);
+  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  bv = __float_as_uint(v);
+  auto q = __builtin_amdgcn_permlane32_swap(bv, bv, false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
 
 template <int PREC, int RB>
 __global__ __launch_bounds__(QuantCfg<RB>::NT) void quant_act_kernel(
     int M, int K, const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
     const uint16_t* __restrict__ l1t, float alpha, uint8_t* __restrict__ codes,
     void* __restrict__ scales, float* __restrict__ xl1) {
-  constexpr int WAVES = QuantCfg<RB>::WAVES, NT = QuantCfg<RB>::NT, SPP = QuantCfg<RB>::SPP;
+  constexpr int WAVES = QuantCfg<RB>::WAVES, NT = QuantCfg<RB>::NT, W = QuantCfg<RB>::W;
   constexpr int RBX = RB > 0 ? RB : 1;
+  constexpr int kOut = 0x7FFFFFF0;  // offset past num_records: the load returns 0
   extern __shared__ __align__(16) float smem[];
   float* rl = smem;   // [K] fp32 reciprocals of lambda (main loop)
   float* red = smem;  // [WAVES][16 rows][RB*16] partial XL1 (after it, same space)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row0 = blockIdx.x * 16;
-
-  for (int k = tid; k < K; k += NT) rl[k] = lam ? 1.0f / bf16_bits_to_f32(lam[k]) : 1.0f;
-  __syncthreads();
-
   const int r = lane & 15, c = lane >> 4;
   const int m = row0 + r;
   const bool valid = m < M;
   const int nsteps = K >> 6;
-  // Raw buffer loads: rows past M read as zeros, no branches in the load phase.
+  // this wave's steps are wave + WAVES * j, j < nst
+  const int nst = nsteps > wave ? (nsteps - wave + WAVES - 1) / WAVES : 0;
+
+  // Raw buffer loads with every offset in the range-checked vector operand:
+  // rows past M and steps past the end read zeros, with no branches.
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t lres = __builtin_amdgcn_make_buffer_rsrc((void*)l1t, (short)0, RB * 16 * K * 2, 0x00020000);
-  const int xrow = m * K * 2;  // byte offset of this lane's row (past the end when m >= M)
+  const u32 xo = (u32)m * (u32)K * 2u + 32u * c;  // step 0, first 16 bytes of this lane
+  u32 lo[RBX];
+#pragma unroll
+  for (int rb = 0; rb < RBX; ++rb) lo[rb] = (u32)(rb * 16 + r) * (u32)K * 2u + 32u * c;
+
+  uint4 xa[W], xb[W];
+  uint4 lb[W][RBX][2];
+  auto issue = [&](int u, int j) {  // load step j of this wave into slot u
+    const int st = wave + WAVES * j;
+    const bool live = j < nst;
+    const u32 sb = 128u * st;
+    xa[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, live ? xo + sb : kOut, 0, 0));
+    xb[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, live ? xo + sb + 16 : kOut, 0, 0));
+    if constexpr (RB > 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        lb[u][rb][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lres, live ? lo[rb] + sb : kOut, 0, 0));
+        lb[u][rb][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lres, live ? lo[rb] + sb + 16 : kOut, 0, 0));
+      }
+    }
+  };
+  // the first W steps are in flight before the reciprocal table is built
+#pragma unroll
+  for (int u = 0; u < W; ++u) issue(u, u);
+
+  for (int k = tid; k < K; k += NT) rl[k] = lam ? 1.0f / bf16_bits_to_f32(lam[k]) : 1.0f;
+  __syncthreads();
 
   v4f acc[RBX];
 #pragma unroll
   for (int i = 0; i < RBX; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-
   const float d6 = 6.0f * alpha;
 
-  for (int s0 = wave; s0 < nsteps; s0 += WAVES * SPP) {
-    // loads of this pass: steps s0, s0 + WAVES, ... (up to SPP of them)
-    uint4 xa[SPP], xb[SPP];
-    uint4 lb[SPP][RBX][2];
+  for (int j0 = 0; j0 < nst; j0 += W) {
 #pragma unroll
-    for (int u = 0; u < SPP; ++u) {
-      const int st = s0 + u * WAVES;
+    for (int u = 0; u < W; ++u) {
+      const int j = j0 + u;
+      if (j >= nst) break;  // wave-uniform
+      const int st = wave + WAVES * j;
       const int k0 = (st << 6) + (c << 4);
-      const bool live = st < nsteps;
-      const int xo = live ? xrow + k0 * 2 : 0x7FFFFFF0;
-      xa[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, xo, 0, 0));
-      xb[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, xo, 16, 0));
-      if constexpr (RB > 0) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int lo = live ? ((rb * 16 + r) * K + k0) * 2 : 0x7FFFFFF0;
-          lb[u][rb][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lres, lo, 0, 0));
-          lb[u][rb][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lres, lo, 16, 0));
-        }
-      }
-    }
-
-#pragma unroll
-    for (int u = 0; u < SPP; ++u) {
-      const int st = s0 + u * WAVES;
-      if (st >= nsteps) break;  // wave-uniform
-      const int k0 = (st << 6) + (c << 4);
-      const u32 xw[8] = {xa[u].x, xa[u].y, xa[u].z, xa[u].w, xb[u].x, xb[u].y, xb[u].z, xb[u].w};
+      const uint4 va = xa[u], vb = xb[u];
+      const u32 xw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
       float rk[16];
       *(float4*)&rk[0] = *(const float4*)&rl[k0];
       *(float4*)&rk[4] = *(const float4*)&rl[k0 + 4];
@@ -116,11 +136,9 @@ __global__ __launch_bounds__(QuantCfg<RB>::NT) void quant_act_kernel(
 
       u32 pk0 = 0u, pk1 = 0u;
       if constexpr (PREC == 0) {
-        // one 64-channel group = this lane and the lanes 16 and 32 apart
-        amax = fmaxf(amax, shfl_xor_f(amax, 16));
-        amax = fmaxf(amax, shfl_xor_f(amax, 32));
-        const u32 sb = f32_to_f16_sat_bits(amax / 7.0f);
-        const float sf = f16_bits_to_f32(sb);
+        amax = max_over_rows(amax);  // one 64-channel group = lanes l, l^16, l^32, l^48
+        const u32 sbits = f32_to_f16_sat_bits(amax / 7.0f);
+        const float sf = f16_bits_to_f32(sbits);
         const float t = sf == 0.0f ? 0.0f : 1.0f / sf;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -132,12 +150,12 @@ __global__ __launch_bounds__(QuantCfg<RB>::NT) void quant_act_kernel(
         }
         if (valid) {
           *(uint2*)(codes + (size_t)m * (K >> 1) + (k0 >> 1)) = uint2{pk0, pk1};
-          if (c == 0) ((uint16_t*)scales)[(size_t)m * (K >> 6) + st] = (uint16_t)sb;
+          if (c == 0) ((uint16_t*)scales)[(size_t)m * (K >> 6) + st] = (uint16_t)sbits;
         }
       } else {
         // one 16-channel group = this lane's 16 channels
-        const u32 sb = f32_to_e4m3_sat_pos(amax / d6);
-        const float sf = e4m3_to_f32(sb);
+        const u32 sbits = f32_to_e4m3_sat_pos(amax / d6);
+        const float sf = e4m3_to_f32(sbits);
         float t = 0.0f;
         if (sf != 0.0f) {
           const float sa = sf * alpha;
@@ -151,20 +169,21 @@ __global__ __launch_bounds__(QuantCfg<RB>::NT) void quant_act_kernel(
         }
         if (valid) {
           *(uint2*)(codes + (size_t)m * (K >> 1) + (k0 >> 1)) = uint2{pk0, pk1};
-          ((uint8_t*)scales)[(size_t)m * (K >> 4) + (st << 2) + c] = (uint8_t)sb;
+          ((uint8_t*)scales)[(size_t)m * (K >> 4) + (st << 2) + c] = (uint8_t)sbits;
         }
       }
 
       if constexpr (RB > 0) {
         // XL1 += X[16 rows, these 64 channels] . L1[these channels, 16*RB]
-        const v8bf a0 = __builtin_bit_cast(v8bf, xa[u]);
-        const v8bf a1 = __builtin_bit_cast(v8bf, xb[u]);
+        const v8bf a0 = __builtin_bit_cast(v8bf, va);
+        const v8bf a1 = __builtin_bit_cast(v8bf, vb);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, lb[u][rb][0]), acc[rb], 0, 0, 0);
           acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, lb[u][rb][1]), acc[rb], 0, 0, 0);
         }
       }
+      issue(u, j + W);  // refill this slot (past the end: zeros, never used)
     }
   }
 
