@@ -11,9 +11,19 @@ are cycled so that the 256 MB Infinity Cache cannot serve a step from the
 previous one.  `value` is whole-step throughput in tera-ops per second,
 2*M*N*K of the W4A4 linear divided by the time of the full step.
 
+Besides the step, the same run times the other workloads of the hot path one
+call at a time (median of timed calls, HIP events on the launch stream): the
+DiT MLP up/down projections, the NVFP4 variant of the QKV projection, the
+AWQ GEMV at M=64, and a plain device-to-device copy as the attainable-HBM
+line.  `roofline` describes the dominant kernel (the int4 GEMM); its `traffic`
+is the HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE
+counter summary, reported only while the kernel source still matches the
+hash recorded there.
+
 Prints one JSON line.  --gpus above 1 exits: this build measures one GPU.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,7 +36,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "W4A4 SVDQ linear TOPS (M=4608,K=3072) + AWQ GEMV GB/s; % of roofline"
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 matrix peak, 5.0 POP/s
+PEAK_FP8_TFLOPS = 5000.0  # dense fp8
+PEAK_FP4_TFLOPS = 10100.0 # dense fp4 / fp6
+PEAK_BF16_TFLOPS = 2500.0 # dense bf16
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+GEMM_SOURCES = ["gemm_int4.hip", "common.h", "launch.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_int4_dit_qkv_4608x9216x3072.txt")
 
 
 def parse():
@@ -36,8 +51,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--copies", type=int, default=4, help="input copies cycled for the linear")
     p.add_argument("--awq-copies", type=int, default=16, help="AWQ weight copies cycled (>= 512 MB)")
+    p.add_argument("--calls", type=int, default=20, help="timed calls per extra workload")
+    p.add_argument("--no-extras", action="store_true", help="time only the step")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=768, help="rows of X in the oracle's timed sample")
+    p.add_argument("--cpu-rows", type=int, default=2304, help="rows of X in the oracle's timed sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of the benchmark, copy MIB MiB device-to-device a few times (the known-size "
                         "transfer that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -53,6 +70,31 @@ def copy_calibration(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "bit_w4a4_quantized_smooth_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic():
+    """HBM bytes per launch of the int4 GEMM from the committed counter summary,
+    or None when it is missing or was taken on a different kernel source."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("source_sha256") != gemm_source_hash():
+            return None
+        return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -73,11 +115,6 @@ def main():
     torch.cuda.set_device(dev)
     sq.lib()
 
-    # ---- inputs ----------------------------------------------------------------
-    M, N, K, R = 4608, 9216, 3072, 32
-    lin = synth.svdq_layer(1002, M, N, K, R, synth.INT4, 0.005, 30.0)
-    awq = synth.awq_layer(1005, 2, 18432, 3072)
-
     def t(a, dtype=None):
         x = torch.from_numpy(np.ascontiguousarray(a))
         return (x.view(dtype) if dtype is not None else x).to(dev)
@@ -87,6 +124,13 @@ def main():
 
     def f16(bits):
         return t(np.asarray(bits, np.uint16).view(np.int16), torch.float16)
+
+    stream = torch.cuda.current_stream()
+
+    # ---- the step: DiT QKV int4 linear + AWQ modulation GEMV --------------------
+    M, N, K, R = 4608, 9216, 3072, 32
+    lin = synth.svdq_layer(1002, M, N, K, R, synth.INT4, 0.005, 30.0)
+    awq = synth.awq_layer(1005, 2, 18432, 3072)
 
     C = max(1, args.copies)
     X = [bf(lin["x"]) for _ in range(C)]
@@ -110,8 +154,6 @@ def main():
     AY = torch.empty((2, 18432), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
-
     def step(i, ev=None):
         c = i % C
         if ev is not None:
@@ -133,6 +175,7 @@ def main():
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
@@ -146,11 +189,26 @@ def main():
     ms_step = float(wall_s * 1e3 / args.steps)
 
     ops = 2.0 * M * N * K
-    gemm_ms = float(t_gemm.mean())
+    gemm_ms = float(t_gemm.mean())  # mean, like the kernel-trace average it is checked against
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
     quant_bytes = M * K * 2 + K * 2 + R * K * 2 + M * K // 2 + M * (K // 64) * 2 + M * R * 4
     awq_bytes = 18432 * 3072 // 2 + 2 * 18432 * 48 * 2 + 2 * 3072 * 2 + 18432 * 2 + 2 * 18432 * 2
 
+    components = {
+        "quantize_ms": round(float(t_quant.mean()), 5),
+        "quantize_GBps": round(quant_bytes / (t_quant.mean() * 1e-3) / 1e9, 1),
+        "gemm_ms": round(gemm_ms, 5),
+        "gemm_TOPS": round(gemm_tops, 2),
+        "linear_TOPS": round(ops / ((t_quant.mean() + gemm_ms) * 1e-3) / 1e12, 2),
+        "awq_ms": round(float(t_awq.mean()), 5),
+        "awq_GBps": round(awq_bytes / (t_awq.mean() * 1e-3) / 1e9, 1),
+        "awq_frac_hbm": round(awq_bytes / (t_awq.mean() * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "event_step_ms": round(float(t_step.mean()), 5),
+    }
+    if not args.no_extras:
+        components.update(extras(args, torch, sq, synth, t, bf, f16, stream))
+
+    traffic = committed_traffic()
     out = {
         "metric": METRIC,
         "value": round(ops / (ms_step * 1e-3) / 1e12, 2),
@@ -166,25 +224,97 @@ def main():
         "data": "synthetic",
         "config": {"workload": "dit_qkv_int4_4608x9216x3072_r32 + awq_mod_2x18432x3072",
                    "M": M, "N": N, "K": K, "rank": R, "group": 64, "awq": [2, 18432, 3072]},
-        "components": {
-            "quantize_ms": round(float(t_quant.mean()), 5),
-            "quantize_GBps": round(quant_bytes / (t_quant.mean() * 1e-3) / 1e9, 1),
-            "gemm_ms": round(gemm_ms, 5),
-            "gemm_TOPS": round(gemm_tops, 2),
-            "linear_TOPS": round(ops / ((t_quant.mean() + gemm_ms) * 1e-3) / 1e12, 2),
-            "awq_ms": round(float(t_awq.mean()), 5),
-            "awq_GBps": round(awq_bytes / (t_awq.mean() * 1e-3) / 1e9, 1),
-            "awq_frac_hbm": round(awq_bytes / (t_awq.mean() * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "event_step_ms": round(float(t_step.mean()), 5),
-        },
+        "components": components,
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": None,
-                     "kernel": "gemm_int4_kernel", "per_launch_ops": ops},
+                     "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                     "kernel": "gemm_int4_kernel", "per_launch_ops": ops,
+                     "algorithmic_bytes": int(M * K // 2 + M * K // 64 * 2 + N * K // 2 + N * K // 64 * 2
+                                              + M * R * 4 + N * R * 2 + N * 2 + M * N * 2)},
     }
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(lin, args.cpu_rows)
     print(json.dumps(out), flush=True)
+
+
+def median_ms(fn, calls, stream, torch):
+    """Median duration of `calls` back-to-back calls, each bracketed by HIP events
+    on the launch stream (after 3 untimed calls)."""
+    for _ in range(3):
+        fn(0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def extras(args, torch, sq, synth, t, bf, f16, stream):
+    """The hot path's other workloads, one call at a time."""
+    res = {}
+    dev = torch.device("cuda:0")
+    n = args.calls
+
+    def linear(name, seed, M, N, K, prec, outlier_frac, outlier_scale, kind="normal"):
+        d = synth.svdq_layer(seed, M, N, K, 32, prec, outlier_frac, outlier_scale, kind)
+        G = 64 if prec == sq.SVDQ_INT4 else 16
+        x, lam, l1t = bf(d["x"]), bf(d["lam"]), bf(d["l1t"])
+        wc = t(d["w_codes"])
+        ws = f16(d["w_scales"]) if prec == sq.SVDQ_INT4 else t(d["w_scales"])
+        l2t, bias = bf(d["l2t"]), bf(d["bias"])
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        scales = (torch.empty((M, K // G), dtype=torch.float16, device=dev) if prec == sq.SVDQ_INT4
+                  else torch.empty((M, K // G), dtype=torch.uint8, device=dev))
+        xl1 = torch.empty((M, 32), dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        aa, aw = float(d["alpha_a"]), float(d["alpha_w"])
+        q_ms = median_ms(lambda i: sq.quantize_act(prec, x, lam, l1t, aa, out=(codes, scales, xl1), stream=stream),
+                         n, stream, torch)
+        g_ms = median_ms(lambda i: sq.w4a4_gemm(prec, codes, scales, wc, ws, xl1, l2t, bias, aa, aw, out=y,
+                                                stream=stream), n, stream, torch)
+        ops = 2.0 * M * N * K
+        tops = ops / (g_ms * 1e-3) / 1e12
+        qb = M * K * 2 + K * 2 + 32 * K * 2 + M * K // 2 + M * (K // G) * (2 if prec == sq.SVDQ_INT4 else 1) + M * 32 * 4
+        r = {"quantize_ms": round(q_ms, 5), "quantize_GBps": round(qb / (q_ms * 1e-3) / 1e9, 1),
+             "gemm_ms": round(g_ms, 5), "gemm_TOPS": round(tops, 2),
+             "linear_TOPS": round(ops / ((q_ms + g_ms) * 1e-3) / 1e12, 2)}
+        if prec == sq.SVDQ_INT4:
+            r["gemm_frac_int8"] = round(tops / PEAK_INT8_TOPS, 4)
+        else:
+            r["gemm_frac_fp8"] = round(tops / PEAK_FP8_TFLOPS, 4)
+            r["gemm_frac_fp4"] = round(tops / PEAK_FP4_TFLOPS, 4)
+        res[name] = r
+        del x, lam, l1t, wc, ws, l2t, bias, codes, scales, xl1, y
+
+    linear("mlp_up_int4_4608x12288x3072", 1002, 4608, 12288, 3072, sq.SVDQ_INT4, 0.005, 30.0)
+    linear("mlp_down_int4_4608x3072x12288", 1003, 4608, 3072, 12288, sq.SVDQ_INT4, 0.0, 1.0, "gelu")
+    linear("qkv_nvfp4_4608x9216x3072", 1004, 4608, 9216, 3072, sq.SVDQ_NVFP4, 0.005, 30.0)
+
+    # AWQ at M=64 over >= 512 MB of weight copies
+    d = synth.awq_layer(1005, 64, 18432, 3072)
+    A = max(1, args.awq_copies)
+    x = bf(d["x"])
+    wc = [t(d["w_codes"]) for _ in range(A)]
+    ws = [f16(d["w_scales"]) for _ in range(A)]
+    wz = [f16(d["w_zeros"]) for _ in range(A)]
+    b = bf(d["bias"])
+    y = torch.empty((64, 18432), dtype=torch.bfloat16, device=dev)
+    ms = median_ms(lambda i: sq.awq_gemv(x, wc[i % A], ws[i % A], wz[i % A], b, out=y, stream=stream),
+                   n, stream, torch)
+    byts = 18432 * 3072 // 2 + 2 * 18432 * 48 * 2 + 64 * 3072 * 2 + 18432 * 2 + 64 * 18432 * 2
+    res["awq_m64"] = {"ms": round(ms, 5), "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del wc, ws, wz
+
+    # attainable HBM: a 1 GiB device-to-device copy (read + write)
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms = median_ms(lambda i: dst.copy_(src), 5, stream, torch)
+    res["copy_attainable_GBps"] = round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)
+    return res
 
 
 def cpu_baseline(lin, rows):
