@@ -73,10 +73,15 @@ def copy_calibration(mib):
 
 
 def gemm_source_hash():
+    """SHA-256 of the GEMM's source code with // comments and blank lines
+    removed, so that editing a comment does not invalidate the counters."""
     h = hashlib.sha256()
     for name in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "bit_w4a4_quantized_smooth_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "bit_w4a4_quantized_smooth_amd", "csrc", name)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

@@ -8,32 +8,31 @@
 //
 // gfx950 design
 // -------------
-// * Workgroup = 8 wave64 (two per SIMD, so one wave's matrix-core work
-//   overlaps the other's vector ALU work) computing a 256(n) x 128(m) tile of
-//   Y^T; each wave owns 64x64 = 2x2 blocks of 32x32.  The matrix-core A operand
-//   is the weight tile (rows n) and B the activation tile (columns m): every
-//   lane ends up with one output row m and runs of four adjacent n, so the
-//   bf16 epilogue writes 8-byte pieces of Y rows.
-// * Two 64-channel groups per pipeline stage: each row contributes a 64-byte
-//   segment of packed codes (four 16-byte loads per row, consecutive lanes).
-//   While staging to LDS the nibbles are expanded to int8 16*q: the two's
-//   complement nibble in the high half of a byte is 16*q exactly (one mask for
-//   odd channels, one shift and mask for even ones, no sign extension).  Both
-//   operands get the same channel permutation, so P is unchanged and the
-//   matrix core (v_mfma_i32_32x32x32_i8) returns 256*P.
-// * int32 -> fp32 without a conversion instruction: each group's MFMA chain
+// * Workgroup = 4 wave64 (2x2) computing a 128(n) x 128(m) tile of Y^T; each
+//   wave owns 64x64 = 4x4 blocks of 16x16.  The matrix-core A operand is the
+//   weight tile (rows n) and B the activation tile (columns m).  Two
+//   workgroups share a CU.
+// * Two 64-channel groups per double-buffered LDS stage: each row contributes
+//   a 64-byte segment of packed codes (four 16-byte loads per row).  While
+//   staging to LDS the nibbles are expanded to int8 16*q: the two's
+//   complement nibble in the high half of a byte is 16*q exactly (one mask
+//   for odd channels, one shift and mask for even ones, no sign extension).
+//   Both operands get the same channel permutation, so P is unchanged and the
+//   matrix core (v_mfma_i32_16x16x64_i8, one per block and group) returns
+//   256*P.
+// * int32 -> fp32 without a conversion instruction: each group's product
 //   starts from the accumulator bit pattern of c0 = 1/(2 pi) (an inline
-//   constant, so no registers), whose mantissa leaves more than 2^20 of
-//   head-room on both sides; the integer sum bits(c0) + 256*P is therefore the
-//   float c0 + P*2^-18 exactly.
-// * The per-group scale product S = sw (x) sa is an outer product; it is
-//   computed on the matrix core by v_mfma_f32_32x32x1_2b_f32, which takes the
-//   two 32-lane halves as two independent blocks (one fp32 per lane: two
-//   32-row weight blocks against one 32-column activation block), leaving one
-//   VALU FMA per output per group: acc += S * (c0 + P*2^-18).  The epilogue
-//   removes the constant: y = 2^18 * (acc - c0 * sum_g S), where
-//   sum_g S = Sw . Sa^T is one small K = #groups fp16 GEMM on the matrix core
-//   (fp16 x fp16 products are exact in fp32).
+//   constant), whose mantissa leaves more than 2^20 of head-room on both
+//   sides; the integer sum bits(c0) + 256*P is therefore the float
+//   c0 + P*2^-18 exactly.
+// * The per-group scale product S = sw (x) sa is an outer product computed on
+//   the matrix core by v_mfma_f32_16x16x1_4b_f32 (four independent 16x16
+//   blocks, one fp32 per lane: a 2x2 quad of output blocks), leaving one VALU
+//   FMA per output per group: acc += S * (c0 + P*2^-18).  Quads are software
+//   pipelined: the FMAs of quad Q-1 issue under the five matrix instructions
+//   of quad Q.  The epilogue removes the constant: y = 2^18 * (acc - c0 *
+//   sum_g S), where sum_g S = Sw . Sa^T is one small K = #groups fp16 GEMM on
+//   the matrix core (fp16 x fp16 products are exact in fp32).
 // * Operand loads are raw buffer loads: rows past the end of a tensor read as
 //   zero in hardware, so the M and N tails need no per-lane predication.
 // * Tiles are ordered so that each XCD (own L2) works on a contiguous range
