@@ -8,43 +8,48 @@
 // two, while NVFP4 scales 16 channels by an E4M3 number, so the scales are not
 // folded into the matrix core.  Instead each operand is dequantized exactly:
 // an E2M1 value (at most 2 significant bits) times an E4M3 scale (at most 4)
-// has at most 6 significant bits, so e2m1(c) * s is exact in bf16.  The tile
-// is expanded to bf16 while staging to LDS and the whole K reduction runs on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation; there is no per-group
-// rescale on the vector ALUs (which would cost more than the matrix work at
-// 16-channel groups).  With unit scales the same path yields the exact group
-// products P (multiples of 1/4) for the partial-product test mode.
+// has at most 6 significant bits and lies in [2^-10, 2688], so e2m1(c) * s is
+// exact in fp16.  Dequantization is two instructions per pair of codes:
+// v_cvt_scalef32_pk_f16_fp4 with a unit scale (its scale operand only applies
+// a power of two) gives the E2M1 values in fp16, and v_pk_mul_f16 multiplies
+// both by the group's scale, exactly.  The tile is expanded to fp16 while
+// staging to LDS and the whole K reduction runs on v_mfma_f32_32x32x16_f16
+// with fp32 accumulation; there is no per-group rescale on the vector ALUs
+// (which would cost more than the matrix work at 16-channel groups).  With
+// unit scales the same path yields the exact group products P (multiples of
+// 1/4) for the partial-product test mode.
 //
 // Tiling: 128(n) x 128(m) per 256-thread workgroup, wave tiles of 64x64,
-// K steps of 64 channels (four NVFP4 groups) double buffered in LDS.
+// K steps of 64 channels (four NVFP4 groups) double buffered in LDS; the
+// next step's codes and scales are loaded (branch-free buffer loads, rows
+// past M read as zero) while the current step computes.  Tiles are assigned
+// so that each XCD works on a contiguous part of a banded order.
 #include "common.h"
 #include "launch.h"
 
 namespace svdq {
 
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
 namespace {
 constexpr int BM = 128, BN = 128;
-constexpr int ROW = 72;  // bf16 per LDS row: 64 channels + 8 padding
-
-// E2M1 nibble -> fp32 value (exact).  Magnitudes 2..7 are the fp32 numbers
-// with bit pattern (m + 252) << 22; 1 is 0.5 and 0 is 0.
-__device__ __forceinline__ float e2m1_val(u32 c) {
-  const u32 m = c & 7u;
-  const float mag = m >= 2u ? __uint_as_float((m + 252u) << 22) : 0.5f * (float)m;
-  return (c & 8u) ? -mag : mag;
-}
+constexpr int ROW = 72;  // fp16 per LDS row: 64 channels + 8 padding
+constexpr uint32_t kBufDword3 = 0x00020000u;  // raw buffer, 32-bit data format
 
 // 8 codes of one dword (channels 0..7, even channel in the low nibble) times
-// scale s -> 8 bf16 (exact; the product's low 16 bits are zero).
-__device__ __forceinline__ uint4 dequant8(u32 w, float s) {
-  u32 o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float f0 = e2m1_val((w >> (8 * i)) & 0xFu) * s;
-    const float f1 = e2m1_val((w >> (8 * i + 4)) & 0xFu) * s;
-    o[i] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-  }
-  return uint4{o[0], o[1], o[2], o[3]};
+// the scale pair s -> 8 fp16 (exact).
+__device__ __forceinline__ uint4 dequant8(u32 w, h2 s) {
+  const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+  return uint4{__builtin_bit_cast(u32, p0), __builtin_bit_cast(u32, p1), __builtin_bit_cast(u32, p2),
+               __builtin_bit_cast(u32, p3)};
+}
+__device__ __forceinline__ h2 scale_pair(u32 e4m3) {
+  const _Float16 v = (_Float16)e4m3_to_f32(e4m3);  // exact: E4M3 values are fp16 numbers
+  return h2{v, v};
 }
 }  // namespace
 
@@ -58,20 +63,28 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   __shared__ __align__(16) uint16_t sX[2][BM * ROW];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int m_tiles = (M + BM - 1) / BM;
-  const int mt = blockIdx.x % m_tiles, nt = blockIdx.x / m_tiles;
-  const int m0 = mt * BM, n0 = nt * BN;
+  // XCD-contiguous ranges of a banded tile order (see gemm_int4.hip)
+  const int m_tiles = (M + BM - 1) / BM, n_tiles = N / BN;
+  const int tiles = m_tiles * n_tiles;
+  int t = blockIdx.x;
+  if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
+  constexpr int kBandM = 12;
+  const int band = t / (kBandM * n_tiles), in_band = t - band * (kBandM * n_tiles);
+  const int band_m0 = band * kBandM;
+  const int band_h = m_tiles - band_m0 < kBandM ? m_tiles - band_m0 : kBandM;
+  const int m0 = (band_m0 + in_band % band_h) * BM, n0 = (in_band / band_h) * BN;
   const int wn = (wave >> 1) * 64, wm = (wave & 1) * 64;
   const int steps = K >> 6, G = K >> 4;
-  const size_t rowb = (size_t)(K >> 1);
+  const int rowb = K >> 1;
 
   // staging: thread -> (row, 16-byte half = 32 channels = two NVFP4 groups)
   const int srow = tid >> 1, shalf = tid & 1;
-  const bool xvalid = (m0 + srow) < M;
-  const uint8_t* wsrc = wc + (size_t)(n0 + srow) * rowb + shalf * 16;
-  const uint8_t* xsrc = ac + (size_t)(xvalid ? m0 + srow : 0) * rowb + shalf * 16;
-  const uint8_t* wssrc = MODE == 0 ? ws + (size_t)(n0 + srow) * G + 2 * shalf : nullptr;
-  const uint8_t* xssrc = MODE == 0 ? as + (size_t)(xvalid ? m0 + srow : 0) * G + 2 * shalf : nullptr;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wc, (short)0, N * rowb, kBufDword3);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)ac, (short)0, M * rowb, kBufDword3);
+  const __amdgpu_buffer_rsrc_t wsres = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, MODE == 0 ? N * G : 0, kBufDword3);
+  const __amdgpu_buffer_rsrc_t asres = __builtin_amdgcn_make_buffer_rsrc((void*)as, (short)0, MODE == 0 ? M * G : 0, kBufDword3);
+  const int woff = (n0 + srow) * rowb + shalf * 16, xoff = (m0 + srow) * rowb + shalf * 16;  // rows past M: zeros
+  const int wsoff = (n0 + srow) * G + 2 * shalf, xsoff = (m0 + srow) * G + 2 * shalf;
 
   v16f acc[2][2];
 #pragma unroll
@@ -84,16 +97,16 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   uint4 wv, xv;
   u32 wsb = 0x3838u, xsb = 0x3838u;  // two E4M3 scales (1.0, 1.0 in test mode)
   auto gload = [&](int st) {
-    wv = *(const uint4*)(wsrc + st * 32);
-    xv = xvalid ? *(const uint4*)(xsrc + st * 32) : uint4{0u, 0u, 0u, 0u};
+    wv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, woff + st * 32, 0, 0));
+    xv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff + st * 32, 0, 0));
     if constexpr (MODE == 0) {
-      wsb = *(const uint16_t*)(wssrc + st * 4);
-      xsb = xvalid ? *(const uint16_t*)(xssrc + st * 4) : 0u;
+      wsb = __builtin_amdgcn_raw_buffer_load_b16(wsres, wsoff + st * 4, 0, 0);
+      xsb = __builtin_amdgcn_raw_buffer_load_b16(asres, xsoff + st * 4, 0, 0);
     }
   };
   auto sstore = [&](int buf) {
-    const float w0 = e4m3_to_f32(wsb & 0xFFu), w1 = e4m3_to_f32(wsb >> 8);
-    const float x0 = e4m3_to_f32(xsb & 0xFFu), x1 = e4m3_to_f32(xsb >> 8);
+    const h2 w0 = scale_pair(wsb & 0xFFu), w1 = scale_pair(wsb >> 8);
+    const h2 x0 = scale_pair(xsb & 0xFFu), x1 = scale_pair(xsb >> 8);
     uint16_t* dw = &sW[buf][srow * ROW + shalf * 32];
     *(uint4*)(dw + 0) = dequant8(wv.x, w0);
     *(uint4*)(dw + 8) = dequant8(wv.y, w0);
@@ -116,11 +129,11 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
     if (st + 1 < steps) gload(st + 1);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {  // one NVFP4 group per 16-channel MFMA step
-      v8bf a[2], b[2];
+      v8h a[2], b[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        a[i] = *(const v8bf*)&sW[buf][(wn + 32 * i + lr) * ROW + 16 * kk + 8 * lh];
-        b[i] = *(const v8bf*)&sX[buf][(wm + 32 * i + lr) * ROW + 16 * kk + 8 * lh];
+        a[i] = *(const v8h*)&sW[buf][(wn + 32 * i + lr) * ROW + 16 * kk + 8 * lh];
+        b[i] = *(const v8h*)&sX[buf][(wm + 32 * i + lr) * ROW + 16 * kk + 8 * lh];
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -130,7 +143,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
             v16f d;
 #pragma unroll
             for (int v = 0; v < 16; ++v) d[v] = 0.0f;
-            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], d, 0, 0, 0);
             const int m = m0 + wm + 32 * j + lr;
             if (m < M) {
 #pragma unroll
@@ -140,7 +153,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
               }
             }
           } else {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
           }
         }
     }
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
 
 hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st) {
   const int m_tiles = (int)((a.M + BM - 1) / BM);
-  const int blocks = m_tiles * (int)(a.N / BN);
+  const int blocks = m_tiles * (int)(a.N / BN);  // N % 128 == 0
   if (a.psums) {
     hipLaunchKernelGGL(gemm_nvfp4_kernel<1>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
                        (int)a.K, 0, (const uint8_t*)a.act_codes, nullptr, 1.0f,
