@@ -47,9 +47,12 @@ __device__ __forceinline__ uint4 dequant8(u32 w, h2 s) {
   return uint4{__builtin_bit_cast(u32, p0), __builtin_bit_cast(u32, p1), __builtin_bit_cast(u32, p2),
                __builtin_bit_cast(u32, p3)};
 }
-__device__ __forceinline__ h2 scale_pair(u32 e4m3) {
-  const _Float16 v = (_Float16)e4m3_to_f32(e4m3);  // exact: E4M3 values are fp16 numbers
-  return h2{v, v};
+// The two E4M3 scales in the low 16 bits of `bits` -> fp16 (exact: E4M3 values
+// are fp16 numbers), each duplicated into a pair.
+__device__ __forceinline__ void scale_pairs(u32 bits, h2& s0, h2& s1) {
+  const h2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bits, 1.0f, false);
+  s0 = __builtin_shufflevector(v, v, 0, 0);
+  s1 = __builtin_shufflevector(v, v, 1, 1);
 }
 }  // namespace
 
@@ -105,8 +108,9 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
     }
   };
   auto sstore = [&](int buf) {
-    const h2 w0 = scale_pair(wsb & 0xFFu), w1 = scale_pair(wsb >> 8);
-    const h2 x0 = scale_pair(xsb & 0xFFu), x1 = scale_pair(xsb >> 8);
+    h2 w0, w1, x0, x1;
+    scale_pairs(wsb, w0, w1);
+    scale_pairs(xsb, x0, x1);
     uint16_t* dw = &sW[buf][srow * ROW + shalf * 32];
     *(uint4*)(dw + 0) = dequant8(wv.x, w0);
     *(uint4*)(dw + 8) = dequant8(wv.y, w0);
