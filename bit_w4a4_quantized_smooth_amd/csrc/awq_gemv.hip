@@ -44,6 +44,12 @@ constexpr int AWQ_PT = 6;                     // 512-channel blocks whose codes 
 constexpr int AWQ_TBMAX = 16;                 // K <= 8192
 constexpr int AWQ_SS = (AWQ_ROWS * AWQ_TBMAX + AWQ_NT - 1) / AWQ_NT;  // scale items per thread
 
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+constexpr u32 kOnes2 = 0x3F803F80u;  // the bf16 pair (1, 1)
+__device__ __forceinline__ float dot2bf(u32 a, u32 b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a), __builtin_bit_cast(v2bf, b), c, false);
+}
+
 __device__ __forceinline__ v4bf as_v4bf(u32 lo, u32 hi) {
   return __builtin_bit_cast(v4bf, uint2{lo, hi});
 }
@@ -155,10 +161,10 @@ __global__ __launch_bounds__(AWQ_NT) void awq_gemv_kernel(
                       __builtin_amdgcn_perm(w.w, w.y, 0x05040100u),   // (k2, k6)
                       __builtin_amdgcn_perm(w.w, w.y, 0x07060302u)};  // (k3, k7)
     *(uint4*)(lds + (live ? (((tt * 4 + i) * 16 + bb) * MR + m) * 16 : L.trash)) = pr;
-    float sm = bf16_bits_to_f32(w.x & 0xFFFFu) + bf16_bits_to_f32(w.x >> 16);
-    sm += bf16_bits_to_f32(w.y & 0xFFFFu) + bf16_bits_to_f32(w.y >> 16);
-    sm += bf16_bits_to_f32(w.z & 0xFFFFu) + bf16_bits_to_f32(w.z >> 16);
-    sm += bf16_bits_to_f32(w.w & 0xFFFFu) + bf16_bits_to_f32(w.w >> 16);
+    float sm = dot2bf(w.x, kOnes2, 0.0f);  // fp32 sum of the 8 channels
+    sm = dot2bf(w.y, kOnes2, sm);
+    sm = dot2bf(w.z, kOnes2, sm);
+    sm = dot2bf(w.w, kOnes2, sm);
     // the four words of a chunk are adjacent lanes: sum them with quad DPP moves
     sm += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sm), 0xB1, 0xF, 0xF, false));
     sm += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sm), 0x4E, 0xF, 0xF, false));
@@ -254,94 +260,176 @@ __global__ __launch_bounds__(AWQ_NT) void awq_gemv_kernel(
   }
 }
 
-// 4 < M <= 64 (or a K too long for the small kernel's LDS): D[m][n] = sum_k x[m,k] * q[n,k] per 64-channel group on the bf16
-// matrix cores (both operands exact in bf16), then in fp32
-//   acc[m][n] += s[n,g] * (P[m][n] - z[n,g] * xsum[m,g]).
-// Workgroup: 64 weight rows x all (<= 64, zero padded) activation rows; wave w
-// owns the 32x32 block (m half w&1, n half w>>1).  The matrix-core A operand
-// is x (rows m) and B the weight tile (columns n), so each lane holds one
-// column n: its scale and zero-point are per-lane scalars and each store of
-// the 32 lanes covers 64 contiguous bytes of a Y row.
-__global__ __launch_bounds__(256) void awq_gemm_mfma_kernel(
+// Other shapes (4 < M <= 64, or a K the small kernel does not take):
+//   D[m][n] = sum_{k in g} x[m,k] * (128 + q[n,k]) per 64-channel group on the
+//   bf16 matrix cores (both operands exact in bf16), then in fp32
+//   acc[m][n] += s[n,g] * (D[m][n] - (z[n,g] + 128) * xsum[m,g]).
+// Workgroup: 64 weight rows x 64 activation rows (rows past M read as zero);
+// wave w owns the 32x32 block (m half w&1, n half (w>>1)&1).  The matrix-core A
+// operand is x (rows m) and B the weight tile (columns n), so each lane holds
+// one column n: its scale and zero-point are per-lane scalars and each store
+// of the 32 lanes covers 64 contiguous bytes of a Y row.  Eight waves: waves
+// 0-3 take the first 64-channel group of every stage and waves 4-7 the
+// second, so two waves share each SIMD; their partial sums meet in LDS at
+// the end (fixed order).  Stages of two groups are double buffered in LDS;
+// the next stage's x, codes, scales and zero-points are loaded (branch-free
+// buffer loads) while the current one computes.  Within each 8-channel block both operands take the channel
+// order (k0,k4) (k1,k5) (k2,k6) (k3,k7), which is the order the AND-OR code
+// expansion produces.
+namespace {
+constexpr int AG_ROW = 136;  // bf16 per LDS row: two 64-channel groups + 8 padding
+struct AwqGemmLds {
+  uint16_t x[2][64 * AG_ROW];   // x pairs, per buffer
+  uint16_t w[2][64 * AG_ROW];   // 128 + q as bf16, per buffer
+  float xs[2][2][64];           // [buffer][group][m] sum of x over the group
+  float sc[2][2][64];           // [buffer][group][n] scale
+  float zp[2][2][64];           // [buffer][group][n] zero-point + 128
+};
+}  // namespace
+
+__global__ __launch_bounds__(512) void awq_gemm_mfma_kernel(
     int M, int N, int K, const uint16_t* __restrict__ x, const uint8_t* __restrict__ wc,
     const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wz,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y) {
-  constexpr int ROW = 72;  // bf16 per LDS row: 64 channels + 8 padding
-  __shared__ __align__(16) uint16_t sX[64 * ROW];
-  __shared__ __align__(16) uint16_t sW[64 * ROW];
-  __shared__ float sXS[64];
-
+  extern __shared__ __align__(16) uint8_t awq_smem[];
+  AwqGemmLds& L = *(AwqGemmLds*)awq_smem;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n0 = blockIdx.x * 64;
-  const int G = K >> 6;
-  const size_t rowb = (size_t)(K >> 1);
-  const int bm = (wave & 1) * 32, bn = (wave >> 1) * 32;
+  const int G = K >> 6, rowb = K >> 1, stages = (G + 1) >> 1;
+  // waves 0-3 take the first group of every stage, waves 4-7 the second
+  const int half = wave >> 2;
+  const int bm = (wave & 1) * 32, bn = ((wave >> 1) & 1) * 32;
   const int lr = lane & 31, lh = lane >> 5;
-  const int n = n0 + bn + lr;
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * K * 2, kBufDword3);
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wc, (short)0, N * rowb, kBufDword3);
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, N * G * 2, kBufDword3);
+  const __amdgpu_buffer_rsrc_t zres = __builtin_amdgcn_make_buffer_rsrc((void*)wz, (short)0, N * G * 2, kBufDword3);
+
+  // staging roles: x chunk c = tid + 512 r (r < 2) -> row c/16, 8-channel block
+  // c%16; threads < 256: codes of row tid/4, 32 codes (tid%4); threads >= 256:
+  // scale (t < 384) or zero-point of row t%64, group (t/64)%2
+  uint4 xv[2], wv;
+  u32 szv;
+  const bool is_w = tid < 256;
+  auto gload = [&](int st) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int c = tid + 512 * r, row = c >> 4, blk = c & 15;
+      const bool ok = row < M && 2 * st + (blk >> 3) < G;
+      xv[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            xres, ok ? (row * K + 128 * st + 8 * blk) * 2 : kOut, 0, 0));
+    }
+    if (is_w) {  // wave-uniform
+      const int row = tid >> 2, part = tid & 3;
+      const bool ok = 2 * st + (part >> 1) < G;
+      wv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         wres, ok ? (n0 + row) * rowb + 64 * st + 16 * part : kOut, 0, 0));
+    } else {
+      const int row = tid & 63, g = 2 * st + ((tid >> 6) & 1);
+      const int off = g < G ? ((n0 + row) * G + g) * 2 : kOut;
+      szv = tid < 384 ? __builtin_amdgcn_raw_buffer_load_b16(sres, off, 0, 0)
+                      : __builtin_amdgcn_raw_buffer_load_b16(zres, off, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int c = tid + 512 * r, row = c >> 4, blk = c & 15;
+      const uint4 v = xv[r];
+      *(uint4*)&L.x[buf][row * AG_ROW + 8 * blk] =
+          uint4{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
+      // fp32 sum of the 8 channels: pairs of bf16 times (1, 1) on v_dot2_f32_bf16
+      float sm = dot2bf(v.x, kOnes2, 0.0f);
+      sm = dot2bf(v.y, kOnes2, sm);
+      sm = dot2bf(v.z, kOnes2, sm);
+      sm = dot2bf(v.w, kOnes2, sm);
+      // the 8 blocks of a group are 8 adjacent lanes: quad DPP, then the lane 4 above
+      sm += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sm), 0xB1, 0xF, 0xF, false));
+      sm += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sm), 0x4E, 0xF, 0xF, false));
+      sm += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, sm), 0x104, 0xF, 0xF, false));
+      if ((blk & 7) == 0) L.xs[buf][blk >> 3][row] = sm;
+    }
+    if (is_w) {
+      const int row = tid >> 2, part = tid & 3;
+      const u32 d4[4] = {wv.x, wv.y, wv.z, wv.w};
+      u32 o[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32 d = d4[i];
+        o[4 * i + 0] = (d & 0x000F000Fu) | 0x43004300u;          // (k0, k4)
+        o[4 * i + 1] = ((d >> 4) & 0x000F000Fu) | 0x43004300u;   // (k1, k5)
+        o[4 * i + 2] = ((d >> 8) & 0x000F000Fu) | 0x43004300u;   // (k2, k6)
+        o[4 * i + 3] = ((d >> 12) & 0x000F000Fu) | 0x43004300u;  // (k3, k7)
+      }
+      uint16_t* dst = &L.w[buf][row * AG_ROW + 32 * part];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(uint4*)(dst + 8 * i) = uint4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+    } else {
+      const int row = tid & 63, g = (tid >> 6) & 1;
+      const float v = f16_bits_to_f32(szv);
+      if (tid < 384) L.sc[buf][g][row] = v;
+      else L.zp[buf][g][row] = v + 128.0f;
+    }
+  };
 
   v16f acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
 
-  // staging: x rows 64 x 64 channels (thread: row tid>>2, 16 channels);
-  //          weight rows 64 x 32 bytes (thread: row tid>>2, 8 bytes = 16 codes)
-  const int srow = tid >> 2, sq = tid & 3;
-  for (int g = 0; g < G; ++g) {
-    uint4 xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
-    if (srow < M) {
-      const uint4* src = (const uint4*)(x + (size_t)srow * K + 64 * g + 16 * sq);
-      xa = src[0];
-      xb = src[1];
-    }
-    const uint2 wq = *(const uint2*)(wc + (size_t)(n0 + srow) * rowb + 32 * g + 8 * sq);
-    __syncthreads();  // previous group's LDS reads are done
-    *(uint4*)&sX[srow * ROW + 16 * sq] = xa;
-    *(uint4*)&sX[srow * ROW + 16 * sq + 8] = xb;
-    // codes -> bf16 values 0..15 (exact): 0x4300|q is 128+q, minus 128 below
-    u32 wb[8];
-    const u32 wq2[2] = {wq.x, wq.y};
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int st = 0; st < stages; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < stages) gload(st + 1);
+    if (2 * st + half < G) {  // wave-uniform: a last stage may hold one group
+      const int gg = half;
+      v16f d;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int v = 0; v < 16; ++v) d[v] = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const u32 q0 = (wq2[h] >> (8 * e)) & 0xFu, q1 = (wq2[h] >> (8 * e + 4)) & 0xFu;
-        const float f0 = (float)q0, f1 = (float)q1;
-        wb[4 * h + e] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+      for (int kk = 0; kk < 4; ++kk) {
+        const v8bf a = *(const v8bf*)&L.x[buf][(bm + lr) * AG_ROW + 64 * gg + 16 * kk + 8 * lh];
+        const v8bf b = *(const v8bf*)&L.w[buf][(bn + lr) * AG_ROW + 64 * gg + 16 * kk + 8 * lh];
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d, 0, 0, 0);
       }
-    *(uint4*)&sW[srow * ROW + 16 * sq] = uint4{wb[0], wb[1], wb[2], wb[3]};
-    *(uint4*)&sW[srow * ROW + 16 * sq + 8] = uint4{wb[4], wb[5], wb[6], wb[7]};
-    // per-row sums of x over the group (fp32), four threads per row
-    float ps = 0.0f;
-    const u32 xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+      const float sc = L.sc[buf][gg][bn + lr], zp = L.zp[buf][gg][bn + lr];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ps += bf16_bits_to_f32(xw[i] & 0xFFFFu) + bf16_bits_to_f32(xw[i] >> 16);
-    ps += __shfl_xor(ps, 1, 64);
-    ps += __shfl_xor(ps, 2, 64);
-    if (sq == 0) sXS[srow] = ps;
-    __syncthreads();
-
-    v16f d;
+      for (int q = 0; q < 4; ++q) {
+        const float4 xs4 = *(const float4*)&L.xs[buf][gg][bm + 8 * q + 4 * lh];
+        const float xs[4] = {xs4.x, xs4.y, xs4.z, xs4.w};
 #pragma unroll
-    for (int v = 0; v < 16; ++v) d[v] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const v8bf a = *(const v8bf*)&sX[(bm + lr) * ROW + 16 * kk + 8 * lh];
-      const v8bf b = *(const v8bf*)&sW[(bn + lr) * ROW + 16 * kk + 8 * lh];
-      d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d, 0, 0, 0);
+        for (int v = 0; v < 4; ++v)
+          acc[4 * q + v] = fmaf(sc, fmaf(-zp, xs[v], d[4 * q + v]), acc[4 * q + v]);
+      }
     }
-    const float s = f16_bits_to_f32(ws[(size_t)n * G + g]);
-    const float z = f16_bits_to_f32(wz[(size_t)n * G + g]);
+    if (st + 1 < stages) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // the second half's partial sums go through LDS (the staging space is free now)
+  float* red = (float*)awq_smem;  // [4 blocks][64 lanes][16]
+  const int blkid = wave & 3;
+  if (half == 1) {
+#pragma unroll
+    for (int v = 0; v < 16; v += 4)
+      *(float4*)&red[(blkid * 64 + lane) * 16 + v] = float4{acc[v], acc[v + 1], acc[v + 2], acc[v + 3]};
+  }
+  __syncthreads();
+  if (half == 0) {
+#pragma unroll
+    for (int v = 0; v < 16; v += 4) {
+      const float4 o = *(const float4*)&red[(blkid * 64 + lane) * 16 + v];
+      acc[v] += o.x; acc[v + 1] += o.y; acc[v + 2] += o.z; acc[v + 3] += o.w;
+    }
+    const int n = n0 + bn + lr;
+    const float bv = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int ml = bm + 8 * (v >> 2) + 4 * lh + (v & 3);
-      acc[v] = fmaf(s, fmaf(-z, sXS[ml], d[v]), acc[v]);
+      const int m = bm + 8 * (v >> 2) + 4 * lh + (v & 3);
+      if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_bits(acc[v] + bv);
     }
-  }
-  const float bv = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int m = bm + 8 * (v >> 2) + 4 * lh + (v & 3);
-    if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_bits(acc[v] + bv);
   }
 }
 
@@ -362,7 +450,10 @@ hipError_t launch_awq(const AwqArgs& a, hipStream_t st) {
                        M, N, K, (const uint16_t*)a.x, (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales,
                        (const uint16_t*)a.w_zeros, (const uint16_t*)a.bias, (uint16_t*)a.y);
   } else {
-    hipLaunchKernelGGL(awq_gemm_mfma_kernel, dim3(N / 64), dim3(256), 0, st, M, N, K,
+    const hipError_t e = hipFuncSetAttribute((const void*)awq_gemm_mfma_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AwqGemmLds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(awq_gemm_mfma_kernel, dim3(N / 64), dim3(512), sizeof(AwqGemmLds), st, M, N, K,
                        (const uint16_t*)a.x, (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales,
                        (const uint16_t*)a.w_zeros, (const uint16_t*)a.bias, (uint16_t*)a.y);
   }
