@@ -103,7 +103,32 @@ __global__ __launch_bounds__(QuantCfg<RB>::NT) void quant_act_kernel(
 #pragma unroll
   for (int u = 0; u < W; ++u) issue(u, u);
 
-  for (int k = tid; k < K; k += NT) rl[k] = lam ? 1.0f / bf16_bits_to_f32(lam[k]) : 1.0f;
+  // lambda reciprocals: 8 channels per 16-byte load, every load of this
+  // thread issued before the first division (K <= 32768: at most 8 each)
+  {
+    const __amdgpu_buffer_rsrc_t lamres = __builtin_amdgcn_make_buffer_rsrc((void*)lam, (short)0, lam ? K * 2 : 0, 0x00020000);
+    constexpr int LCH = 8;
+    uint4 lv[LCH];
+#pragma unroll
+    for (int i = 0; i < LCH; ++i) {
+      const int ch = tid + NT * i;  // 8-channel chunk
+      lv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lamres, ch * 8 < K ? ch * 16 : kOut, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < LCH; ++i) {
+      const int ch = tid + NT * i;
+      if (ch * 8 >= K) break;
+      const u32 w4[4] = {lv[i].x, lv[i].y, lv[i].z, lv[i].w};
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = lam ? 1.0f / bf16_bits_to_f32(w4[e] & 0xFFFFu) : 1.0f;
+        o[2 * e + 1] = lam ? 1.0f / bf16_bits_to_f32(w4[e] >> 16) : 1.0f;
+      }
+      *(float4*)&rl[ch * 8] = float4{o[0], o[1], o[2], o[3]};
+      *(float4*)&rl[ch * 8 + 4] = float4{o[4], o[5], o[6], o[7]};
+    }
+  }
   __syncthreads();
 
   v4f acc[RBX];
