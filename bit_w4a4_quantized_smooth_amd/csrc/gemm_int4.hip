@@ -93,19 +93,6 @@ __device__ __forceinline__ uint4 nib_hi16(uint4 v) {  // 16*q of odd channels
   return uint4{v.x & 0xF0F0F0F0u, v.y & 0xF0F0F0F0u, v.z & 0xF0F0F0F0u, v.w & 0xF0F0F0F0u};
 }
 
-// 8 fp16 scales of one row starting at group kb (zero past the last group).
-// Rows of 8k groups are 16-byte aligned: one vector load.
-__device__ __forceinline__ v8h load_scales8(const uint16_t* row, int kb, int G) {
-  if ((G & 7) == 0) return kb < G ? *(const v8h*)(row + kb) : __builtin_bit_cast(v8h, uint4{0u, 0u, 0u, 0u});
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = kb + 2 * i < G ? row[kb + 2 * i] : 0u;
-    const uint32_t hi = kb + 2 * i + 1 < G ? row[kb + 2 * i + 1] : 0u;
-    w[i] = lo | (hi << 16);
-  }
-  return __builtin_bit_cast(v8h, uint4{w[0], w[1], w[2], w[3]});
-}
 }  // namespace
 
 template <int MODE>  // 0: Y = bf16 linear output; 1: int32 partial products
@@ -341,53 +328,59 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
     // Epilogue.  Every global load it needs (bias, the scale rows of the
     // sum_g S product, the first low-rank slices) is issued before any of them
     // is consumed, so the workgroup pays one memory latency here, not several.
+    // (branch-free buffer loads: rows past N or M, groups past G and rank
+    // slices past r read as zero)
+    constexpr int kOutE = 0x7FFFFFF0;
+    const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc((void*)bias, (short)0, bias ? N * 2 : 0, kBufDword3);
+    const __amdgpu_buffer_rsrc_t l2res = __builtin_amdgcn_make_buffer_rsrc((void*)l2t, (short)0, N * rank * 2, kBufDword3);
+    const __amdgpu_buffer_rsrc_t x1res = __builtin_amdgcn_make_buffer_rsrc((void*)xl1, (short)0, M * rank * 4, kBufDword3);
     uint2 bb[BI];
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
       const int n = n0 + wn + 16 * i + 4 * lg;
-      bb[i] = (bias && n < N) ? *(const uint2*)(bias + n) : uint2{0u, 0u};
+      bb[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(bres, n * 2, 0, 0));
     }
-    auto load_ts = [&](int kb, v8h* aw, v8h* bx) {
+    // 8 fp16 scales of one row from group g0 (zeros past G and past the tensor)
+    auto load8h = [&](__amdgpu_buffer_rsrc_t res, int row, int g0) -> v8h {
+      if ((G & 7) == 0)  // rows of 8k groups: one 16-byte load
+        return __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(res, g0 < G ? (row * G + g0) * 2 : kOutE, 0, 0));
+      u32 w[4];
 #pragma unroll
-      for (int i = 0; i < BI; ++i) {
-        const int n = n0 + wn + 16 * i + l16;
-        aw[i] = n < N ? load_scales8(ws + (size_t)n * G, kb + 8 * lg, G)
-                      : __builtin_bit_cast(v8h, uint4{0u, 0u, 0u, 0u});
+      for (int e = 0; e < 4; ++e) {
+        const u32 lo = __builtin_amdgcn_raw_buffer_load_b16(res, g0 + 2 * e < G ? (row * G + g0 + 2 * e) * 2 : kOutE, 0, 0);
+        const u32 hi = __builtin_amdgcn_raw_buffer_load_b16(res, g0 + 2 * e + 1 < G ? (row * G + g0 + 2 * e + 1) * 2 : kOutE, 0, 0);
+        w[e] = lo | (hi << 16);
       }
-#pragma unroll
-      for (int j = 0; j < BJ; ++j) {
-        const int m = m0 + wm + 16 * j + l16;
-        bx[j] = m < M ? load_scales8(as + (size_t)m * G, kb + 8 * lg, G)
-                      : __builtin_bit_cast(v8h, uint4{0u, 0u, 0u, 0u});
-      }
+      return __builtin_bit_cast(v8h, uint4{w[0], w[1], w[2], w[3]});
     };
-    auto load_lr = [&](int jb, v8bf* al, float4* xf) {
+    v8h aw[2][BI], bx[2][BJ];
+    auto load_ts = [&](int kb, int h) {
+#pragma unroll
+      for (int i = 0; i < BI; ++i) aw[h][i] = load8h(wsres, n0 + wn + 16 * i + l16, kb + 8 * lg);
+#pragma unroll
+      for (int j = 0; j < BJ; ++j) bx[h][j] = load8h(asres, m0 + wm + 16 * j + l16, kb + 8 * lg);
+    };
+    v8bf al[BI];
+    float4 xf[2 * BJ];
+    auto load_lr = [&](int jb) {
       const bool live = jb + 8 * lg < rank;  // rank 16 leaves lane groups 2, 3 empty
 #pragma unroll
       for (int i = 0; i < BI; ++i) {
         const int n = n0 + wn + 16 * i + l16;
-        al[i] = (live && n < N) ? *(const v8bf*)(l2t + (size_t)n * rank + jb + 8 * lg)
-                                : __builtin_bit_cast(v8bf, uint4{0u, 0u, 0u, 0u});
+        al[i] = __builtin_bit_cast(v8bf, __builtin_amdgcn_raw_buffer_load_b128(
+                                             l2res, live ? (n * rank + jb + 8 * lg) * 2 : kOutE, 0, 0));
       }
 #pragma unroll
       for (int j = 0; j < BJ; ++j) {
         const int m = m0 + wm + 16 * j + l16;
-        if (live && m < M) {
-          const float4* src4 = (const float4*)(xl1 + (size_t)m * rank + jb + 8 * lg);
-          xf[2 * j] = src4[0];
-          xf[2 * j + 1] = src4[1];
-        } else {
-          xf[2 * j] = float4{0.f, 0.f, 0.f, 0.f};
-          xf[2 * j + 1] = float4{0.f, 0.f, 0.f, 0.f};
-        }
+        const int off = live ? (m * rank + jb + 8 * lg) * 4 : kOutE;
+        xf[2 * j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(x1res, off, 0, 0));
+        xf[2 * j + 1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(x1res, live ? off + 16 : kOutE, 0, 0));
       }
     };
-    v8h aw[2][BI], bx[2][BJ];
-    v8bf al[BI];
-    float4 xf[2 * BJ];
-    load_ts(0, aw[0], bx[0]);
-    if (G > 32) load_ts(32, aw[1], bx[1]);
-    if (rank > 0) load_lr(0, al, xf);
+    load_ts(0, 0);
+    if (G > 32) load_ts(32, 1);
+    if (rank > 0) load_lr(0);
 
     // sum_g S = Sw . Sa^T on the matrix core (v_mfma_f32_16x16x32_f16, K = 32
     // groups per instruction), then y = 2^18 * (acc - c0 * sum_g S)
@@ -406,8 +399,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
             for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(-c0, T[v], acc[i][j][v]);
           }
       }
-      if (kb + 64 < G) load_ts(kb + 64, aw[0], bx[0]);
-      if (kb + 96 < G) load_ts(kb + 96, aw[1], bx[1]);
+      if (kb + 64 < G) load_ts(kb + 64, 0);
+      if (kb + 96 < G) load_ts(kb + 96, 1);
     }
 #pragma unroll
     for (int i = 0; i < BI; ++i)
@@ -419,7 +412,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
     // low-rank up-projection on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16):
     // acc += L2^T[n, :] . XL1[m, :]; lane = (row l16, rank entries 8*lg .. +8)
     for (int jb = 0; jb < rank; jb += 32) {
-      if (jb > 0) load_lr(jb, al, xf);
+      if (jb > 0) load_lr(jb);
       v8bf bl[BJ];
 #pragma unroll
       for (int j = 0; j < BJ; ++j) {
