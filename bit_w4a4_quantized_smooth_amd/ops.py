@@ -1,0 +1,129 @@
+"""torch custom ops over the C ABI, so that a model using the SVDQuant W4A4 and
+AWQ W4A16 linears can be traced whole by torch.compile (fullgraph=True).
+
+The pages say the quantized linear layers work under torch.compile ("Nunchaku
+Lite", section "torch.compile"; blog "Nunchaku 4-bit inference in Diffusers",
+"Benchmarks").  Here each library entry point becomes one opaque operator
+(`svdq::quantize_act`, `svdq::w4a4_gemm`, `svdq::awq_gemv`) with a fake
+(meta) implementation that only computes output shapes and dtypes, so the
+tracer never runs a kernel; the real implementation is the ctypes call into
+libsvdq.so on the tensors' current stream.  Nothing here computes: every
+arithmetic step stays in the library's kernels.
+
+`SVDQLinear` and `AWQLinear` are nn.Modules holding the packed layer tensors
+(as buffers) whose forward uses these operators.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+from torch import Tensor
+
+from . import SVDQ_INT4, SVDQ_NVFP4, GROUP, awq_gemv, quantize_act, w4a4_gemm
+
+_SCALE_DTYPE = {SVDQ_INT4: torch.float16, SVDQ_NVFP4: torch.uint8}
+
+
+@torch.library.custom_op("svdq::quantize_act", mutates_args=())
+def quantize_act_op(x: Tensor, smooth: Optional[Tensor], l1t: Optional[Tensor], precision: int,
+                    act_global_scale: float) -> Tuple[Tensor, Tensor, Tensor]:
+    """svdq_quantize_act: returns (codes u8 [M, K/2], scales, xl1 fp32 [M, r]); r = 0 gives an
+    empty xl1."""
+    codes, scales, xl1 = quantize_act(precision, x, smooth, l1t, act_global_scale)
+    if xl1 is None:
+        xl1 = x.new_empty((x.shape[0], 0), dtype=torch.float32)
+    return codes, scales, xl1
+
+
+@quantize_act_op.register_fake
+def _(x, smooth, l1t, precision, act_global_scale):
+    M, K = x.shape
+    r = 0 if l1t is None else l1t.shape[0]
+    return (x.new_empty((M, K // 2), dtype=torch.uint8),
+            x.new_empty((M, K // GROUP[precision]), dtype=_SCALE_DTYPE[precision]),
+            x.new_empty((M, r), dtype=torch.float32))
+
+
+@torch.library.custom_op("svdq::w4a4_gemm", mutates_args=())
+def w4a4_gemm_op(act_codes: Tensor, act_scales: Tensor, w_codes: Tensor, w_scales: Tensor,
+                 xl1: Optional[Tensor], l2t: Optional[Tensor], bias: Optional[Tensor], precision: int,
+                 act_global_scale: float, w_global_scale: float) -> Tensor:
+    """svdq_w4a4_gemm: Y bf16 [M, N]."""
+    if xl1 is not None and xl1.shape[1] == 0:
+        xl1 = None
+    return w4a4_gemm(precision, act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias,
+                     act_global_scale, w_global_scale)
+
+
+@w4a4_gemm_op.register_fake
+def _(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, precision, act_global_scale, w_global_scale):
+    return act_codes.new_empty((act_codes.shape[0], w_codes.shape[0]), dtype=torch.bfloat16)
+
+
+@torch.library.custom_op("svdq::awq_gemv", mutates_args=())
+def awq_gemv_op(x: Tensor, w_codes: Tensor, w_scales: Tensor, w_zeros: Tensor, bias: Optional[Tensor]) -> Tensor:
+    """awq_w4a16_gemv: y bf16 [M, N]."""
+    return awq_gemv(x, w_codes, w_scales, w_zeros, bias)
+
+
+@awq_gemv_op.register_fake
+def _(x, w_codes, w_scales, w_zeros, bias):
+    return x.new_empty((x.shape[0], w_codes.shape[0]), dtype=torch.bfloat16)
+
+
+def svdq_linear(x: Tensor, smooth: Optional[Tensor], l1t: Optional[Tensor], w_codes: Tensor, w_scales: Tensor,
+                l2t: Optional[Tensor], bias: Optional[Tensor], precision: int = SVDQ_INT4,
+                act_global_scale: float = 1.0, w_global_scale: float = 1.0) -> Tensor:
+    """The SVDQuant linear as two traceable operators; x may have any leading shape."""
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, x.shape[-1])
+    codes, scales, xl1 = torch.ops.svdq.quantize_act(x2, smooth, l1t, precision, act_global_scale)
+    y = torch.ops.svdq.w4a4_gemm(codes, scales, w_codes, w_scales, xl1, l2t, bias, precision,
+                                 act_global_scale, w_global_scale)
+    return y.reshape(*lead, w_codes.shape[0])
+
+
+class SVDQLinear(torch.nn.Module):
+    """A linear layer in SVDQuant W4A4 form ([Lite] "NunchakuLiteQuantizationConfig":
+    precision, group size, rank): smoothing factor, rank-r low-rank branch in bf16,
+    4-bit residual weight with per-group scales.  Tensors use the C ABI's layouts
+    (nn.Linear orientation: codes [N, K/2], l1t = L1^T [r, K], l2t = L2^T [N, r])."""
+
+    def __init__(self, in_features: int, out_features: int, rank: int = 32, precision: int = SVDQ_INT4,
+                 bias: bool = True, device=None):
+        super().__init__()
+        G = GROUP[precision]
+        self.precision, self.rank = precision, rank
+        self.in_features, self.out_features = in_features, out_features
+        kw = dict(device=device)
+        self.register_buffer("smooth", torch.ones(in_features, dtype=torch.bfloat16, **kw))
+        self.register_buffer("w_codes", torch.zeros(out_features, in_features // 2, dtype=torch.uint8, **kw))
+        self.register_buffer("w_scales", torch.zeros(out_features, in_features // G, dtype=_SCALE_DTYPE[precision], **kw))
+        self.register_buffer("l1t", torch.zeros(rank, in_features, dtype=torch.bfloat16, **kw) if rank else None)
+        self.register_buffer("l2t", torch.zeros(out_features, rank, dtype=torch.bfloat16, **kw) if rank else None)
+        self.register_buffer("bias", torch.zeros(out_features, dtype=torch.bfloat16, **kw) if bias else None)
+        self.act_global_scale = 1.0  # NVFP4: static, calibrated offline
+        self.w_global_scale = 1.0
+
+    def forward(self, x: Tensor) -> Tensor:
+        return svdq_linear(x, self.smooth, self.l1t, self.w_codes, self.w_scales, self.l2t, self.bias,
+                           self.precision, self.act_global_scale, self.w_global_scale)
+
+
+class AWQLinear(torch.nn.Module):
+    """A linear layer in AWQ W4A16 form (int4 weight-only, group 64, unsigned codes with
+    fp16 scale and zero-point per (row, group))."""
+
+    def __init__(self, in_features: int, out_features: int, bias: bool = True, device=None):
+        super().__init__()
+        kw = dict(device=device)
+        self.register_buffer("w_codes", torch.zeros(out_features, in_features // 2, dtype=torch.uint8, **kw))
+        self.register_buffer("w_scales", torch.zeros(out_features, in_features // 64, dtype=torch.float16, **kw))
+        self.register_buffer("w_zeros", torch.zeros(out_features, in_features // 64, dtype=torch.float16, **kw))
+        self.register_buffer("bias", torch.zeros(out_features, dtype=torch.bfloat16, **kw) if bias else None)
+
+    def forward(self, x: Tensor) -> Tensor:
+        lead = x.shape[:-1]
+        y = torch.ops.svdq.awq_gemv(x.reshape(-1, x.shape[-1]), self.w_codes, self.w_scales, self.w_zeros, self.bias)
+        return y.reshape(*lead, self.w_codes.shape[0])
