@@ -126,6 +126,32 @@ def svdq_layer(seed: int, M: int, N: int, K: int, rank: int, prec: int = INT4,
                 l1t=np.ascontiguousarray(l1t), l2t=np.ascontiguousarray(l2t), bias=bias)
 
 
+def rope_table(S: int, head_dim: int, base: float = 10000.0) -> np.ndarray:
+    """fp32 [S, head_dim/2, 2] (cos, sin) pairs of the angles s * base^(-2p/head_dim) for
+    token positions s = 0..S-1 and channel pairs p: a standard rotary table (the
+    operator takes any table of (cos, sin) pairs as an input)."""
+    s = np.arange(S, dtype=np.float64)[:, None]
+    p = np.arange(head_dim // 2, dtype=np.float64)[None, :]
+    ang = s * base ** (-2.0 * p / head_dim)
+    return np.ascontiguousarray(np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32))
+
+
+def qkv_layer(seed: int, M: int, heads: int, head_dim: int, K: int, rank: int, prec: int = INT4,
+              outlier_frac: float = 0.01, outlier_scale: float = 20.0, S: int | None = None,
+              with_rope: bool = True, with_bias: bool = True) -> dict:
+    """All inputs of the fused attention projection: an svdq_w4a4 linear with
+    N = 3 * heads * head_dim (Q, K, V weights concatenated in that order), per-head
+    RMSNorm weights norm_q, norm_k bf16 ~ U(0.5, 1.5) [head_dim], eps = 1e-6, and a
+    rotary table for S positions (default S = M: one sequence)."""
+    d = svdq_layer(seed, M, 3 * heads * head_dim, K, rank, prec, outlier_frac, outlier_scale,
+                   with_bias=with_bias)
+    d.update(heads=heads, head_dim=head_dim,
+             norm_q=to_bf16_bits(_rng(seed, 9).uniform(0.5, 1.5, head_dim)),
+             norm_k=to_bf16_bits(_rng(seed, 10).uniform(0.5, 1.5, head_dim)),
+             eps=1e-6, rope=rope_table(S if S is not None else M, head_dim) if with_rope else None)
+    return d
+
+
 def awq_layer(seed: int, M: int, N: int, K: int, with_bias: bool = True) -> dict:
     """All inputs of one awq_w4a16 linear: x bf16 ~ N(0,1) [M, K]; unsigned codes
     uniform in 0..15 [N, K]; fp16 scales ~ U(0.005, 0.02) and fp16 zero-points

@@ -181,3 +181,39 @@ def awq_linear(x, w_codes, w_scales, w_zeros, bias=None, rows=None, cols=None, n
                           _p(w_zeros), _p(bias), _i64(count), _p(ri), _p(ci), _p(y), _p(yb),
                           ctypes.c_int(nthreads))
     return y, yb
+
+
+def qkv_norm_rope(y, row_ids, heads, head_dim, norm_q, norm_k, eps, rope=None):
+    """Q/K RMSNorm + rotary epilogue on the projection y float64 [rows, 3*heads*D] of
+    tokens row_ids; returns (y float64, y_bf16 uint16) of the same shape."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    rows = y.shape[0]
+    assert y.shape[1] == 3 * heads * head_dim
+    rid = np.ascontiguousarray(row_ids if row_ids is not None else np.arange(rows), dtype=np.int64)
+    nq = np.ascontiguousarray(norm_q, dtype=np.uint16)
+    nk = np.ascontiguousarray(norm_k, dtype=np.uint16)
+    assert nq.shape == (head_dim,) and nk.shape == (head_dim,)
+    rope_rows = 0
+    if rope is not None:
+        rope = np.ascontiguousarray(rope, dtype=np.float32)
+        assert rope.shape[1:] == (head_dim // 2, 2)
+        rope_rows = rope.shape[0]
+    out = np.zeros_like(y)
+    outb = np.zeros(y.shape, np.uint16)
+    _lib().orc_qkv_norm_rope(_i64(rows), ctypes.c_int(heads), ctypes.c_int(head_dim), _p(y), _p(rid),
+                             _p(nq), _p(nk), ctypes.c_double(eps), _p(rope), _i64(rope_rows),
+                             _p(out), _p(outb))
+    return out, outb
+
+
+def w4a4_linear_qkv(prec, a_codes, a_scales, w_codes, w_scales, xl1, l2t, bias, heads, head_dim,
+                    norm_q, norm_k, eps, rope=None, alpha_a=1.0, alpha_w=1.0, rows=None, nthreads=0):
+    """The fused attention projection: w4a4_linear over whole rows (all of them, or the
+    token rows `rows`), then qkv_norm_rope.  Returns (y float64, y_bf16) [rows, N]."""
+    M, N = a_codes.shape[0], w_codes.shape[0]
+    rid = np.arange(M, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    ri = np.repeat(rid, N)
+    ci = np.tile(np.arange(N, dtype=np.int64), rid.size)
+    y, _ = w4a4_linear(prec, a_codes, a_scales, w_codes, w_scales, xl1, l2t, bias, alpha_a=alpha_a,
+                       alpha_w=alpha_w, rows=ri, cols=ci, nthreads=nthreads)
+    return qkv_norm_rope(y.reshape(rid.size, N), rid, heads, head_dim, norm_q, norm_k, eps, rope)

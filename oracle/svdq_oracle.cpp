@@ -449,4 +449,60 @@ void orc_awq_linear(int64_t M, int64_t N, int64_t K, const uint16_t* x, const ui
   }
 }
 
+// ---------------------------------------------------------------------------
+// Q/K/V epilogue of the fused attention projection (blog "Nunchaku 4-bit
+// inference in Diffusers", "Quantizing models with structural rewrites": the
+// Q, K and V projections are one linear whose output concatenates Q, K and V
+// in that order, and one operator applies the projection, the Q and K
+// normalizations and the rotary embedding; "Nunchaku Lite", "Fused kernels":
+// the QKV + RMSNorm + RoPE fusion of the original engine).  The pages give
+// the order of the steps (norm of Q and K, then the rotary embedding) but no
+// formulas; readings, all in double:
+//   * columns: [Q | K | V], each heads*D wide; head h of Q is columns
+//     h*D .. h*D+D-1, of K the same plus heads*D; V is left as it is;
+//   * RMSNorm of one head of one token: y_d * w_d / sqrt(mean_d(y_d^2) + eps),
+//     w = norm_q (bf16 [D]) for Q heads, norm_k for K heads;
+//   * rotary embedding, applied after the norm: channel pairs (2p, 2p+1) of
+//     the head are rotated by the angle of table entry (s, p):
+//     (a, b) -> (a*cos - b*sin, a*sin + b*cos), with (cos, sin) given as fp32
+//     pairs in rope [S, D/2, 2]; token row m uses table row m mod S (rows are
+//     batch-major [batch, S]).  rope == NULL: no rotation.
+// y_in [rows, 3*heads*D] holds the projection (bias included) of the tokens
+// row_ids[i]; y_out gets the result in double and y_bf16 (may be NULL) its
+// bf16 rounding.
+// ---------------------------------------------------------------------------
+void orc_qkv_norm_rope(int64_t rows, int heads, int D, const double* y_in, const int64_t* row_ids,
+                       const uint16_t* norm_q, const uint16_t* norm_k, double eps,
+                       const float* rope, int64_t rope_rows, double* y_out, uint16_t* y_bf16) {
+  const int64_t HD = (int64_t)heads * D, N = 3 * HD;
+  std::vector<double> head(D);
+  for (int64_t i = 0; i < rows; ++i) {
+    const double* yi = y_in + i * N;
+    double* yo = y_out + i * N;
+    for (int64_t n = 0; n < N; ++n) yo[n] = yi[n];
+    for (int part = 0; part < 2; ++part) {  // 0: Q, 1: K
+      const uint16_t* w = part == 0 ? norm_q : norm_k;
+      for (int h = 0; h < heads; ++h) {
+        const int64_t c0 = part * HD + (int64_t)h * D;
+        double ss = 0.0;
+        for (int d = 0; d < D; ++d) ss += yi[c0 + d] * yi[c0 + d];
+        const double inv = 1.0 / std::sqrt(ss / D + eps);
+        for (int d = 0; d < D; ++d) head[d] = yi[c0 + d] * inv * (double)bf16_to_f32(w[d]);
+        if (rope) {
+          const int64_t s = row_ids[i] % rope_rows;
+          for (int p = 0; p < D / 2; ++p) {
+            const double c = rope[(s * (D / 2) + p) * 2], sn = rope[(s * (D / 2) + p) * 2 + 1];
+            const double a = head[2 * p], b = head[2 * p + 1];
+            head[2 * p] = a * c - b * sn;
+            head[2 * p + 1] = a * sn + b * c;
+          }
+        }
+        for (int d = 0; d < D; ++d) yo[c0 + d] = head[d];
+      }
+    }
+    if (y_bf16)
+      for (int64_t n = 0; n < N; ++n) y_bf16[i * N + n] = f64_to_bf16(yo[n]);
+  }
+}
+
 }  // extern "C"
