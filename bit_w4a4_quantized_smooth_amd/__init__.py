@@ -25,8 +25,8 @@ GROUP = {SVDQ_INT4: 64, SVDQ_NVFP4: 16}
 _STATUS = {0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARG", 2: "SVDQ_ERR_UNSUPPORTED",
            3: "SVDQ_ERR_ALIGNMENT", 4: "SVDQ_ERR_DEVICE"}
 
-EXPORTS = ["svdq_quantize_act", "svdq_w4a4_gemm", "awq_w4a16_gemv", "svdq_w4a4_group_psums",
-           "svdq_last_error", "svdq_abi_version", "svdq_test_set_arch_override"]
+EXPORTS = ["svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_qkv_norm_rope", "awq_w4a16_gemv",
+           "svdq_w4a4_group_psums", "svdq_last_error", "svdq_abi_version", "svdq_test_set_arch_override"]
 
 
 class SvdqError(RuntimeError):
@@ -50,9 +50,12 @@ def lib() -> ctypes.CDLL:
         L.svdq_quantize_act.argtypes = [i32, i32, i32, i64, i64, vp, vp, vp, f32, vp, vp, vp, vp]
         L.svdq_w4a4_gemm.argtypes = [i32, i32, i32, i64, i64, i64, vp, vp, f32, vp, vp, f32, vp, vp,
                                      vp, vp, vp]
+        L.svdq_w4a4_gemm_qkv_norm_rope.argtypes = [i32, i32, i32, i64, i32, i32, i64, vp, vp, f32, vp, vp,
+                                                   f32, vp, vp, vp, vp, vp, f32, vp, i64, vp, vp]
         L.awq_w4a16_gemv.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.svdq_w4a4_group_psums.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp]
-        for f in ("svdq_quantize_act", "svdq_w4a4_gemm", "awq_w4a16_gemv", "svdq_w4a4_group_psums"):
+        for f in ("svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_qkv_norm_rope", "awq_w4a16_gemv",
+                  "svdq_w4a4_group_psums"):
             getattr(L, f).restype = i32
         L.svdq_last_error.restype = ctypes.c_char_p
         L.svdq_abi_version.restype = i32
@@ -117,6 +120,26 @@ def w4a4_gemm(precision: int, act_codes, act_scales, w_codes, w_scales, xl1=None
                                 float(act_global_scale), _ptr(w_codes), _ptr(w_scales),
                                 float(w_global_scale), _ptr(xl1), _ptr(l2t), _ptr(bias), _ptr(y),
                                 _stream(stream)))
+    return y
+
+
+def w4a4_gemm_qkv_norm_rope(precision: int, act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias,
+                            heads: int, head_dim: int, norm_q, norm_k, eps: float, rope=None,
+                            act_global_scale: float = 1.0, w_global_scale: float = 1.0, out=None,
+                            stream=None):
+    """svdq_w4a4_gemm_qkv_norm_rope: the fused attention projection.  w_codes holds the Q, K
+    and V weights concatenated along N (= 3 * heads * head_dim); rope is fp32
+    [S, head_dim/2, 2] (cos, sin) or None.  Returns Y bf16 [M, N]."""
+    M, K = act_codes.shape[0], act_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    G = GROUP.get(precision, 64)
+    r = 0 if l2t is None else l2t.shape[1]
+    rope_rows = 0 if rope is None else rope.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=act_codes.device)
+    _check(lib().svdq_w4a4_gemm_qkv_norm_rope(
+        precision, G, r, M, heads, head_dim, K, _ptr(act_codes), _ptr(act_scales), float(act_global_scale),
+        _ptr(w_codes), _ptr(w_scales), float(w_global_scale), _ptr(xl1), _ptr(l2t), _ptr(bias), _ptr(norm_q),
+        _ptr(norm_k), float(eps), _ptr(rope), rope_rows, _ptr(y), _stream(stream)))
     return y
 
 

@@ -40,6 +40,7 @@
 //   activation and weight panels in that XCD's L2.
 #include "common.h"
 #include "launch.h"
+#include "qkv_epi.h"
 
 namespace svdq {
 
@@ -95,12 +96,14 @@ __device__ __forceinline__ uint4 nib_hi16(uint4 v) {  // 16*q of odd channels
 
 }  // namespace
 
-template <int MODE>  // 0: Y = bf16 linear output; 1: int32 partial products
+// MODE 0: Y = bf16 linear output; 1: int32 partial products; 2: Y of the fused
+// attention projection (Q/K RMSNorm and rotary embedding in the epilogue)
+template <int MODE>
 __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
     int M, int N, int K, int rank, const uint8_t* __restrict__ ac, const uint16_t* __restrict__ as,
     const uint8_t* __restrict__ wc, const uint16_t* __restrict__ ws, const float* __restrict__ xl1,
     const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-    int32_t* __restrict__ psums) {
+    int32_t* __restrict__ psums, QkvEpi qe) {
   extern __shared__ __align__(16) uint8_t smem[];
   float* ssc = (float*)(smem + 2 * STAGE);  // [2][KG][NROWS] fp32 scales
 
@@ -129,8 +132,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
   // Buffer resources: reads past the last row return zeros (the M and N tails).
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wc, (short)0, N * rowb, kBufDword3);
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)ac, (short)0, M * rowb, kBufDword3);
-  const __amdgpu_buffer_rsrc_t wsres = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, MODE == 0 ? N * G * 2 : 0, kBufDword3);
-  const __amdgpu_buffer_rsrc_t asres = __builtin_amdgcn_make_buffer_rsrc((void*)as, (short)0, MODE == 0 ? M * G * 2 : 0, kBufDword3);
+  const __amdgpu_buffer_rsrc_t wsres = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, MODE != 1 ? N * G * 2 : 0, kBufDword3);
+  const __amdgpu_buffer_rsrc_t asres = __builtin_amdgcn_make_buffer_rsrc((void*)as, (short)0, MODE != 1 ? M * G * 2 : 0, kBufDword3);
 
   // staging: chunk c = tid + NT*r -> (row c / PARTS, 16-byte part c % PARTS);
   // rows [0, BN) are weight rows n0+row, rows [BN, NROWS) activation rows.
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
 #pragma unroll
     for (int r = 0; r < CHUNKS; ++r)
       rc[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r < WCH ? wres : xres, coff[r] + kbyte, 0, 0));
-    if constexpr (MODE == 0) {
+    if constexpr (MODE != 1) {
 #pragma unroll
       for (int r = 0; r < SROWS; ++r) {
 #pragma unroll
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
       *(uint4*)dst = nib_lo16(rc[r]);
       *(uint4*)(dst + 16) = nib_hi16(rc[r]);
     }
-    if constexpr (MODE == 0) {
+    if constexpr (MODE != 1) {
 #pragma unroll
       for (int r = 0; r < SROWS; ++r) {
         const int row = tid + NT * r;
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
     for (int j = 0; j < BJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   v4i cinit;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) cinit[v] = MODE == 0 ? kMagicBits : 0;
+  for (int v = 0; v < 4; ++v) cinit[v] = MODE != 1 ? kMagicBits : 0;
   const v16f zero16 = {};
 
   // Pipeline buffers: the 2x2 quads of 16x16 blocks alternate between two
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
     __syncthreads();
   }
 
-  if constexpr (MODE == 0) {
+  if constexpr (MODE != 1) {
     {  // retire the last quad of the last group
       constexpr int Qp = NQ - 1;
       constexpr int pi = Qp / (BJ / 2), pj = Qp % (BJ / 2);
@@ -431,10 +434,78 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bl[j], acc[i][j], 0, 0, 0);
     }
 
-    // bias, bf16 rounding, then the wave's tile goes through LDS (free after
-    // the main loop) so that each store instruction writes whole 128-byte row
-    // segments of Y: lane l of a store covers row l/8, bytes 16*(l%8) .. +16.
-    constexpr int TROW = BI * 16 * 2 + 16;  // bytes per LDS row of the wave tile (+ pad)
+    constexpr int TROW = BI * 16 * 2 + 16;  // bytes per LDS row of a wave's output tile (+ pad)
+    if constexpr (MODE == 2) {
+      // Fused attention projection.  The bias joins the projection before the
+      // norm; then every Q and K head is normalized per token and rotated, V
+      // passes.  This lane holds columns 16i + 4lg .. +3 of the wave's 64 for
+      // tokens 16j + l16, so rotary pairs stay in the lane.  The part (Q, K
+      // or V) is the same for the whole workgroup: heads * head_dim is a
+      // multiple of the 128-column tile.
+      static_assert(WAVES_N == 2 && BI * 16 == 64, "a 128-channel head spans the two column waves");
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const float b[4] = {bf16_bits_to_f32(bb[i].x & 0xFFFFu), bf16_bits_to_f32(bb[i].x >> 16),
+                            bf16_bits_to_f32(bb[i].y & 0xFFFFu), bf16_bits_to_f32(bb[i].y >> 16)};
+#pragma unroll
+        for (int j = 0; j < BJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][j][v] += b[v];
+      }
+      const int nw = n0 + wn;
+      const int part = qkv_part(nw, qe);
+      if (part < 2) {
+        const uint16_t* wnorm = part == 0 ? qe.norm_q : qe.norm_k;
+        const int c0 = qkv_channel(nw, qe);  // 0, or 64 in the second half of a 128-channel head
+        uint2 wv[BI];
+        float4 cs[BI][BJ];
+#pragma unroll
+        for (int i = 0; i < BI; ++i) wv[i] = *(const uint2*)(wnorm + c0 + 16 * i + 4 * lg);
+#pragma unroll
+        for (int j = 0; j < BJ; ++j) {
+          const int row = qe.rope ? (m0 + wm + 16 * j + l16) % qe.rope_rows : 0;
+#pragma unroll
+          for (int i = 0; i < BI; ++i)
+            cs[i][j] = qe.rope ? *(const float4*)(qe.rope + (size_t)row * qe.head_dim + c0 + 16 * i + 4 * lg)
+                               : float4{1.0f, 0.0f, 1.0f, 0.0f};
+        }
+        float ss[BJ];
+#pragma unroll
+        for (int j = 0; j < BJ; ++j) {
+          float t = 0.0f;
+#pragma unroll
+          for (int i = 0; i < BI; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) t = fmaf(acc[i][j][v], acc[i][j][v], t);
+          ss[j] = sum_over_rows16(t);  // the wave's 64 columns
+        }
+        if (qe.head_dim == 128) {  // the head's other 64 columns are the partner wave's (wn ^ 64)
+          float* red = (float*)(smem + (NT / 64) * (BJ * 16) * TROW);  // past the output tiles
+          if (lg == 0) {
+#pragma unroll
+            for (int j = 0; j < BJ; ++j) red[wave * 64 + 16 * j + l16] = ss[j];
+          }
+          __syncthreads();
+#pragma unroll
+          for (int j = 0; j < BJ; ++j) ss[j] += red[(wave ^ WAVES_M) * 64 + 16 * j + l16];
+        }
+#pragma unroll
+        for (int j = 0; j < BJ; ++j) {
+          const float r = inv_rms(ss[j], qe);
+#pragma unroll
+          for (int i = 0; i < BI; ++i) {
+            const float4 o = norm_rope4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3], r, wv[i], cs[i][j]);
+            acc[i][j] = v4f{o.x, o.y, o.z, o.w};
+          }
+        }
+      }
+    }
+
+    // bias (MODE 0), bf16 rounding, then the wave's tile goes through LDS
+    // (free after the main loop) so that each store instruction writes whole
+    // 128-byte row segments of Y: lane l of a store covers row l/8, bytes
+    // 16*(l%8) .. +16.
+    static_assert((NT / 64) * (BJ * 16) * TROW + NT * 4 <= LDS_BYTES, "output tiles and norm sums fit in LDS");
     uint8_t* tile = smem + wave * (BJ * 16) * TROW;
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
@@ -443,8 +514,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
 #pragma unroll
       for (int j = 0; j < BJ; ++j) {
         uint2 o;
-        o.x = f32_to_bf16_bits(acc[i][j][0] + b0) | (f32_to_bf16_bits(acc[i][j][1] + b1) << 16);
-        o.y = f32_to_bf16_bits(acc[i][j][2] + b2) | (f32_to_bf16_bits(acc[i][j][3] + b3) << 16);
+        if constexpr (MODE == 2) {  // bias already in
+          o.x = f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16);
+          o.y = f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16);
+        } else {
+          o.x = f32_to_bf16_bits(acc[i][j][0] + b0) | (f32_to_bf16_bits(acc[i][j][1] + b1) << 16);
+          o.y = f32_to_bf16_bits(acc[i][j][2] + b2) | (f32_to_bf16_bits(acc[i][j][3] + b3) << 16);
+        }
         *(uint2*)(tile + (16 * j + l16) * TROW + (16 * i + 4 * lg) * 2) = o;
       }
     }
@@ -467,18 +543,25 @@ hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
   const int blocks = m_tiles * (int)((a.N + BN - 1) / BN);
   auto k0 = gemm_int4_kernel<0>;
   auto k1 = gemm_int4_kernel<1>;
-  hipError_t e = hipFuncSetAttribute((const void*)(a.psums ? k1 : k0),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+  auto k2 = gemm_int4_kernel<2>;
+  const void* kf = a.psums ? (const void*)k1 : a.qkv ? (const void*)k2 : (const void*)k0;
+  hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
   if (e != hipSuccess) return e;
+  const QkvEpi none{};
   if (a.psums) {
     hipLaunchKernelGGL(k1, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, 0,
                        (const uint8_t*)a.act_codes, nullptr, (const uint8_t*)a.w_codes, nullptr, nullptr,
-                       nullptr, nullptr, nullptr, (int32_t*)a.psums);
+                       nullptr, nullptr, nullptr, (int32_t*)a.psums, none);
+  } else if (a.qkv) {
+    hipLaunchKernelGGL(k2, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
+                       (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
+                       (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
+                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, *a.qkv);
   } else {
     hipLaunchKernelGGL(k0, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
                        (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
                        (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
-                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr);
+                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, none);
   }
   return hipGetLastError();
 }

@@ -26,6 +26,7 @@
 // so that each XCD works on a contiguous part of a banded order.
 #include "common.h"
 #include "launch.h"
+#include "qkv_epi.h"
 
 namespace svdq {
 
@@ -56,12 +57,14 @@ __device__ __forceinline__ void scale_pairs(u32 bits, h2& s0, h2& s1) {
 }
 }  // namespace
 
-template <int MODE>  // 0: Y; 1: fp32 partial products per 16-channel group
+// MODE 0: Y; 1: fp32 partial products per 16-channel group; 2: Y of the fused
+// attention projection (Q/K RMSNorm and rotary embedding in the epilogue)
+template <int MODE>
 __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
     int M, int N, int K, int rank, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
     float alpha, const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
     const float* __restrict__ xl1, const uint16_t* __restrict__ l2t,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, float* __restrict__ psums) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, float* __restrict__ psums, QkvEpi qe) {
   __shared__ __align__(16) uint16_t sW[2][BN * ROW];
   __shared__ __align__(16) uint16_t sX[2][BM * ROW];
 
@@ -84,8 +87,8 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   const int srow = tid >> 1, shalf = tid & 1;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wc, (short)0, N * rowb, kBufDword3);
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)ac, (short)0, M * rowb, kBufDword3);
-  const __amdgpu_buffer_rsrc_t wsres = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, MODE == 0 ? N * G : 0, kBufDword3);
-  const __amdgpu_buffer_rsrc_t asres = __builtin_amdgcn_make_buffer_rsrc((void*)as, (short)0, MODE == 0 ? M * G : 0, kBufDword3);
+  const __amdgpu_buffer_rsrc_t wsres = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, MODE != 1 ? N * G : 0, kBufDword3);
+  const __amdgpu_buffer_rsrc_t asres = __builtin_amdgcn_make_buffer_rsrc((void*)as, (short)0, MODE != 1 ? M * G : 0, kBufDword3);
   const int woff = (n0 + srow) * rowb + shalf * 16, xoff = (m0 + srow) * rowb + shalf * 16;  // rows past M: zeros
   const int wsoff = (n0 + srow) * G + 2 * shalf, xsoff = (m0 + srow) * G + 2 * shalf;
 
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   auto gload = [&](int st) {
     wv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, woff + st * 32, 0, 0));
     xv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff + st * 32, 0, 0));
-    if constexpr (MODE == 0) {
+    if constexpr (MODE != 1) {
       wsb = __builtin_amdgcn_raw_buffer_load_b16(wsres, wsoff + st * 4, 0, 0);
       xsb = __builtin_amdgcn_raw_buffer_load_b16(asres, xsoff + st * 4, 0, 0);
     }
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
     __syncthreads();
   }
 
-  if constexpr (MODE == 0) {
+  if constexpr (MODE != 1) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -197,6 +200,86 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bl[j], acc[i][j], 0, 0, 0);
     }
+    if constexpr (MODE == 2) {
+      // Fused attention projection (see gemm_int4.hip): bias first, then
+      // per-token RMSNorm and rotary embedding of every Q and K head.  This
+      // lane holds columns 32i + 8q + 4lh .. +3 of the wave's 64 for tokens
+      // 32j + lr; the workgroup's 128 columns lie in one part (Q, K or V).
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn + 32 * i + 8 * q + 4 * lh;
+          float b[4] = {0.f, 0.f, 0.f, 0.f};
+          if (bias) {
+            const uint2 bb = *(const uint2*)(bias + n);
+            b[0] = bf16_bits_to_f32(bb.x & 0xFFFFu);
+            b[1] = bf16_bits_to_f32(bb.x >> 16);
+            b[2] = bf16_bits_to_f32(bb.y & 0xFFFFu);
+            b[3] = bf16_bits_to_f32(bb.y >> 16);
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][j][4 * q + v] += b[v];
+        }
+      const int part = qkv_part(n0 + wn, qe);
+      if (part < 2) {
+        const uint16_t* wnorm = part == 0 ? qe.norm_q : qe.norm_k;
+        const int c0 = qkv_channel(n0 + wn, qe);
+        uint2 wv[2][4];
+        float4 cs[2][2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) wv[i][q] = *(const uint2*)(wnorm + c0 + 32 * i + 8 * q + 4 * lh);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int row = qe.rope ? (m0 + wm + 32 * j + lr) % qe.rope_rows : 0;
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              cs[i][j][q] = qe.rope ? *(const float4*)(qe.rope + (size_t)row * qe.head_dim + c0 + 32 * i + 8 * q + 4 * lh)
+                                    : float4{1.0f, 0.0f, 1.0f, 0.0f};
+        }
+        float ss[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float t = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) t = fmaf(acc[i][j][v], acc[i][j][v], t);
+          ss[j] = sum_over_halves(t);  // the wave's 64 columns
+        }
+        if (qe.head_dim == 128) {  // the other 64 columns of the head: partner wave (wn ^ 64)
+          float* red = (float*)&sW[0][0];  // free after the main loop
+          if (lh == 0) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) red[wave * 64 + 32 * j + lr] = ss[j];
+          }
+          __syncthreads();
+#pragma unroll
+          for (int j = 0; j < 2; ++j) ss[j] += red[(wave ^ 2) * 64 + 32 * j + lr];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float r = inv_rms(ss[j], qe);
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 o = norm_rope4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                          acc[i][j][4 * q + 3], r, wv[i][q], cs[i][j][q]);
+              acc[i][j][4 * q] = o.x;
+              acc[i][j][4 * q + 1] = o.y;
+              acc[i][j][4 * q + 2] = o.z;
+              acc[i][j][4 * q + 3] = o.w;
+            }
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -207,7 +290,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
         for (int q = 0; q < 4; ++q) {
           const int n = n0 + wn + 32 * i + 8 * q + 4 * lh;
           float bv[4] = {0.f, 0.f, 0.f, 0.f};
-          if (bias) {
+          if (MODE == 0 && bias) {
             const uint2 bb = *(const uint2*)(bias + n);
             bv[0] = bf16_bits_to_f32(bb.x & 0xFFFFu);
             bv[1] = bf16_bits_to_f32(bb.x >> 16);
@@ -226,16 +309,23 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
 hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st) {
   const int m_tiles = (int)((a.M + BM - 1) / BM);
   const int blocks = m_tiles * (int)(a.N / BN);  // N % 128 == 0
+  const QkvEpi none{};
   if (a.psums) {
     hipLaunchKernelGGL(gemm_nvfp4_kernel<1>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
                        (int)a.K, 0, (const uint8_t*)a.act_codes, nullptr, 1.0f,
                        (const uint8_t*)a.w_codes, nullptr, nullptr, nullptr, nullptr, nullptr,
-                       (float*)a.psums);
+                       (float*)a.psums, none);
+  } else if (a.qkv) {
+    hipLaunchKernelGGL(gemm_nvfp4_kernel<2>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
+                       (int)a.K, a.rank, (const uint8_t*)a.act_codes, (const uint8_t*)a.act_scales,
+                       a.alpha_a * a.alpha_w, (const uint8_t*)a.w_codes, (const uint8_t*)a.w_scales,
+                       a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr,
+                       *a.qkv);
   } else {
     hipLaunchKernelGGL(gemm_nvfp4_kernel<0>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
                        (int)a.K, a.rank, (const uint8_t*)a.act_codes, (const uint8_t*)a.act_scales,
                        a.alpha_a * a.alpha_w, (const uint8_t*)a.w_codes, (const uint8_t*)a.w_scales,
-                       a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr);
+                       a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, none);
   }
   return hipGetLastError();
 }

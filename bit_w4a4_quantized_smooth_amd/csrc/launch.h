@@ -19,6 +19,19 @@ struct QuantArgs {
   float* xl1;
 };
 
+// Epilogue of the fused attention projection: columns [Q | K | V], each hd =
+// heads * head_dim wide; Q and K heads get RMSNorm (weights norm_q / norm_k,
+// epsilon eps) and then the rotary embedding from rope [rope_rows, head_dim/2, 2]
+// (cos, sin) pairs, token row m using table row m % rope_rows (rope may be null).
+struct QkvEpi {
+  int hd, head_dim;
+  const uint16_t* norm_q;
+  const uint16_t* norm_k;
+  float eps;
+  const float* rope;
+  int rope_rows;
+};
+
 struct GemmArgs {
   int precision, rank;
   int64_t M, N, K;
@@ -33,6 +46,7 @@ struct GemmArgs {
   const void* bias;
   void* y;       // bf16 [M, N] (GEMM) ...
   void* psums;   // ... or [M, N, K/G] partial products (test support)
+  const QkvEpi* qkv;  // non-null: Y with the Q/K norm and rotary epilogue
 };
 
 struct AwqArgs {

@@ -164,11 +164,14 @@ static svdq_status gemm_common(int precision, int group_size, int rank, int64_t 
   return SVDQ_OK;
 }
 
-svdq_status svdq_w4a4_gemm(int precision, int group_size, int rank, int64_t M, int64_t N,
-                           int64_t K, const void* act_codes, const void* act_scales,
-                           float act_global_scale, const void* w_codes, const void* w_scales,
-                           float w_global_scale, const float* xl1, const void* l2t,
-                           const void* bias, void* y, void* stream) {
+// Checks shared by the two Y-producing GEMM entry points; qkv (may be NULL)
+// is the attention-projection epilogue.
+static svdq_status gemm_y(int precision, int group_size, int rank, int64_t M, int64_t N,
+                          int64_t K, const void* act_codes, const void* act_scales,
+                          float act_global_scale, const void* w_codes, const void* w_scales,
+                          float w_global_scale, const float* xl1, const void* l2t,
+                          const void* bias, void* y, void* stream, const svdq::QkvEpi* qkv,
+                          size_t rope_bytes) {
   svdq_status s;
   if ((s = gemm_common(precision, group_size, rank, M, N, K, act_codes, w_codes)) != SVDQ_OK) return s;
   if (M == 0) return ok();  // empty call: nothing to read or write
@@ -189,13 +192,55 @@ svdq_status svdq_w4a4_gemm(int precision, int group_size, int rank, int64_t M, i
       overlaps(y, ny, xl1, (size_t)M * rank * 4) || overlaps(y, ny, l2t, (size_t)N * rank * 2) ||
       overlaps(y, ny, bias, (size_t)N * 2))
     return fail(SVDQ_ERR_INVALID_ARG, "y must not overlap an input");
+  if (qkv) {
+    const size_t nw = (size_t)qkv->head_dim * 2;
+    if (!aligned16(qkv->norm_q) || !aligned16(qkv->norm_k) || !aligned16(qkv->rope))
+      return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
+    if (overlaps(y, ny, qkv->norm_q, nw) || overlaps(y, ny, qkv->norm_k, nw) ||
+        overlaps(y, ny, qkv->rope, rope_bytes))
+      return fail(SVDQ_ERR_INVALID_ARG, "y must not overlap an input");
+  }
   if ((s = check_arch()) != SVDQ_OK) return s;
   if (M == 0) return ok();
   if ((s = check_sticky()) != SVDQ_OK) return s;
   svdq::GemmArgs a{precision, rank, M, N, K, act_codes, act_scales, act_global_scale, w_codes,
-                   w_scales, w_global_scale, xl1, l2t, bias, y, nullptr};
+                   w_scales, w_global_scale, xl1, l2t, bias, y, nullptr, qkv};
   return launched(precision == SVDQ_INT4 ? svdq::launch_gemm_int4(a, (hipStream_t)stream)
                                          : svdq::launch_gemm_nvfp4(a, (hipStream_t)stream));
+}
+
+svdq_status svdq_w4a4_gemm(int precision, int group_size, int rank, int64_t M, int64_t N,
+                           int64_t K, const void* act_codes, const void* act_scales,
+                           float act_global_scale, const void* w_codes, const void* w_scales,
+                           float w_global_scale, const float* xl1, const void* l2t,
+                           const void* bias, void* y, void* stream) {
+  return gemm_y(precision, group_size, rank, M, N, K, act_codes, act_scales, act_global_scale, w_codes,
+                w_scales, w_global_scale, xl1, l2t, bias, y, stream, nullptr, 0);
+}
+
+svdq_status svdq_w4a4_gemm_qkv_norm_rope(int precision, int group_size, int rank, int64_t M,
+                                         int heads, int head_dim, int64_t K, const void* act_codes,
+                                         const void* act_scales, float act_global_scale,
+                                         const void* w_codes, const void* w_scales,
+                                         float w_global_scale, const float* xl1, const void* l2t,
+                                         const void* bias, const void* norm_q, const void* norm_k,
+                                         float eps, const float* rope, int64_t rope_rows, void* y,
+                                         void* stream) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SVDQ_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+  if (heads <= 0 || heads > (1 << 20)) return fail(SVDQ_ERR_INVALID_ARG, "bad head count %d", heads);
+  const int64_t N = 3 * (int64_t)heads * head_dim;
+  if (N % 128 != 0)
+    return fail(SVDQ_ERR_UNSUPPORTED, "3 * heads * head_dim = %lld must be a multiple of 128", (long long)N);
+  if (!(eps >= 0.0f && eps < 3.0e38f)) return fail(SVDQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (rope && (rope_rows <= 0 || rope_rows > kMaxDim))
+    return fail(SVDQ_ERR_INVALID_ARG, "rope_rows must be >= 1 when rope is given");
+  if (M > 0 && (!norm_q || !norm_k)) return fail(SVDQ_ERR_INVALID_ARG, "norm_q and norm_k are required");
+  const svdq::QkvEpi q{(int)(heads * head_dim), head_dim, (const uint16_t*)norm_q, (const uint16_t*)norm_k,
+                       eps, rope, rope ? (int)rope_rows : 1};
+  const size_t rope_bytes = rope ? (size_t)rope_rows * head_dim * 4 : 0;
+  return gemm_y(precision, group_size, rank, M, N, K, act_codes, act_scales, act_global_scale, w_codes,
+                w_scales, w_global_scale, xl1, l2t, bias, y, stream, &q, rope_bytes);
 }
 
 svdq_status svdq_w4a4_group_psums(int precision, int group_size, int64_t M, int64_t N, int64_t K,
@@ -214,7 +259,7 @@ svdq_status svdq_w4a4_group_psums(int precision, int group_size, int64_t M, int6
   if (M == 0) return ok();
   if ((s = check_sticky()) != SVDQ_OK) return s;
   svdq::GemmArgs a{precision, 0, M, N, K, act_codes, nullptr, 1.0f, w_codes, nullptr, 1.0f,
-                   nullptr, nullptr, nullptr, nullptr, psums};
+                   nullptr, nullptr, nullptr, nullptr, psums, nullptr};
   return launched(precision == SVDQ_INT4 ? svdq::launch_gemm_int4(a, (hipStream_t)stream)
                                          : svdq::launch_gemm_nvfp4(a, (hipStream_t)stream));
 }

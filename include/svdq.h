@@ -115,6 +115,42 @@ svdq_status svdq_w4a4_gemm(int precision, int group_size, int rank, int64_t M, i
                            const void* bias, void* y, void* stream);
 
 /*
+ * svdq_w4a4_gemm_qkv_norm_rope -- the fused attention projection: the 4-bit
+ * GEMM of the grouped Q/K/V weights with the per-head RMSNorm of Q and K and
+ * the rotary embedding applied to its fp32 result inside the epilogue, so Y
+ * is written once ("Nunchaku Lite", "Fused kernels"; blog, "Quantizing models
+ * with structural rewrites": Q, K and V weights concatenated along the output
+ * dimension in that order, one operator for projection, norms and rotary
+ * embedding):
+ *   y   = the svdq_w4a4_gemm result (bias included) before rounding, with
+ *         columns [Q | K | V], each heads * head_dim wide, head h of Q at
+ *         columns h*head_dim .. +head_dim-1 (K likewise after Q)
+ *   for every token m and every head of Q (weights w = norm_q) and of K (norm_k):
+ *     u_d = y_d * w_d / sqrt(mean_d(y_d^2) + eps)            d = 0 .. head_dim-1
+ *     (u_2p, u_2p+1) <- (u_2p*c - u_2p+1*s, u_2p*s + u_2p+1*c),
+ *     (c, s) = rope[m mod rope_rows][p]
+ *   V columns are y unchanged; Y = bf16 of the result.
+ *
+ *   heads, head_dim   head_dim 64 or 128; N = 3 * heads * head_dim must be a
+ *                     multiple of 128 (N is implied, not passed)
+ *   norm_q, norm_k    bf16 [head_dim]; required when M > 0
+ *   eps               finite, >= 0
+ *   rope              fp32 [rope_rows, head_dim/2, 2] (cos, sin) pairs, or NULL
+ *                     for no rotary embedding; token rows are batch-major, so
+ *                     rope_rows is the sequence length (>= 1 when rope is given)
+ *   y                 out bf16 [M, N]; must not overlap any input
+ *   other arguments and limits as for svdq_w4a4_gemm.
+ */
+svdq_status svdq_w4a4_gemm_qkv_norm_rope(int precision, int group_size, int rank, int64_t M,
+                                         int heads, int head_dim, int64_t K, const void* act_codes,
+                                         const void* act_scales, float act_global_scale,
+                                         const void* w_codes, const void* w_scales,
+                                         float w_global_scale, const float* xl1, const void* l2t,
+                                         const void* bias, const void* norm_q, const void* norm_k,
+                                         float eps, const float* rope, int64_t rope_rows, void* y,
+                                         void* stream);
+
+/*
  * awq_w4a16_gemv -- AWQ-style int4 weight-only linear for memory-bound
  * modulation projections ("Supported quantization types": awq_w4a16, int4,
  * group 64; blog, "Introducing Nunchaku Lite"):

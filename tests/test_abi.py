@@ -130,3 +130,33 @@ def test_python_binding_raises_loudly(L):
     with pytest.raises(sq.SvdqError) as e:
         sq._check(q(L))
     assert e.value.status == UNSUPPORTED
+
+
+def qkv(L, prec=0, G=64, r=16, M=256, H=24, D=128, K=512, ac=A, as_=2 * A, aa=1.0, wc=3 * A, ws=4 * A,
+        aw=1.0, xl1=5 * A, l2t=6 * A, bias=7 * A, nq=9 * A, nk=10 * A, eps=1e-6, rope=11 * A, rope_rows=256,
+        y=12 * A):
+    return L.svdq_w4a4_gemm_qkv_norm_rope(prec, G, r, M, H, D, K, ac, as_, aa, wc, ws, aw, xl1, l2t, bias,
+                                          nq, nk, eps, rope, rope_rows, y, None)
+
+
+def test_qkv_entry_point_validation(L):
+    assert qkv(L) == UNSUPPORTED                      # valid: reaches the arch check
+    assert qkv(L, prec=1, G=16) == UNSUPPORTED
+    assert qkv(L, rope=None, rope_rows=0) == UNSUPPORTED  # the rotary table is optional
+    assert qkv(L, bias=None) == UNSUPPORTED
+    assert qkv(L, D=96) == UNSUPPORTED                # head_dim 64 or 128
+    assert qkv(L, D=64, H=1) == UNSUPPORTED           # N = 192 is not a multiple of 128
+    assert qkv(L, D=64, H=2) == UNSUPPORTED           # N = 384: valid
+    assert qkv(L, H=0) == INVALID
+    assert qkv(L, eps=-1e-6) == INVALID
+    assert qkv(L, eps=float("nan")) == INVALID
+    assert qkv(L, rope_rows=0) == INVALID
+    assert qkv(L, nq=None) == INVALID
+    assert qkv(L, nk=None) == INVALID
+    assert qkv(L, y=None) == INVALID
+    assert qkv(L, rope=11 * A + 4) == ALIGN
+    assert qkv(L, nk=10 * A + 2) == ALIGN
+    assert qkv(L, y=11 * A) == INVALID                # y aliases the rotary table
+    assert qkv(L, y=9 * A) == INVALID                 # y aliases norm_q
+    L.svdq_test_set_arch_override(b"gfx950")
+    assert qkv(L, M=0) == OK
