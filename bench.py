@@ -298,6 +298,49 @@ def extras(args, torch, sq, synth, t, bf, f16, stream):
     linear("mlp_down_int4_4608x3072x12288", 1003, 4608, 3072, 12288, sq.SVDQ_INT4, 0.0, 1.0, "gelu")
     linear("qkv_nvfp4_4608x9216x3072", 1004, 4608, 9216, 3072, sq.SVDQ_NVFP4, 0.005, 30.0)
 
+    # fused attention projection (QKV GEMM + per-head RMSNorm + rotary epilogue)
+    # against the same GEMM followed by the norm and rotary steps as separate
+    # torch kernels on the bf16 output
+    for name, seed, prec in (("qkv_fused_int4_4608x9216x3072_h24d128", 1002, sq.SVDQ_INT4),
+                             ("qkv_fused_nvfp4_4608x9216x3072_h24d128", 1004, sq.SVDQ_NVFP4)):
+        M, H, D, K = 4608, 24, 128, 3072
+        HD, N = H * D, 3 * H * D
+        d = synth.qkv_layer(seed, M, H, D, K, 32, prec, 0.005, 30.0)
+        G = 64 if prec == sq.SVDQ_INT4 else 16
+        x, lam, l1t = bf(d["x"]), bf(d["lam"]), bf(d["l1t"])
+        wc = t(d["w_codes"])
+        ws = f16(d["w_scales"]) if prec == sq.SVDQ_INT4 else t(d["w_scales"])
+        l2t, bias = bf(d["l2t"]), bf(d["bias"])
+        nq, nk, rope = bf(d["norm_q"]), bf(d["norm_k"]), t(d["rope"])
+        aa, aw, eps = float(d["alpha_a"]), float(d["alpha_w"]), float(d["eps"])
+        codes, scales, xl1 = sq.quantize_act(prec, x, lam, l1t, aa, stream=stream)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        fused_ms = median_ms(lambda i: sq.w4a4_gemm_qkv_norm_rope(
+            prec, codes, scales, wc, ws, xl1, l2t, bias, H, D, nq, nk, eps, rope, aa, aw, out=y, stream=stream),
+            n, stream, torch)
+        plain_ms = median_ms(lambda i: sq.w4a4_gemm(prec, codes, scales, wc, ws, xl1, l2t, bias, aa, aw, out=y,
+                                                    stream=stream), n, stream, torch)
+        cos, sin = rope[:, :, 0].unsqueeze(1), rope[:, :, 1].unsqueeze(1)
+
+        def norm_rope(part, w):
+            h = y[:, part * HD:(part + 1) * HD].view(M, H, D).float()
+            h = h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + eps) * w.float()
+            a, b = h[..., 0::2], h[..., 1::2]
+            y[:, part * HD:(part + 1) * HD] = torch.stack([a * cos - b * sin, a * sin + b * cos], -1).view(M, HD).to(
+                torch.bfloat16)
+
+        def unfused(i):
+            sq.w4a4_gemm(prec, codes, scales, wc, ws, xl1, l2t, bias, aa, aw, out=y, stream=stream)
+            norm_rope(0, nq)
+            norm_rope(1, nk)
+
+        unfused_ms = median_ms(unfused, n, stream, torch)
+        res[name] = {"fused_ms": round(fused_ms, 5), "plain_gemm_ms": round(plain_ms, 5),
+                     "unfused_torch_ms": round(unfused_ms, 5),
+                     "epilogue_overhead": round(fused_ms / plain_ms, 4),
+                     "speedup_vs_unfused": round(unfused_ms / fused_ms, 3)}
+        del x, lam, l1t, wc, ws, l2t, bias, nq, nk, rope, codes, scales, xl1, y
+
     # AWQ at M=64 over >= 512 MB of weight copies
     d = synth.awq_layer(1005, 64, 18432, 3072)
     A = max(1, args.awq_copies)

@@ -25,6 +25,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// Two fp32 -> packed bf16 pair (a in the low half) with the hardware
+// conversion v_cvt_pk_bf16_f32: round to nearest even, the same bits as
+// f32_to_bf16_bits for every finite input.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{a, b}), bf2_t));
+}
+
 // fp32 (finite, >= 0) -> fp16 bits, round-to-nearest-even, saturating at 65504.
 __device__ __forceinline__ uint32_t f32_to_f16_sat_bits(float f) {
   _Float16 h = (_Float16)fminf(f, 65504.0f);

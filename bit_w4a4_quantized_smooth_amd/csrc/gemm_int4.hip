@@ -343,6 +343,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
       const int n = n0 + wn + 16 * i + 4 * lg;
       bb[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(bres, n * 2, 0, 0));
     }
+    // Inputs of the attention-projection epilogue (MODE 2), issued early so
+    // that their latency overlaps the scale-sum and low-rank products: the
+    // norm weights of this lane's columns here, the rotary (cos, sin) pairs of
+    // its tokens once the scale-sum operands are dead (register budget of two
+    // workgroups per CU).  The part (Q, K or V) is the same for the whole
+    // workgroup, as heads * head_dim is a multiple of the 128-column tile.
+    const int qpart = MODE == 2 ? qkv_part(n0 + wn, qe) : 2;
+    const int qc0 = MODE == 2 ? qkv_channel(n0 + wn, qe) : 0;  // 0, or 64 in a 128-channel head's second half
+    uint2 wv[BI];
+    float4 cs[BI][BJ];
+    if (MODE == 2 && qpart < 2) {
+      const uint16_t* wnorm = qpart == 0 ? qe.norm_q : qe.norm_k;
+#pragma unroll
+      for (int i = 0; i < BI; ++i) wv[i] = *(const uint2*)(wnorm + qc0 + 16 * i + 4 * lg);
+    }
     // 8 fp16 scales of one row from group g0 (zeros past G and past the tensor)
     auto load8h = [&](__amdgpu_buffer_rsrc_t res, int row, int g0) -> v8h {
       if ((G & 7) == 0)  // rows of 8k groups: one 16-byte load
@@ -405,6 +420,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
       if (kb + 64 < G) load_ts(kb + 64, 0);
       if (kb + 96 < G) load_ts(kb + 96, 1);
     }
+    if (MODE == 2 && qpart < 2) {
+      int row[BJ];
+      rope_rows_of<BJ, 16>(m0 + wm + l16, qe, row);
+#pragma unroll
+      for (int j = 0; j < BJ; ++j)
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+          cs[i][j] = qe.rope ? *(const float4*)(qe.rope + (size_t)row[j] * qe.head_dim + qc0 + 16 * i + 4 * lg)
+                             : float4{1.0f, 0.0f, 1.0f, 0.0f};
+    }
 #pragma unroll
     for (int i = 0; i < BI; ++i)
 #pragma unroll
@@ -421,10 +446,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
       for (int j = 0; j < BJ; ++j) {
         const float4 f0 = xf[2 * j], f1 = xf[2 * j + 1];
         uint4 pk;
-        pk.x = f32_to_bf16_bits(f0.x) | (f32_to_bf16_bits(f0.y) << 16);
-        pk.y = f32_to_bf16_bits(f0.z) | (f32_to_bf16_bits(f0.w) << 16);
-        pk.z = f32_to_bf16_bits(f1.x) | (f32_to_bf16_bits(f1.y) << 16);
-        pk.w = f32_to_bf16_bits(f1.z) | (f32_to_bf16_bits(f1.w) << 16);
+        pk.x = pack_bf16x2(f0.x, f0.y);
+        pk.y = pack_bf16x2(f0.z, f0.w);
+        pk.z = pack_bf16x2(f1.x, f1.y);
+        pk.w = pack_bf16x2(f1.z, f1.w);
         bl[j] = __builtin_bit_cast(v8bf, pk);
       }
 #pragma unroll
@@ -439,9 +464,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
       // Fused attention projection.  The bias joins the projection before the
       // norm; then every Q and K head is normalized per token and rotated, V
       // passes.  This lane holds columns 16i + 4lg .. +3 of the wave's 64 for
-      // tokens 16j + l16, so rotary pairs stay in the lane.  The part (Q, K
-      // or V) is the same for the whole workgroup: heads * head_dim is a
-      // multiple of the 128-column tile.
+      // tokens 16j + l16, so rotary pairs stay in the lane.
       static_assert(WAVES_N == 2 && BI * 16 == 64, "a 128-channel head spans the two column waves");
 #pragma unroll
       for (int i = 0; i < BI; ++i) {
@@ -452,23 +475,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[i][j][v] += b[v];
       }
-      const int nw = n0 + wn;
-      const int part = qkv_part(nw, qe);
-      if (part < 2) {
-        const uint16_t* wnorm = part == 0 ? qe.norm_q : qe.norm_k;
-        const int c0 = qkv_channel(nw, qe);  // 0, or 64 in the second half of a 128-channel head
-        uint2 wv[BI];
-        float4 cs[BI][BJ];
-#pragma unroll
-        for (int i = 0; i < BI; ++i) wv[i] = *(const uint2*)(wnorm + c0 + 16 * i + 4 * lg);
-#pragma unroll
-        for (int j = 0; j < BJ; ++j) {
-          const int row = qe.rope ? (m0 + wm + 16 * j + l16) % qe.rope_rows : 0;
-#pragma unroll
-          for (int i = 0; i < BI; ++i)
-            cs[i][j] = qe.rope ? *(const float4*)(qe.rope + (size_t)row * qe.head_dim + c0 + 16 * i + 4 * lg)
-                               : float4{1.0f, 0.0f, 1.0f, 0.0f};
-        }
+      if (qpart < 2) {
         float ss[BJ];
 #pragma unroll
         for (int j = 0; j < BJ; ++j) {
@@ -515,11 +522,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
       for (int j = 0; j < BJ; ++j) {
         uint2 o;
         if constexpr (MODE == 2) {  // bias already in
-          o.x = f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16);
-          o.y = f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16);
+          o.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+          o.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
         } else {
-          o.x = f32_to_bf16_bits(acc[i][j][0] + b0) | (f32_to_bf16_bits(acc[i][j][1] + b1) << 16);
-          o.y = f32_to_bf16_bits(acc[i][j][2] + b2) | (f32_to_bf16_bits(acc[i][j][3] + b3) << 16);
+          o.x = pack_bf16x2(acc[i][j][0] + b0, acc[i][j][1] + b1);
+          o.y = pack_bf16x2(acc[i][j][2] + b2, acc[i][j][3] + b3);
         }
         *(uint2*)(tile + (16 * j + l16) * TROW + (16 * i + 4 * lg) * 2) = o;
       }

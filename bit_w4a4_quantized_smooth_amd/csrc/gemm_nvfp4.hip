@@ -169,6 +169,32 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   }
 
   if constexpr (MODE != 1) {
+    // Inputs of the attention-projection epilogue (MODE 2), issued first so
+    // that their latency overlaps the low-rank products: norm weights of this
+    // lane's columns and rotary (cos, sin) pairs of its tokens.  The part (Q,
+    // K or V) is the same for the whole workgroup (heads * head_dim is a
+    // multiple of the 128-column tile).
+    const int qpart = MODE == 2 ? qkv_part(n0 + wn, qe) : 2;
+    const int qc0 = MODE == 2 ? qkv_channel(n0 + wn, qe) : 0;
+    uint2 wv[2][4];
+    float4 cs[2][2][4];
+    if (MODE == 2 && qpart < 2) {
+      const uint16_t* wnorm = qpart == 0 ? qe.norm_q : qe.norm_k;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wv[i][q] = *(const uint2*)(wnorm + qc0 + 32 * i + 8 * q + 4 * lh);
+      int row[2];
+      rope_rows_of<2, 32>(m0 + wm + lr, qe, row);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            cs[i][j][q] = qe.rope ? *(const float4*)(qe.rope + (size_t)row[j] * qe.head_dim + qc0 + 32 * i + 8 * q + 4 * lh)
+                                  : float4{1.0f, 0.0f, 1.0f, 0.0f};
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -187,10 +213,10 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
         if (m < M) {
           const float4* src = (const float4*)(xl1 + (size_t)m * rank + jb + 8 * lh);
           const float4 f0 = src[0], f1 = src[1];
-          pk.x = f32_to_bf16_bits(f0.x) | (f32_to_bf16_bits(f0.y) << 16);
-          pk.y = f32_to_bf16_bits(f0.z) | (f32_to_bf16_bits(f0.w) << 16);
-          pk.z = f32_to_bf16_bits(f1.x) | (f32_to_bf16_bits(f1.y) << 16);
-          pk.w = f32_to_bf16_bits(f1.z) | (f32_to_bf16_bits(f1.w) << 16);
+          pk.x = pack_bf16x2(f0.x, f0.y);
+          pk.y = pack_bf16x2(f0.z, f0.w);
+          pk.z = pack_bf16x2(f1.x, f1.y);
+          pk.w = pack_bf16x2(f1.z, f1.w);
         }
         bl[j] = __builtin_bit_cast(v8bf, pk);
       }
@@ -204,7 +230,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
       // Fused attention projection (see gemm_int4.hip): bias first, then
       // per-token RMSNorm and rotary embedding of every Q and K head.  This
       // lane holds columns 32i + 8q + 4lh .. +3 of the wave's 64 for tokens
-      // 32j + lr; the workgroup's 128 columns lie in one part (Q, K or V).
+      // 32j + lr.
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -223,26 +249,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[i][j][4 * q + v] += b[v];
         }
-      const int part = qkv_part(n0 + wn, qe);
-      if (part < 2) {
-        const uint16_t* wnorm = part == 0 ? qe.norm_q : qe.norm_k;
-        const int c0 = qkv_channel(n0 + wn, qe);
-        uint2 wv[2][4];
-        float4 cs[2][2][4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) wv[i][q] = *(const uint2*)(wnorm + c0 + 32 * i + 8 * q + 4 * lh);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int row = qe.rope ? (m0 + wm + 32 * j + lr) % qe.rope_rows : 0;
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              cs[i][j][q] = qe.rope ? *(const float4*)(qe.rope + (size_t)row * qe.head_dim + c0 + 32 * i + 8 * q + 4 * lh)
-                                    : float4{1.0f, 0.0f, 1.0f, 0.0f};
-        }
+      if (qpart < 2) {
         float ss[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -298,8 +305,8 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
             bv[3] = bf16_bits_to_f32(bb.y >> 16);
           }
           uint2 o;
-          o.x = f32_to_bf16_bits(acc[i][j][4 * q] + bv[0]) | (f32_to_bf16_bits(acc[i][j][4 * q + 1] + bv[1]) << 16);
-          o.y = f32_to_bf16_bits(acc[i][j][4 * q + 2] + bv[2]) | (f32_to_bf16_bits(acc[i][j][4 * q + 3] + bv[3]) << 16);
+          o.x = pack_bf16x2(acc[i][j][4 * q] + bv[0], acc[i][j][4 * q + 1] + bv[1]);
+          o.y = pack_bf16x2(acc[i][j][4 * q + 2] + bv[2], acc[i][j][4 * q + 3] + bv[3]);
           *(uint2*)(y + (size_t)m * N + n) = o;
         }
       }

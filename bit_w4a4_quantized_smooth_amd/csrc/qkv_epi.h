@@ -34,9 +34,30 @@ __device__ __forceinline__ float sum_over_halves(float v) {
 }
 
 // 1 / sqrt(mean square + eps) from a head's sum of squares (head_dim is a
-// power of two, so the mean is exact).
+// power of two, so the mean is exact), with the hardware reciprocal square
+// root v_rsq_f32 (about 1 ulp; the result is rounded to bf16 in the end).
 __device__ __forceinline__ float inv_rms(float ss, const QkvEpi& q) {
-  return 1.0f / __builtin_sqrtf(ss * (1.0f / (float)q.head_dim) + q.eps);
+  return __builtin_amdgcn_rsqf(ss * (1.0f / (float)q.head_dim) + q.eps);
+}
+
+// Rotary-table rows of the tokens m, m + STEP, ..., m + (NJ-1)*STEP, i.e. each
+// token mod rope_rows: one division, then one conditional subtraction per
+// step whenever the table is longer than the span (wave-uniform choice).
+template <int NJ, int STEP>
+__device__ __forceinline__ void rope_rows_of(int m, const QkvEpi& q, int (&row)[NJ]) {
+  const int S = q.rope_rows;
+  if (S > (NJ - 1) * STEP) {
+    int r = m % S;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      row[j] = r;
+      r += STEP;
+      r = r >= S ? r - S : r;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) row[j] = (m + j * STEP) % S;
+  }
 }
 
 // Four consecutive channels 4c .. 4c+3 of one head of one token: multiply by

@@ -4,7 +4,8 @@ AWQ W4A16 linears can be traced whole by torch.compile (fullgraph=True).
 The pages say the quantized linear layers work under torch.compile ("Nunchaku
 Lite", section "torch.compile"; blog "Nunchaku 4-bit inference in Diffusers",
 "Benchmarks").  Here each library entry point becomes one opaque operator
-(`svdq::quantize_act`, `svdq::w4a4_gemm`, `svdq::awq_gemv`) with a fake
+(`svdq::quantize_act`, `svdq::w4a4_gemm`, `svdq::w4a4_gemm_qkv_norm_rope`,
+`svdq::awq_gemv`) with a fake
 (meta) implementation that only computes output shapes and dtypes, so the
 tracer never runs a kernel; the real implementation is the ctypes call into
 libsvdq.so on the tensors' current stream.  Nothing here computes: every
@@ -20,7 +21,7 @@ from typing import Optional, Tuple
 import torch
 from torch import Tensor
 
-from . import SVDQ_INT4, SVDQ_NVFP4, GROUP, awq_gemv, quantize_act, w4a4_gemm
+from . import SVDQ_INT4, SVDQ_NVFP4, GROUP, awq_gemv, quantize_act, w4a4_gemm, w4a4_gemm_qkv_norm_rope
 
 _SCALE_DTYPE = {SVDQ_INT4: torch.float16, SVDQ_NVFP4: torch.uint8}
 
@@ -59,6 +60,24 @@ def w4a4_gemm_op(act_codes: Tensor, act_scales: Tensor, w_codes: Tensor, w_scale
 @w4a4_gemm_op.register_fake
 def _(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, precision, act_global_scale, w_global_scale):
     return act_codes.new_empty((act_codes.shape[0], w_codes.shape[0]), dtype=torch.bfloat16)
+
+
+@torch.library.custom_op("svdq::w4a4_gemm_qkv_norm_rope", mutates_args=())
+def w4a4_gemm_qkv_op(act_codes: Tensor, act_scales: Tensor, w_codes: Tensor, w_scales: Tensor,
+                     xl1: Optional[Tensor], l2t: Optional[Tensor], bias: Optional[Tensor], norm_q: Tensor,
+                     norm_k: Tensor, rope: Optional[Tensor], heads: int, head_dim: int, eps: float,
+                     precision: int, act_global_scale: float, w_global_scale: float) -> Tensor:
+    """svdq_w4a4_gemm_qkv_norm_rope: Y bf16 [M, 3 * heads * head_dim]."""
+    if xl1 is not None and xl1.shape[1] == 0:
+        xl1 = None
+    return w4a4_gemm_qkv_norm_rope(precision, act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, heads,
+                                   head_dim, norm_q, norm_k, eps, rope, act_global_scale, w_global_scale)
+
+
+@w4a4_gemm_qkv_op.register_fake
+def _(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, norm_q, norm_k, rope, heads, head_dim, eps,
+      precision, act_global_scale, w_global_scale):
+    return act_codes.new_empty((act_codes.shape[0], 3 * heads * head_dim), dtype=torch.bfloat16)
 
 
 @torch.library.custom_op("svdq::awq_gemv", mutates_args=())

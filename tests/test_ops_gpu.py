@@ -57,6 +57,14 @@ def test_opcheck(prec):
     m = _svdq_module(d)
     torch.library.opcheck(torch.ops.svdq.w4a4_gemm.default,
                           (codes, scales, m.w_codes, m.w_scales, xl1, m.l2t, m.bias, prec, d["alpha_a"], d["alpha_w"]))
+    qd = synth.qkv_layer(33, 96, 2, 128, 256, 16, prec)
+    qc, qs, qx = torch.ops.svdq.quantize_act(_t(qd["x"], torch.bfloat16), _t(qd["lam"], torch.bfloat16),
+                                             _t(qd["l1t"], torch.bfloat16), prec, qd["alpha_a"])
+    qm = _svdq_module(qd)
+    torch.library.opcheck(torch.ops.svdq.w4a4_gemm_qkv_norm_rope.default,
+                          (qc, qs, qm.w_codes, qm.w_scales, qx, qm.l2t, qm.bias, _t(qd["norm_q"], torch.bfloat16),
+                           _t(qd["norm_k"], torch.bfloat16), torch.from_numpy(qd["rope"]).cuda(), 2, 128,
+                           qd["eps"], prec, qd["alpha_a"], qd["alpha_w"]))
     a = synth.awq_layer(32, 3, 512, 1024)
     am = _awq_module(a)
     torch.library.opcheck(torch.ops.svdq.awq_gemv.default,

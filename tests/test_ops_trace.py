@@ -69,3 +69,14 @@ def test_export_full_graph(prec):
     assert targets.count(torch.ops.svdq.awq_gemv.default) == 1
     out = [n for n in ep.graph.nodes if n.op == "output"][0].args[0][0].meta["val"]
     assert out.shape == (2, 48, 256) and out.dtype == torch.bfloat16
+
+
+def test_fake_qkv():
+    with FakeTensorMode():
+        codes = torch.empty(4608, 1536, dtype=torch.uint8)
+        y = torch.ops.svdq.w4a4_gemm_qkv_norm_rope(
+            codes, torch.empty(4608, 48, dtype=torch.float16), torch.empty(9216, 1536, dtype=torch.uint8),
+            torch.empty(9216, 48, dtype=torch.float16), torch.empty(4608, 32), torch.empty(9216, 32, dtype=torch.bfloat16),
+            None, torch.empty(128, dtype=torch.bfloat16), torch.empty(128, dtype=torch.bfloat16),
+            torch.empty(4608, 64, 2), 24, 128, 1e-6, sq.SVDQ_INT4, 1.0, 1.0)
+        assert (y.shape, y.dtype) == ((4608, 9216), torch.bfloat16)
