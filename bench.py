@@ -47,8 +47,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_int4_dit_qkv_4608x92
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # The GPU's clocks need tens of milliseconds of sustained load to settle
+    # (a 4608x9216x3072 GEMM runs ~15% slower for the first ~40 ms after idle),
+    # so the default warm-up is 200 untimed steps (~60 ms).
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--copies", type=int, default=4, help="input copies cycled for the linear")
     p.add_argument("--awq-copies", type=int, default=16, help="AWQ weight copies cycled (>= 512 MB)")
     p.add_argument("--calls", type=int, default=20, help="timed calls per extra workload")
@@ -242,10 +245,17 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def median_ms(fn, calls, stream, torch):
+def median_ms(fn, calls, stream, torch, settle_ms=50.0):
     """Median duration of `calls` back-to-back calls, each bracketed by HIP events
-    on the launch stream (after 3 untimed calls)."""
-    for _ in range(3):
+    on the launch stream, after untimed calls that keep the GPU busy for about
+    settle_ms (its clocks settle under sustained load)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    fn(0)
+    b.record(stream)
+    torch.cuda.synchronize()
+    n_settle = int(min(2000, max(3, settle_ms / max(a.elapsed_time(b), 1e-3))))
+    for _ in range(n_settle):
         fn(0)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
