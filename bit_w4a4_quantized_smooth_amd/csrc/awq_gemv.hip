@@ -35,14 +35,11 @@ typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 namespace {
 constexpr uint32_t kBufDword3 = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr int kOut = 0x7FFFFFF0;              // offset past num_records: the load returns 0
-constexpr int AWQ_WAVES = 8;                  // small-M kernel: waves per workgroup
-constexpr int AWQ_RQ = 1;                     // row quads per wave
-constexpr int AWQ_ROWS = 4 * AWQ_RQ * AWQ_WAVES;  // weight rows per workgroup (power of 2)
-constexpr int AWQ_LOG_ROWS = AWQ_ROWS == 32 ? 5 : AWQ_ROWS == 64 ? 6 : 7;
-constexpr int AWQ_NT = 64 * AWQ_WAVES;
+// Small-M kernel: W waves per workgroup (W = 4, 6 or 8, chosen per shape so
+// that the workgroups spread evenly over the 256 CUs), each owning 4 weight
+// rows, so a workgroup covers 4W rows.
 constexpr int AWQ_PT = 6;                     // 512-channel blocks whose codes are loaded together
 constexpr int AWQ_TBMAX = 16;                 // K <= 8192
-constexpr int AWQ_SS = (AWQ_ROWS * AWQ_TBMAX + AWQ_NT - 1) / AWQ_NT;  // scale items per thread
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr u32 kOnes2 = 0x3F803F80u;  // the bf16 pair (1, 1)
@@ -64,38 +61,40 @@ __device__ __forceinline__ u32 in_vgpr(u32 v) {
 
 // LDS of the small-M kernel, in bytes: x as pairs [TB][4 words][16][MR]
 // (16 B each), the per-chunk sums of x [TB*16][MR] (fp32), the workgroup's
-// (scale, zero-point + 128) pairs [AWQ_ROWS][G] (fp32), and a spare slot
-// that takes the stores of staging items past the end.
+// (scale, zero-point + 128) pairs [rows][G] (fp32), and a spare slot that
+// takes the stores of staging items past the end.
 struct AwqLds {
   int xsl, sz, trash, total, nx, ns;  // nx: 16-byte x items; ns: 8-group scale items
 };
-__host__ __device__ inline AwqLds awq_lds(int K, int MR) {
+__host__ __device__ inline AwqLds awq_lds(int K, int MR, int rows) {
   const int TB = K / 512, G = K / 64;
   AwqLds L;
   L.xsl = TB * 64 * MR * 16;
   L.sz = L.xsl + TB * 16 * MR * 4;
-  L.trash = L.sz + AWQ_ROWS * G * 8;
+  L.trash = L.sz + rows * G * 8;
   L.total = L.trash + 64;
   L.nx = MR * TB * 64;
-  L.ns = AWQ_ROWS * TB;
+  L.ns = rows * TB;
   return L;
 }
 }  // namespace
 
 // Requires K % 512 == 0 (every 16-lane load of a row is whole), K <= 8192,
-// N % AWQ_ROWS == 0 and M <= MR.
-template <int MR, int SX>
-__global__ __launch_bounds__(AWQ_NT) void awq_gemv_kernel(
+// N % (4W) == 0 and M <= MR.
+template <int MR, int SX, int W>
+__global__ __launch_bounds__(64 * W) void awq_gemv_kernel(
     int M, int N, int K, const uint16_t* __restrict__ x, const uint8_t* __restrict__ wc,
     const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wz,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y) {
+  constexpr int ROWS = 4 * W, NT = 64 * W;
+  constexpr int SS = (ROWS * AWQ_TBMAX + NT - 1) / NT;  // scale items per thread
   extern __shared__ __align__(16) uint4 lds4[];
   const int TB = K >> 9, G = K >> 6, rowb = K >> 1;
-  const AwqLds L = awq_lds(K, MR);
+  const AwqLds L = awq_lds(K, MR, ROWS);
   uint8_t* lds = (uint8_t*)lds4;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int b = lane >> 2, c = lane & 3;
-  const int n0 = blockIdx.x * AWQ_ROWS;
+  const int n0 = blockIdx.x * ROWS;
   const int arow = c % MR;  // A rows past MR only feed D rows that are never read
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * K * 2, kBufDword3);
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wc, (short)0, N * rowb, kBufDword3);
@@ -105,11 +104,11 @@ __global__ __launch_bounds__(AWQ_NT) void awq_gemv_kernel(
   // Staging loads, issued before the weight loads so that waiting for them
   // (the counter is in order) does not wait for the weights.  x item
   // it = ((m * TB + t) * 16 + chunk-in-block) * 4 + word; scale item
-  // q = 8-group block * AWQ_ROWS + row.  Items past the end read zeros.
+  // q = 8-group block * ROWS + row.  Items past the end read zeros.
   uint4 xw[SX];
 #pragma unroll
   for (int j = 0; j < SX; ++j) {
-    const int it = tid + j * AWQ_NT;
+    const int it = tid + j * NT;
     int m = 0, tt = it >> 6;
 #pragma unroll
     for (int e = 1; e < MR; ++e)
@@ -119,27 +118,25 @@ __global__ __launch_bounds__(AWQ_NT) void awq_gemv_kernel(
     xw[j] = __builtin_bit_cast(
         uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, ok ? (m * K + 32 * ch + 8 * (it & 3)) * 2 : kOut, 0, 0));
   }
-  uint4 sr[AWQ_SS], zr[AWQ_SS];
+  uint4 sr[SS], zr[SS];
 #pragma unroll
-  for (int j = 0; j < AWQ_SS; ++j) {
-    const int q = tid + j * AWQ_NT;
-    const int off = q < L.ns ? ((n0 + (q & (AWQ_ROWS - 1))) * G + 8 * (q >> AWQ_LOG_ROWS)) * 2 : kOut;
+  for (int j = 0; j < SS; ++j) {
+    const int q = tid + j * NT;
+    const int off = q < L.ns ? ((n0 + q % ROWS) * G + 8 * (q / ROWS)) * 2 : kOut;
     sr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, 0));
     zr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(zres, off, 0, 0));
   }
 
   // codes of this lane's chunks in blocks t0 .. t0+AWQ_PT-1 for its rows,
   // block-major so that block u waits only for its own loads
-  uint4 cv[AWQ_PT][AWQ_RQ];
+  uint4 cv[AWQ_PT];
   auto load_pass = [&](int t0) {
 #pragma unroll
-    for (int u = 0; u < AWQ_PT; ++u)
-#pragma unroll
-      for (int q = 0; q < AWQ_RQ; ++q) {
-        const int n = n0 + wave * 4 * AWQ_RQ + 4 * q + c;
-        cv[u][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 wres, t0 + u < TB ? n * rowb + 16 * (16 * (t0 + u) + b) : kOut, 0, 0));
-      }
+    for (int u = 0; u < AWQ_PT; ++u) {
+      const int n = n0 + wave * 4 + c;
+      cv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            wres, t0 + u < TB ? n * rowb + 16 * (16 * (t0 + u) + b) : kOut, 0, 0));
+    }
   };
   load_pass(0);
 
@@ -148,7 +145,7 @@ __global__ __launch_bounds__(AWQ_NT) void awq_gemv_kernel(
   // the end go to the spare slot).
 #pragma unroll
   for (int j = 0; j < SX; ++j) {
-    const int it = tid + j * AWQ_NT;
+    const int it = tid + j * NT;
     int m = 0, tt = it >> 6;
 #pragma unroll
     for (int e = 1; e < MR; ++e)
@@ -172,8 +169,8 @@ __global__ __launch_bounds__(AWQ_NT) void awq_gemv_kernel(
   }
   // (scale, zero-point + 128) as fp32 pairs
 #pragma unroll
-  for (int j = 0; j < AWQ_SS; ++j) {
-    const int q = tid + j * AWQ_NT;
+  for (int j = 0; j < SS; ++j) {
+    const int q = tid + j * NT;
     const bool live = q < L.ns;
     const u32 sw4[4] = {sr[j].x, sr[j].y, sr[j].z, sr[j].w}, zw4[4] = {zr[j].x, zr[j].y, zr[j].z, zr[j].w};
     float4 o[4];
@@ -181,7 +178,7 @@ __global__ __launch_bounds__(AWQ_NT) void awq_gemv_kernel(
     for (int e = 0; e < 4; ++e)
       o[e] = float4{f16_bits_to_f32(sw4[e] & 0xFFFFu), f16_bits_to_f32(zw4[e] & 0xFFFFu) + 128.0f,
                     f16_bits_to_f32(sw4[e] >> 16), f16_bits_to_f32(zw4[e] >> 16) + 128.0f};
-    float4* dst = (float4*)(lds + (live ? L.sz + ((q & (AWQ_ROWS - 1)) * G + 8 * (q >> AWQ_LOG_ROWS)) * 8 : L.trash));
+    float4* dst = (float4*)(lds + (live ? L.sz + ((q % ROWS) * G + 8 * (q / ROWS)) * 8 : L.trash));
     const int step = live ? 1 : 0;  // the spare slot takes all four
 #pragma unroll
     for (int e = 0; e < 4; ++e) dst[e * step] = o[e];
@@ -193,11 +190,9 @@ __global__ __launch_bounds__(AWQ_NT) void awq_gemv_kernel(
   const float2* szl = (const float2*)(lds + L.sz);
   const u32 kMask = in_vgpr(0x000F000Fu), kBf128 = in_vgpr(0x43004300u);
 
-  float acc[AWQ_RQ][MR];
+  float acc[MR];
 #pragma unroll
-  for (int q = 0; q < AWQ_RQ; ++q)
-#pragma unroll
-    for (int v = 0; v < MR; ++v) acc[q][v] = 0.0f;
+  for (int v = 0; v < MR; ++v) acc[v] = 0.0f;
 
   for (int t0 = 0;;) {
 #pragma unroll
@@ -211,11 +206,10 @@ __global__ __launch_bounds__(AWQ_NT) void awq_gemv_kernel(
       float xs[MR];
 #pragma unroll
       for (int v = 0; v < MR; ++v) xs[v] = xsl[(16 * t + b) * MR + v];
-#pragma unroll
-      for (int q = 0; q < AWQ_RQ; ++q) {
-        const int r = wave * 4 * AWQ_RQ + 4 * q + c;
+      {
+        const int r = wave * 4 + c;
         const float2 sz = szl[r * G + 8 * t + (b >> 1)];
-        const u32 d4[4] = {cv[u][q].x, cv[u][q].y, cv[u][q].z, cv[u][q].w};
+        const u32 d4[4] = {cv[u].x, cv[u].y, cv[u].z, cv[u].w};
         v4f d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -228,7 +222,7 @@ __global__ __launch_bounds__(AWQ_NT) void awq_gemv_kernel(
           d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(as_v4bf(a[i].z, a[i].w), as_v4bf(q2, q3), d, 0, 0, 0);
         }
 #pragma unroll
-        for (int v = 0; v < MR; ++v) acc[q][v] = fmaf(sz.x, fmaf(-sz.y, xs[v], d[v]), acc[q][v]);
+        for (int v = 0; v < MR; ++v) acc[v] = fmaf(sz.x, fmaf(-sz.y, xs[v], d[v]), acc[v]);
       }
     }
     t0 += AWQ_PT;
@@ -238,25 +232,20 @@ __global__ __launch_bounds__(AWQ_NT) void awq_gemv_kernel(
 
   // sum over the 16 blocks (lanes c, c+4, ..., c+60), then lanes 0..3 store
 #pragma unroll
-  for (int q = 0; q < AWQ_RQ; ++q)
-#pragma unroll
-    for (int v = 0; v < MR; ++v) {
-      float r = acc[q][v];
-      r += __shfl_xor(r, 4, 64);
-      r += __shfl_xor(r, 8, 64);
-      r += __shfl_xor(r, 16, 64);
-      r += __shfl_xor(r, 32, 64);
-      acc[q][v] = r;
-    }
+  for (int v = 0; v < MR; ++v) {
+    float r = acc[v];
+    r += __shfl_xor(r, 4, 64);
+    r += __shfl_xor(r, 8, 64);
+    r += __shfl_xor(r, 16, 64);
+    r += __shfl_xor(r, 32, 64);
+    acc[v] = r;
+  }
   if (b == 0) {
+    const int n = n0 + wave * 4 + c;
+    const float bv = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
 #pragma unroll
-    for (int q = 0; q < AWQ_RQ; ++q) {
-      const int n = n0 + wave * 4 * AWQ_RQ + 4 * q + c;
-      const float bv = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
-#pragma unroll
-      for (int v = 0; v < MR; ++v)
-        if (v < M) y[(size_t)v * N + n] = (uint16_t)f32_to_bf16_bits(acc[q][v] + bv);
-    }
+    for (int v = 0; v < MR; ++v)
+      if (v < M) y[(size_t)v * N + n] = (uint16_t)f32_to_bf16_bits(acc[v] + bv);
   }
 }
 
@@ -433,20 +422,45 @@ __global__ __launch_bounds__(512) void awq_gemm_mfma_kernel(
   }
 }
 
+using AwqKern = void (*)(int, int, int, const uint16_t*, const uint8_t*, const uint16_t*, const uint16_t*,
+                         const uint16_t*, uint16_t*);
+template <int W>
+AwqKern awq_small_kernel(int mr_idx, int sx_idx) {
+  static const AwqKern table[3][4] = {
+      {awq_gemv_kernel<1, 1, W>, awq_gemv_kernel<1, 2, W>, awq_gemv_kernel<1, 4, W>, awq_gemv_kernel<1, 8, W>},
+      {awq_gemv_kernel<2, 1, W>, awq_gemv_kernel<2, 2, W>, awq_gemv_kernel<2, 4, W>, awq_gemv_kernel<2, 8, W>},
+      {awq_gemv_kernel<4, 1, W>, awq_gemv_kernel<4, 2, W>, awq_gemv_kernel<4, 4, W>, awq_gemv_kernel<4, 8, W>}};
+  return table[mr_idx][sx_idx];
+}
+
 hipError_t launch_awq(const AwqArgs& a, hipStream_t st) {
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
   const int MR = M <= 1 ? 1 : M <= 2 ? 2 : 4;
-  const AwqLds L = awq_lds(K, MR);
-  const int si = (L.nx + AWQ_NT - 1) / AWQ_NT;  // x staging items per thread
-  if (M <= 4 && K % 512 == 0 && K / 512 <= AWQ_TBMAX && L.total <= 64 * 1024 && si <= 8 && N % AWQ_ROWS == 0) {
-    using Kern = void (*)(int, int, int, const uint16_t*, const uint8_t*, const uint16_t*, const uint16_t*,
-                          const uint16_t*, uint16_t*);
-    static const Kern table[3][4] = {
-        {awq_gemv_kernel<1, 1>, awq_gemv_kernel<1, 2>, awq_gemv_kernel<1, 4>, awq_gemv_kernel<1, 8>},
-        {awq_gemv_kernel<2, 1>, awq_gemv_kernel<2, 2>, awq_gemv_kernel<2, 4>, awq_gemv_kernel<2, 8>},
-        {awq_gemv_kernel<4, 1>, awq_gemv_kernel<4, 2>, awq_gemv_kernel<4, 4>, awq_gemv_kernel<4, 8>}};
+  // Small-M kernel: of the wave counts (8, 6, 4 waves of 4 rows) that fit the
+  // shape, the one whose workgroups fill the 256 CUs most evenly (smallest
+  // ratio of rounds started, ceil(workgroups / 256), to rounds of work).
+  int W = 0, si = 0;
+  long best = 0, best_den = 1;  // compare ceil(wg/256)/(wg/256) as fractions
+  if (M <= 4 && K % 512 == 0 && K / 512 <= AWQ_TBMAX) {
+    for (int w : {8, 6, 4}) {
+      if (N % (4 * w) != 0) continue;
+      const AwqLds L = awq_lds(K, MR, 4 * w);
+      const int items = (L.nx + 64 * w - 1) / (64 * w);  // x staging items per thread
+      if (L.total > 64 * 1024 || items > 8) continue;
+      const long wg = N / (4 * w), rounds = (wg + 255) / 256;
+      // rounds * 256 / wg < best / best_den
+      if (W == 0 || rounds * 256 * best_den < best * wg) {
+        W = w; si = items; best = rounds * 256; best_den = wg;
+      }
+    }
+  }
+  if (W) {
+    const AwqLds L = awq_lds(K, MR, 4 * W);
+    const int mi = MR == 1 ? 0 : MR == 2 ? 1 : 2;
     const int sidx = si <= 1 ? 0 : si <= 2 ? 1 : si <= 4 ? 2 : 3;
-    hipLaunchKernelGGL(table[MR == 1 ? 0 : MR == 2 ? 1 : 2][sidx], dim3(N / AWQ_ROWS), dim3(AWQ_NT), L.total, st,
+    const AwqKern k = W == 8 ? awq_small_kernel<8>(mi, sidx) : W == 6 ? awq_small_kernel<6>(mi, sidx)
+                                                                      : awq_small_kernel<4>(mi, sidx);
+    hipLaunchKernelGGL(k, dim3(N / (4 * W)), dim3(64 * W), L.total, st,
                        M, N, K, (const uint16_t*)a.x, (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales,
                        (const uint16_t*)a.w_zeros, (const uint16_t*)a.bias, (uint16_t*)a.y);
   } else {

@@ -205,6 +205,9 @@ AWQ = {
     "awq_5x1024x1024_nobias": lambda: synth.awq_layer(22, 5, 1024, 1024, with_bias=False),
     "awq_64x1024x3072": lambda: synth.awq_layer(23, 64, 1024, 3072),
     "awq_2x256x5120": lambda: synth.awq_layer(24, 2, 256, 5120),
+    "awq_3x8192x1024": lambda: synth.awq_layer(25, 3, 8192, 1024),
+    "awq_2x3072x8192": lambda: synth.awq_layer(26, 2, 3072, 8192),
+    "awq_4x192x1536": lambda: synth.awq_layer(27, 4, 192, 1536, with_bias=False),
 }
 
 
