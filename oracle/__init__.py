@@ -217,3 +217,40 @@ def w4a4_linear_qkv(prec, a_codes, a_scales, w_codes, w_scales, xl1, l2t, bias, 
     y, _ = w4a4_linear(prec, a_codes, a_scales, w_codes, w_scales, xl1, l2t, bias, alpha_a=alpha_a,
                        alpha_w=alpha_w, rows=ri, cols=ci, nthreads=nthreads)
     return qkv_norm_rope(y.reshape(rid.size, N), rid, heads, head_dim, norm_q, norm_k, eps, rope)
+
+
+def gelu(y):
+    """GELU (erf form) of float64 y in double; returns (h float64, h_bf16 uint16)."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    h = np.zeros_like(y)
+    hb = np.zeros(y.shape, np.uint16)
+    _lib().orc_gelu(_i64(y.size), _p(y), _p(h), _p(hb))
+    return h, hb
+
+
+def smooth(x, lam=None):
+    """The smoothed fp32 activation xh = fl32(x * fl32(1/lambda)) the quantizer rounds."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    M, K = x.shape
+    lam = None if lam is None else np.ascontiguousarray(lam, dtype=np.uint16)
+    out = np.zeros((M, K), np.float32)
+    _lib().orc_smooth(_i64(M), _i64(K), _p(x), _p(lam), _p(out))
+    return out
+
+
+def mlp_up_gelu_quant(a_codes, a_scales, w_codes, w_scales, xl1, l2t, bias, lam_down, l1t_down,
+                      rows=None, nthreads=0):
+    """The fused MLP up-projection (int4): the up linear y over whole rows (all of them, or
+    the token rows `rows`), h = bf16(GELU(y)), then the down-projection's activation
+    quantization of h (smoothing lam_down, int4 group 64) and its low-rank input
+    XL1 = h . L1_down.  Returns dict(y, h_bf16, codes, scales, xl1, xh)."""
+    M, N = a_codes.shape[0], w_codes.shape[0]
+    rid = np.arange(M, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    y, _ = w4a4_linear(INT4, a_codes, a_scales, w_codes, w_scales, xl1, l2t, bias,
+                       rows=np.repeat(rid, N), cols=np.tile(np.arange(N, dtype=np.int64), rid.size),
+                       nthreads=nthreads)
+    y = y.reshape(rid.size, N)
+    _, hb = gelu(y)
+    codes, scales = quantize_act(INT4, hb, lam_down, nthreads=nthreads)
+    xl1_down = lowrank_down(hb, l1t_down, nthreads=nthreads)
+    return dict(y=y, h_bf16=hb, codes=codes, scales=scales, xl1=xl1_down, xh=smooth(hb, lam_down))

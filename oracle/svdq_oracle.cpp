@@ -505,4 +505,30 @@ void orc_qkv_norm_rope(int64_t rows, int heads, int D, const double* y_in, const
   }
 }
 
+// ---------------------------------------------------------------------------
+// GELU of the diffusion-transformer MLP ("Nunchaku Lite", "Fused kernels":
+// the original engine fuses the GELU MLP).  The pages name GELU without a
+// formula; read as the exact form y * Phi(y) with Phi the standard normal
+// CDF, written 0.5 * y * erfc(-y / sqrt(2)) (the same function as
+// 0.5 * y * (1 + erf(y / sqrt(2))), without the cancellation for negative y),
+// in double, then rounded once to bf16 (the compute dtype of the layer, the
+// input format of the next quantizer).  h_bf16 may be NULL.
+// ---------------------------------------------------------------------------
+void orc_gelu(int64_t n, const double* y, double* h, uint16_t* h_bf16) {
+  for (int64_t i = 0; i < n; ++i) {
+    const double v = 0.5 * y[i] * std::erfc(-y[i] / std::sqrt(2.0));
+    h[i] = v;
+    if (h_bf16) h_bf16[i] = f64_to_bf16(v);
+  }
+}
+
+// The smoothed activation the quantizer rounds, xh = fl32(x * fl32(1/lambda_k))
+// (same arithmetic as the first step of orc_quantize_act_*), exported so that
+// a check can see how far a value lies from a rounding boundary.
+void orc_smooth(int64_t M, int64_t K, const uint16_t* x, const uint16_t* lam, float* xh) {
+  std::vector<float> rl = smoothing_reciprocals(K, lam);
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t k = 0; k < K; ++k) xh[m * K + k] = bf16_to_f32(x[m * K + k]) * rl[k];
+}
+
 }  // extern "C"
