@@ -351,6 +351,33 @@ def extras(args, torch, sq, synth, t, bf, f16, stream):
                      "speedup_vs_unfused": round(unfused_ms / fused_ms, 3)}
         del x, lam, l1t, wc, ws, l2t, bias, nq, nk, rope, codes, scales, xl1, y
 
+    # fused MLP up-projection (GEMM + GELU + the down projection's quantization and
+    # X.L1) against the same GEMM writing bf16, torch's GELU and the quantizer
+    d = synth.mlp_layer(1002, 4608, 12288, 3072, 32)
+    up, dn = d["up"], d["down"]
+    M, N, K = 4608, 12288, 3072
+    codes, scales, xl1 = sq.quantize_act(sq.SVDQ_INT4, bf(up["x"]), bf(up["lam"]), bf(up["l1t"]), stream=stream)
+    wc, ws, l2t, bias = t(up["w_codes"]), f16(up["w_scales"]), bf(up["l2t"]), bf(up["bias"])
+    lam_d, l1t_d = bf(dn["lam"]), bf(dn["l1t"])
+    outs = (torch.empty((M, N // 2), dtype=torch.uint8, device=dev), torch.empty((M, N // 64), dtype=torch.float16, device=dev),
+            torch.empty((M, 32), dtype=torch.float32, device=dev))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fused_ms = median_ms(lambda i: sq.w4a4_gemm_gelu_quant(codes, scales, wc, ws, xl1, l2t, bias, lam_d, l1t_d,
+                                                           out=outs, stream=stream), n, stream, torch)
+    plain_ms = median_ms(lambda i: sq.w4a4_gemm(sq.SVDQ_INT4, codes, scales, wc, ws, xl1, l2t, bias, out=y,
+                                                stream=stream), n, stream, torch)
+
+    def unfused(i):
+        sq.w4a4_gemm(sq.SVDQ_INT4, codes, scales, wc, ws, xl1, l2t, bias, out=y, stream=stream)
+        h = torch.nn.functional.gelu(y)
+        sq.quantize_act(sq.SVDQ_INT4, h, lam_d, l1t_d, out=outs, stream=stream)
+
+    unfused_ms = median_ms(unfused, n, stream, torch)
+    res["mlp_up_fused_int4_4608x12288x3072"] = {
+        "fused_ms": round(fused_ms, 5), "plain_gemm_ms": round(plain_ms, 5), "unfused_ms": round(unfused_ms, 5),
+        "speedup_vs_unfused": round(unfused_ms / fused_ms, 3)}
+    del codes, scales, xl1, wc, ws, l2t, bias, lam_d, l1t_d, outs, y
+
     # AWQ at M=64 over >= 512 MB of weight copies
     d = synth.awq_layer(1005, 64, 18432, 3072)
     A = max(1, args.awq_copies)

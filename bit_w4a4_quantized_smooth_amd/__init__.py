@@ -25,7 +25,8 @@ GROUP = {SVDQ_INT4: 64, SVDQ_NVFP4: 16}
 _STATUS = {0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARG", 2: "SVDQ_ERR_UNSUPPORTED",
            3: "SVDQ_ERR_ALIGNMENT", 4: "SVDQ_ERR_DEVICE"}
 
-EXPORTS = ["svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_qkv_norm_rope", "awq_w4a16_gemv",
+EXPORTS = ["svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_qkv_norm_rope", "svdq_w4a4_gemm_gelu_quant",
+           "awq_w4a16_gemv",
            "svdq_w4a4_group_psums", "svdq_last_error", "svdq_abi_version", "svdq_test_set_arch_override"]
 
 
@@ -52,10 +53,12 @@ def lib() -> ctypes.CDLL:
                                      vp, vp, vp]
         L.svdq_w4a4_gemm_qkv_norm_rope.argtypes = [i32, i32, i32, i64, i32, i32, i64, vp, vp, f32, vp, vp,
                                                    f32, vp, vp, vp, vp, vp, f32, vp, i64, vp, vp]
+        L.svdq_w4a4_gemm_gelu_quant.argtypes = [i32, i32, i32, i64, i64, i64, vp, vp, f32, vp, vp, f32, vp, vp,
+                                                vp, vp, vp, i32, vp, vp, vp, vp]
         L.awq_w4a16_gemv.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.svdq_w4a4_group_psums.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp]
-        for f in ("svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_qkv_norm_rope", "awq_w4a16_gemv",
-                  "svdq_w4a4_group_psums"):
+        for f in ("svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_qkv_norm_rope",
+                  "svdq_w4a4_gemm_gelu_quant", "awq_w4a16_gemv", "svdq_w4a4_group_psums"):
             getattr(L, f).restype = i32
         L.svdq_last_error.restype = ctypes.c_char_p
         L.svdq_abi_version.restype = i32
@@ -141,6 +144,28 @@ def w4a4_gemm_qkv_norm_rope(precision: int, act_codes, act_scales, w_codes, w_sc
         _ptr(w_codes), _ptr(w_scales), float(w_global_scale), _ptr(xl1), _ptr(l2t), _ptr(bias), _ptr(norm_q),
         _ptr(norm_k), float(eps), _ptr(rope), rope_rows, _ptr(y), _stream(stream)))
     return y
+
+
+def w4a4_gemm_gelu_quant(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, smooth_out=None,
+                         l1t_out=None, out=None, stream=None):
+    """svdq_w4a4_gemm_gelu_quant (int4): the MLP up-projection with GELU and the down
+    projection's quantization fused.  Returns (codes u8 [M, N/2], scales fp16 [M, N/64],
+    xl1 fp32 [M, r_out] or None); `out` may supply that triple preallocated."""
+    M, K = act_codes.shape[0], act_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    r = 0 if l2t is None else l2t.shape[1]
+    ro = 0 if l1t_out is None else l1t_out.shape[0]
+    if out is None:
+        dev = act_codes.device
+        out = (torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
+               torch.empty((M, N // 64), dtype=torch.float16, device=dev),
+               torch.empty((M, ro), dtype=torch.float32, device=dev) if ro else None)
+    codes, scales, xo = out
+    _check(lib().svdq_w4a4_gemm_gelu_quant(
+        SVDQ_INT4, 64, r, M, N, K, _ptr(act_codes), _ptr(act_scales), 1.0, _ptr(w_codes), _ptr(w_scales), 1.0,
+        _ptr(xl1), _ptr(l2t), _ptr(bias), _ptr(smooth_out), _ptr(l1t_out), ro, _ptr(codes), _ptr(scales),
+        _ptr(xo), _stream(stream)))
+    return codes, scales, xo
 
 
 def group_psums(precision: int, act_codes, w_codes, out=None, stream=None):

@@ -40,6 +40,7 @@
 //   activation and weight panels in that XCD's L2.
 #include "common.h"
 #include "launch.h"
+#include "mlp_epi.h"
 #include "qkv_epi.h"
 
 namespace svdq {
@@ -97,13 +98,15 @@ __device__ __forceinline__ uint4 nib_hi16(uint4 v) {  // 16*q of odd channels
 }  // namespace
 
 // MODE 0: Y = bf16 linear output; 1: int32 partial products; 2: Y of the fused
-// attention projection (Q/K RMSNorm and rotary embedding in the epilogue)
+// attention projection (Q/K RMSNorm and rotary embedding in the epilogue);
+// 3: fused MLP up-projection (no Y: GELU, then the down projection's
+// quantization and low-rank input)
 template <int MODE>
 __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
     int M, int N, int K, int rank, const uint8_t* __restrict__ ac, const uint16_t* __restrict__ as,
     const uint8_t* __restrict__ wc, const uint16_t* __restrict__ ws, const float* __restrict__ xl1,
     const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-    int32_t* __restrict__ psums, QkvEpi qe) {
+    int32_t* __restrict__ psums, QkvEpi qe, MlpEpi me) {
   extern __shared__ __align__(16) uint8_t smem[];
   float* ssc = (float*)(smem + 2 * STAGE);  // [2][KG][NROWS] fp32 scales
 
@@ -508,6 +511,110 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
       }
     }
 
+    if constexpr (MODE == 3) {
+#pragma clang fp contract(off)
+      // Fused MLP up-projection.  y (+ bias) -> h = bf16(GELU(y)), then the
+      // down projection's activation quantization of h, exactly as
+      // svdq_quantize_act would do on a bf16 input: xh = fl32(h * fl32(1/lambda)),
+      // s = fp16_sat(fl32(amax / 7)) over the 64 channels of a group (this
+      // wave's 64 columns), q = clamp(rne(fl32(xh * fl32(1/s))), -8, 7); and
+      // the low-rank input XL1 += h . L1 over this wave's columns (fp32
+      // atomics: every column tile adds its share).  Y is never written.
+      const int nw = n0 + wn;  // first column of this wave: the first channel of its group
+      const int G2 = N >> 6, gd = nw >> 6;
+      u32 hp[BI][BJ][2];       // h as bf16 pairs (channels 4lg + {0,1}, {2,3} of block i)
+      float rl[BI][4];
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const float b[4] = {bf16_bits_to_f32(bb[i].x & 0xFFFFu), bf16_bits_to_f32(bb[i].x >> 16),
+                            bf16_bits_to_f32(bb[i].y & 0xFFFFu), bf16_bits_to_f32(bb[i].y >> 16)};
+        const uint2 lw = me.lam ? *(const uint2*)(me.lam + nw + 16 * i + 4 * lg) : uint2{0x3F803F80u, 0x3F803F80u};
+        rl[i][0] = 1.0f / bf16_bits_to_f32(lw.x & 0xFFFFu);
+        rl[i][1] = 1.0f / bf16_bits_to_f32(lw.x >> 16);
+        rl[i][2] = 1.0f / bf16_bits_to_f32(lw.y & 0xFFFFu);
+        rl[i][3] = 1.0f / bf16_bits_to_f32(lw.y >> 16);
+#pragma unroll
+        for (int j = 0; j < BJ; ++j) {
+          float h[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) h[v] = gelu_f32(acc[i][j][v] + b[v]);
+          hp[i][j][0] = pack_bf16x2(h[0], h[1]);
+          hp[i][j][1] = pack_bf16x2(h[2], h[3]);
+          acc[i][j][0] = bf16_bits_to_f32(hp[i][j][0] & 0xFFFFu) * rl[i][0];  // xh
+          acc[i][j][1] = bf16_bits_to_f32(hp[i][j][0] >> 16) * rl[i][1];
+          acc[i][j][2] = bf16_bits_to_f32(hp[i][j][1] & 0xFFFFu) * rl[i][2];
+          acc[i][j][3] = bf16_bits_to_f32(hp[i][j][1] >> 16) * rl[i][3];
+        }
+      }
+      // codes through LDS (free after the main loop): this wave's 64 tokens x
+      // 32 bytes; lane writes 2 bytes per block, then 16-byte row stores
+      constexpr int CROW = 48;  // bytes per LDS row (32 + pad)
+      uint8_t* ct = smem + wave * (BJ * 16) * CROW;
+#pragma unroll
+      for (int j = 0; j < BJ; ++j) {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) a = fmaxf(a, fabsf(acc[i][j][v]));
+        a = max_over_rows16(a);
+        const u32 sbits = f32_to_f16_sat_bits(a / 7.0f);
+        const float sf = f16_bits_to_f32(sbits);
+        const float t = sf == 0.0f ? 0.0f : 1.0f / sf;
+#pragma unroll
+        for (int i = 0; i < BI; ++i) {
+          u32 w = 0u;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float q = __builtin_rintf(acc[i][j][v] * t);
+            q = fminf(fmaxf(q, -8.0f), 7.0f);
+            w |= ((u32)(int)q & 0xFu) << (4 * v);
+          }
+          *(uint16_t*)(ct + (16 * j + l16) * CROW + 8 * i + 2 * lg) = (uint16_t)w;
+        }
+        const int m = m0 + wm + 16 * j + l16;
+        if (lg == 0 && m < M) me.scales[(size_t)m * G2 + gd] = (uint16_t)sbits;
+      }
+#pragma unroll
+      for (int rr = 0; rr < BJ * 16 * 2 / 64; ++rr) {  // 64 rows x 2 halves, 64 lanes per pass
+        const int row = rr * 32 + (lane >> 1), half = lane & 1;
+        const uint4 v = *(const uint4*)(ct + row * CROW + 16 * half);
+        const int m = m0 + wm + row;
+        if (m < M) *(uint4*)(me.codes + (size_t)m * (N >> 1) + gd * 32 + 16 * half) = v;
+      }
+      // XL1 += h . L1 on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16):
+      // A = h [tokens x 32 channels] with this lane's own channels as its k
+      // slots (16*(2c) + 4lg + 0..3, then 16*(2c+1) + 4lg + 0..3), B = L1 with
+      // the same channel order; D[4lg + v][l16] = token 16j + 4lg + v, rank
+      // column rb*16 + l16
+      for (int rb = 0; rb < me.rank; rb += 16) {
+        const int r = rb + l16;
+        v8bf bl[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint2 lo = *(const uint2*)(me.l1t + (size_t)r * N + nw + 32 * c + 4 * lg);
+          const uint2 hi = *(const uint2*)(me.l1t + (size_t)r * N + nw + 32 * c + 16 + 4 * lg);
+          bl[c] = __builtin_bit_cast(v8bf, uint4{lo.x, lo.y, hi.x, hi.y});
+        }
+#pragma unroll
+        for (int j = 0; j < BJ; ++j) {
+          v4f d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const v8bf al = __builtin_bit_cast(
+                v8bf, uint4{hp[2 * c][j][0], hp[2 * c][j][1], hp[2 * c + 1][j][0], hp[2 * c + 1][j][1]});
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bl[c], d, 0, 0, 0);
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int m = m0 + wm + 16 * j + 4 * lg + v;
+            if (m < M) unsafeAtomicAdd(me.xl1 + (size_t)m * me.rank + r, d[v]);
+          }
+        }
+      }
+      return;
+    }
+
     // bias (MODE 0), bf16 rounding, then the wave's tile goes through LDS
     // (free after the main loop) so that each store instruction writes whole
     // 128-byte row segments of Y: lane l of a store covers row l/8, bytes
@@ -551,24 +658,33 @@ hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
   auto k0 = gemm_int4_kernel<0>;
   auto k1 = gemm_int4_kernel<1>;
   auto k2 = gemm_int4_kernel<2>;
-  const void* kf = a.psums ? (const void*)k1 : a.qkv ? (const void*)k2 : (const void*)k0;
+  auto k3 = gemm_int4_kernel<3>;
+  const void* kf = a.psums ? (const void*)k1 : a.qkv ? (const void*)k2 : a.mlp ? (const void*)k3 : (const void*)k0;
   hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
   if (e != hipSuccess) return e;
-  const QkvEpi none{};
+  const QkvEpi qnone{};
+  const MlpEpi mnone{};
   if (a.psums) {
     hipLaunchKernelGGL(k1, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, 0,
                        (const uint8_t*)a.act_codes, nullptr, (const uint8_t*)a.w_codes, nullptr, nullptr,
-                       nullptr, nullptr, nullptr, (int32_t*)a.psums, none);
+                       nullptr, nullptr, nullptr, (int32_t*)a.psums, qnone, mnone);
   } else if (a.qkv) {
     hipLaunchKernelGGL(k2, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
                        (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
                        (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
-                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, *a.qkv);
+                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, *a.qkv, mnone);
+  } else if (a.mlp) {
+    const int nx = (int)(a.M * a.mlp->rank);
+    if (nx > 0) hipLaunchKernelGGL(fill_zero_f32, dim3((nx + 255) / 256), dim3(256), 0, st, a.mlp->xl1, nx);
+    hipLaunchKernelGGL(k3, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
+                       (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
+                       (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
+                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, nullptr, nullptr, qnone, *a.mlp);
   } else {
     hipLaunchKernelGGL(k0, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
                        (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
                        (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
-                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, none);
+                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, qnone, mnone);
   }
   return hipGetLastError();
 }

@@ -32,6 +32,19 @@ struct QkvEpi {
   int rope_rows;
 };
 
+// Epilogue of the fused MLP up-projection: h = bf16(GELU(y)) is quantized for
+// the down projection (int4, group 64, smoothing lam or NULL) into codes
+// [M, N/2] and fp16 scales [M, N/64], and XL1 = h . L1 [M, rank] is summed
+// into xl1 (zeroed by the launcher) from every column tile.
+struct MlpEpi {
+  const uint16_t* lam;
+  const uint16_t* l1t;  // L1^T [rank, N]
+  int rank;
+  uint8_t* codes;
+  uint16_t* scales;
+  float* xl1;
+};
+
 struct GemmArgs {
   int precision, rank;
   int64_t M, N, K;
@@ -47,6 +60,7 @@ struct GemmArgs {
   void* y;       // bf16 [M, N] (GEMM) ...
   void* psums;   // ... or [M, N, K/G] partial products (test support)
   const QkvEpi* qkv;  // non-null: Y with the Q/K norm and rotary epilogue
+  const MlpEpi* mlp;  // non-null: no Y; GELU + the next layer's quantization
 };
 
 struct AwqArgs {

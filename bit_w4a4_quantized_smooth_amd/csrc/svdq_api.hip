@@ -204,7 +204,7 @@ static svdq_status gemm_y(int precision, int group_size, int rank, int64_t M, in
   if (M == 0) return ok();
   if ((s = check_sticky()) != SVDQ_OK) return s;
   svdq::GemmArgs a{precision, rank, M, N, K, act_codes, act_scales, act_global_scale, w_codes,
-                   w_scales, w_global_scale, xl1, l2t, bias, y, nullptr, qkv};
+                   w_scales, w_global_scale, xl1, l2t, bias, y, nullptr, qkv, nullptr};
   return launched(precision == SVDQ_INT4 ? svdq::launch_gemm_int4(a, (hipStream_t)stream)
                                          : svdq::launch_gemm_nvfp4(a, (hipStream_t)stream));
 }
@@ -243,6 +243,52 @@ svdq_status svdq_w4a4_gemm_qkv_norm_rope(int precision, int group_size, int rank
                 w_scales, w_global_scale, xl1, l2t, bias, y, stream, &q, rope_bytes);
 }
 
+svdq_status svdq_w4a4_gemm_gelu_quant(int precision, int group_size, int rank, int64_t M, int64_t N,
+                                     int64_t K, const void* act_codes, const void* act_scales,
+                                     float act_global_scale, const void* w_codes, const void* w_scales,
+                                     float w_global_scale, const float* xl1, const void* l2t,
+                                     const void* bias, const void* smooth_out, const void* l1t_out,
+                                     int rank_out, void* codes_out, void* scales_out, float* xl1_out,
+                                     void* stream) {
+  svdq_status s;
+  if (precision != SVDQ_INT4)
+    return fail(SVDQ_ERR_UNSUPPORTED, "the fused MLP up-projection supports int4 (group 64) only");
+  if ((s = gemm_common(precision, group_size, rank, M, N, K, act_codes, w_codes)) != SVDQ_OK) return s;
+  if (!valid_rank(rank_out)) return fail(SVDQ_ERR_UNSUPPORTED, "rank_out %d not in {0, 16, ..., 128}", rank_out);
+  if (M == 0) return ok();
+  if (!act_scales || !w_scales || !codes_out || !scales_out)
+    return fail(SVDQ_ERR_INVALID_ARG, "act_scales, w_scales, codes_out and scales_out are required");
+  if ((rank > 0) != (xl1 != nullptr) || (rank > 0) != (l2t != nullptr))
+    return fail(SVDQ_ERR_INVALID_ARG, "xl1 and l2t must be given iff rank > 0");
+  if ((rank_out > 0) != (l1t_out != nullptr) || (rank_out > 0) != (xl1_out != nullptr))
+    return fail(SVDQ_ERR_INVALID_ARG, "l1t_out and xl1_out must be given iff rank_out > 0");
+  if (!aligned16(act_codes) || !aligned16(act_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(xl1) || !aligned16(l2t) || !aligned16(bias) || !aligned16(smooth_out) ||
+      !aligned16(l1t_out) || !aligned16(codes_out) || !aligned16(scales_out) || !aligned16(xl1_out))
+    return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
+  const size_t nc = (size_t)M * N / 2, ns = (size_t)M * (N / 64) * 2, nx = (size_t)M * rank_out * 4;
+  const void* ins[] = {act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, smooth_out, l1t_out};
+  const size_t nin[] = {(size_t)M * K / 2, (size_t)M * (K / 64) * 2, (size_t)N * K / 2, (size_t)N * (K / 64) * 2,
+                        (size_t)M * rank * 4, (size_t)N * rank * 2, (size_t)N * 2, (size_t)N * 2,
+                        (size_t)rank_out * N * 2};
+  for (int i = 0; i < 9; ++i)
+    if (overlaps(codes_out, nc, ins[i], nin[i]) || overlaps(scales_out, ns, ins[i], nin[i]) ||
+        overlaps(xl1_out, nx, ins[i], nin[i]))
+      return fail(SVDQ_ERR_INVALID_ARG, "outputs must not overlap an input");
+  if (overlaps(codes_out, nc, scales_out, ns) || overlaps(codes_out, nc, xl1_out, nx) ||
+      overlaps(scales_out, ns, xl1_out, nx))
+    return fail(SVDQ_ERR_INVALID_ARG, "outputs must not overlap each other");
+  if ((s = check_arch()) != SVDQ_OK) return s;
+  if ((s = check_sticky()) != SVDQ_OK) return s;
+  (void)act_global_scale;
+  (void)w_global_scale;
+  const svdq::MlpEpi me{(const uint16_t*)smooth_out, (const uint16_t*)l1t_out, rank_out, (uint8_t*)codes_out,
+                        (uint16_t*)scales_out, xl1_out};
+  svdq::GemmArgs a{precision, rank, M, N, K, act_codes, act_scales, 1.0f, w_codes, w_scales, 1.0f,
+                   xl1, l2t, bias, nullptr, nullptr, nullptr, &me};
+  return launched(svdq::launch_gemm_int4(a, (hipStream_t)stream));
+}
+
 svdq_status svdq_w4a4_group_psums(int precision, int group_size, int64_t M, int64_t N, int64_t K,
                                   const void* act_codes, const void* w_codes, void* psums,
                                   void* stream) {
@@ -259,7 +305,7 @@ svdq_status svdq_w4a4_group_psums(int precision, int group_size, int64_t M, int6
   if (M == 0) return ok();
   if ((s = check_sticky()) != SVDQ_OK) return s;
   svdq::GemmArgs a{precision, 0, M, N, K, act_codes, nullptr, 1.0f, w_codes, nullptr, 1.0f,
-                   nullptr, nullptr, nullptr, nullptr, psums, nullptr};
+                   nullptr, nullptr, nullptr, nullptr, psums, nullptr, nullptr};
   return launched(precision == SVDQ_INT4 ? svdq::launch_gemm_int4(a, (hipStream_t)stream)
                                          : svdq::launch_gemm_nvfp4(a, (hipStream_t)stream));
 }

@@ -152,6 +152,26 @@ def qkv_layer(seed: int, M: int, heads: int, head_dim: int, K: int, rank: int, p
     return d
 
 
+def mlp_layer(seed: int, M: int, hidden: int, dim: int, rank: int, prec: int = INT4) -> dict:
+    """The two linears of a DiT MLP (dim -> hidden -> dim) for the fused up-projection:
+    `up` = svdq_layer(seed, M, hidden, dim, rank) (its X, outliers and weights); the down
+    projection's smoothing factor lam_down bf16 ~ U(0.5, 2) [hidden] (a stand-in for a
+    calibrated one: calibration would need the hidden activations, which only the method
+    computes), its L1^T bf16 ~ N(0, 0.02^2) [rank, hidden] and its weights as in
+    svdq_layer (int4 codes uniform in [-8, 7], fp16 scales ~ U(0.005, 0.02), L2^T, bias)."""
+    up = svdq_layer(seed, M, hidden, dim, rank, prec, 0.005, 30.0)
+    g = 64
+    down = dict(
+        lam=to_bf16_bits(_rng(seed, 21).uniform(0.5, 2.0, hidden)),
+        l1t=to_bf16_bits(_rng(seed, 22).normal(0.0, 0.02, size=(rank, hidden))) if rank else np.zeros((0, hidden), np.uint16),
+        w_codes=pack_nibbles(_rng(seed, 23).integers(-8, 8, size=(dim, hidden)) & 0xF),
+        w_scales=to_f16_bits(_rng(seed, 24).uniform(0.005, 0.02, size=(dim, hidden // g))),
+        l2t=to_bf16_bits(_rng(seed, 25).normal(0.0, 0.02, size=(dim, rank))) if rank else np.zeros((dim, 0), np.uint16),
+        bias=to_bf16_bits(_rng(seed, 26).normal(0.0, 0.01, size=dim)),
+        rank=rank, N=dim, K=hidden)
+    return dict(up=up, down=down)
+
+
 def awq_layer(seed: int, M: int, N: int, K: int, with_bias: bool = True) -> dict:
     """All inputs of one awq_w4a16 linear: x bf16 ~ N(0,1) [M, K]; unsigned codes
     uniform in 0..15 [N, K]; fp16 scales ~ U(0.005, 0.02) and fp16 zero-points

@@ -151,6 +151,42 @@ svdq_status svdq_w4a4_gemm_qkv_norm_rope(int precision, int group_size, int rank
                                          void* stream);
 
 /*
+ * svdq_w4a4_gemm_gelu_quant -- the fused MLP up-projection: the int4 GEMM of
+ * the up projection, GELU, and the down projection's activation quantization
+ * and low-rank input, all in the GEMM's epilogue, so the [M, N] hidden
+ * activation is never written ("Nunchaku Lite", "Fused kernels": the GELU MLP
+ * fusion of the original engine; blog, "Background: SVDQuant and Nunchaku"
+ * for the quantizer and the low-rank branch):
+ *   y  = the svdq_w4a4_gemm result (bias included) before rounding, [M, N]
+ *   h  = bf16(GELU(y)),  GELU(y) = y * Phi(y) (erf form; the kernel evaluates
+ *        Phi with a rational approximation of absolute error below 1e-7)
+ *   codes_out, scales_out = svdq_quantize_act(SVDQ_INT4, group 64) of h with
+ *        smoothing smooth_out (the same decisions, taken on the kernel's h)
+ *   xl1_out = h . L1_out  (fp32, [M, rank_out]; the column tiles' shares are
+ *        summed with fp32 atomics, so the summation order, and the last bits,
+ *        can differ between calls)
+ * The outputs feed svdq_w4a4_gemm of the down projection (K = N).
+ *
+ *   precision   SVDQ_INT4 only (group_size 64), for the up projection and the
+ *               quantization of h
+ *   rank, M, N, K, act_*, w_*, xl1, l2t, bias   as for svdq_w4a4_gemm
+ *   smooth_out  bf16 [N] smoothing factors of the down projection, or NULL for 1
+ *   l1t_out     bf16 [rank_out, N] (L1 of the down projection, transposed);
+ *               NULL iff rank_out == 0
+ *   rank_out    0, 16, ..., 128
+ *   codes_out   out u8 [M, N/2]; scales_out out fp16 [M, N/64];
+ *   xl1_out     out fp32 [M, rank_out] (NULL iff rank_out == 0)
+ * No output may overlap an input or another output.
+ */
+svdq_status svdq_w4a4_gemm_gelu_quant(int precision, int group_size, int rank, int64_t M, int64_t N,
+                                     int64_t K, const void* act_codes, const void* act_scales,
+                                     float act_global_scale, const void* w_codes, const void* w_scales,
+                                     float w_global_scale, const float* xl1, const void* l2t,
+                                     const void* bias, const void* smooth_out, const void* l1t_out,
+                                     int rank_out, void* codes_out, void* scales_out, float* xl1_out,
+                                     void* stream);
+
+/*
  * awq_w4a16_gemv -- AWQ-style int4 weight-only linear for memory-bound
  * modulation projections ("Supported quantization types": awq_w4a16, int4,
  * group 64; blog, "Introducing Nunchaku Lite"):

@@ -160,3 +160,27 @@ def test_qkv_entry_point_validation(L):
     assert qkv(L, y=9 * A) == INVALID                 # y aliases norm_q
     L.svdq_test_set_arch_override(b"gfx950")
     assert qkv(L, M=0) == OK
+
+
+def mlp(L, prec=0, G=64, r=16, M=256, N=512, K=512, ac=A, as_=2 * A, wc=3 * A, ws=4 * A, xl1=5 * A, l2t=6 * A,
+        bias=7 * A, lam=9 * A, l1t=10 * A, ro=32, co=11 * A, so=12 * A, xo=13 * A):
+    return L.svdq_w4a4_gemm_gelu_quant(prec, G, r, M, N, K, ac, as_, 1.0, wc, ws, 1.0, xl1, l2t, bias, lam, l1t,
+                                       ro, co, so, xo, None)
+
+
+def test_mlp_entry_point_validation(L):
+    assert mlp(L) == UNSUPPORTED                       # valid: reaches the arch check
+    assert mlp(L, lam=None) == UNSUPPORTED             # smoothing is optional
+    assert mlp(L, ro=0, l1t=None, xo=None) == UNSUPPORTED
+    assert mlp(L, prec=1, G=16) == UNSUPPORTED         # int4 only
+    assert mlp(L, ro=24) == UNSUPPORTED
+    assert mlp(L, N=500) == UNSUPPORTED
+    assert mlp(L, ro=32, l1t=None) == INVALID
+    assert mlp(L, ro=32, xo=None) == INVALID
+    assert mlp(L, co=None) == INVALID
+    assert mlp(L, so=None) == INVALID
+    assert mlp(L, co=11 * A + 8) == ALIGN
+    assert mlp(L, co=A) == INVALID                     # codes_out aliases act_codes
+    assert mlp(L, xo=12 * A) == INVALID                # xl1_out aliases scales_out
+    L.svdq_test_set_arch_override(b"gfx950")
+    assert mlp(L, M=0) == OK
