@@ -254,3 +254,71 @@ def mlp_up_gelu_quant(a_codes, a_scales, w_codes, w_scales, xl1, l2t, bias, lam_
     codes, scales = quantize_act(INT4, hb, lam_down, nthreads=nthreads)
     xl1_down = lowrank_down(hb, l1t_down, nthreads=nthreads)
     return dict(y=y, h_bf16=hb, codes=codes, scales=scales, xl1=xl1_down, xh=smooth(hb, lam_down))
+
+
+def f64_to_bf16(x):
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, np.uint16)
+    _lib().orc_vec_f64_to_bf16(_p(x), _p(out), _i64(x.size))
+    return out
+
+
+def calibrate_smooth(x_cal, w):
+    """Smoothing factor lambda bf16 [K] from a calibration batch x_cal bf16 [Mc, K] and the
+    dense weight w bf16 [N, K]: bf16(sqrt(fl32(max|x_k| / max|w_k|))), 1 if either is 0."""
+    x_cal = np.ascontiguousarray(x_cal, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    lam = np.zeros(w.shape[1], np.uint16)
+    _lib().orc_calibrate_smooth(_i64(x_cal.shape[0]), _i64(w.shape[0]), _i64(w.shape[1]), _p(x_cal), _p(w),
+                                _p(lam))
+    return lam
+
+
+def lowrank_decompose(w, lam, rank):
+    """The rank-r branch of SVDQuant from the dense weight w bf16 [N, K] and lambda bf16 [K].
+    Definition (double): W_hat = W diag(lambda) (the smoothed weight, so that
+    (X / lambda) W_hat^T = X W^T); W_hat = U S V^T (numpy SVD); the best rank-r
+    approximation (Eckart-Young) is U_r S_r V_r^T, split evenly between the factors and
+    moved back to raw X for the layer:  L1 = diag(1/lambda) V_r S_r^(1/2) [K, r],
+    L2 = S_r^(1/2) U_r^T [r, N].  Returns dict(l1t = bf16(L1^T) [r, K], l2t = bf16(L2^T)
+    [N, r], lowrank = U_r S_r V_r^T, residual = W_hat - (diag(lambda) L1b L2b)^T, the part
+    the 4-bit weight must carry given the stored bf16 factors L1b, L2b, w_hat, sigma)."""
+    wf = bf16_to_f32(np.ascontiguousarray(w, dtype=np.uint16)).astype(np.float64)
+    lamf = bf16_to_f32(np.ascontiguousarray(lam, dtype=np.uint16)).astype(np.float64)
+    w_hat = wf * lamf[None, :]
+    U, S, Vt = np.linalg.svd(w_hat, full_matrices=False)
+    Ur, Sr, Vr = U[:, :rank], S[:rank], Vt[:rank, :].T
+    sq = np.sqrt(Sr)
+    l1 = (Vr * sq[None, :]) / lamf[:, None]          # [K, r]
+    l2 = (Ur * sq[None, :]).T                         # [r, N]
+    l1t = f64_to_bf16(l1.T)
+    l2t = f64_to_bf16(l2.T)
+    l1b = bf16_to_f32(l1t).astype(np.float64).T       # [K, r]
+    l2b = bf16_to_f32(l2t).astype(np.float64).T       # [r, N]
+    lowrank_b = ((lamf[:, None] * l1b) @ l2b).T       # [N, K]
+    return dict(l1t=l1t, l2t=l2t, lowrank=(Ur * Sr[None, :]) @ Vr.T, residual=w_hat - lowrank_b,
+                w_hat=w_hat, sigma=S)
+
+
+def quantize_weight(prec, r, alpha=1.0):
+    """4-bit codes and scales of an fp32 residual r [N, K] (int4 group 64 / nvfp4 group 16)."""
+    r = np.ascontiguousarray(r, dtype=np.float32)
+    N, K = r.shape
+    G = 64 if prec == INT4 else 16
+    codes = np.zeros((N, K // 2), np.uint8)
+    scales = np.zeros((N, K // G), np.uint16 if prec == INT4 else np.uint8)
+    _lib().orc_quantize_weight(ctypes.c_int(prec), _i64(N), _i64(K), _p(r), ctypes.c_float(alpha), _p(codes),
+                               _p(scales))
+    return codes, scales
+
+
+def awq_quantize_weight(w):
+    """AWQ int4 weight-only quantization of w bf16 [N, K]: (codes u8 [N, K/2], scales fp16
+    [N, K/64], zero-points fp16 [N, K/64]), min-max over a range containing 0."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    N, K = w.shape
+    codes = np.zeros((N, K // 2), np.uint8)
+    scales = np.zeros((N, K // 64), np.uint16)
+    zeros = np.zeros((N, K // 64), np.uint16)
+    _lib().orc_awq_quantize_weight(_i64(N), _i64(K), _p(w), _p(codes), _p(scales), _p(zeros))
+    return codes, scales, zeros

@@ -531,4 +531,105 @@ void orc_smooth(int64_t M, int64_t K, const uint16_t* x, const uint16_t* lam, fl
     for (int64_t k = 0; k < K; ++k) xh[m * K + k] = bf16_to_f32(x[m * K + k]) * rl[k];
 }
 
+// ---------------------------------------------------------------------------
+// Offline weight side of SVDQuant (blog "Nunchaku 4-bit inference in
+// Diffusers", "Background: SVDQuant and Nunchaku": activation outliers are
+// moved into the weights, the hardest part of each weight becomes a 16-bit
+// low-rank branch, the residual is quantized to 4 bits; "Nunchaku Lite",
+// quantization walkthrough: the checkpoint is produced offline from the dense
+// weights).  The pages give no formulas; readings:
+//   * smoothing factor per input channel k (SmoothQuant-style migration with
+//     strength 1/2): lambda_k = bf16(sqrt(fl32(a_k / b_k))), a_k = max_m |X_mk|
+//     over the calibration batch, b_k = max_n |W_nk|; 1 when a_k or b_k is 0;
+//   * (the rank-r decomposition of the smoothed weight is computed in
+//     oracle/__init__.py with numpy's SVD in double);
+//   * residual quantization per (row n, group of G channels), int4 G = 64:
+//       s = fp16_sat(fl32(amax / 7)), q = clamp(rne(fl32(r * fl32(1/s))), -8, 7)
+//     nvfp4 G = 16 with the per-tensor scale alpha_w:
+//       s = e4m3_sat(fl32(amax / fl32(6 alpha))), c = e2m1_sat(fl32(r * fl32(1/fl32(s alpha))))
+//     i.e. the activation quantizer's steps on an fp32 input without smoothing;
+//   * AWQ weights (int4 weight-only, group 64, unsigned codes with a zero-point):
+//     min-max asymmetric quantization per (row, group) over a range that
+//     contains 0 (so 0 is exact): lo = min(0, min w), hi = max(0, max w),
+//     s = fp16(fl32((hi - lo) / 15)), z = clamp(rne(fl32(-lo * fl32(1/s))), 0, 15)
+//     stored as fp16, q = clamp(rne(fl32(w * fl32(1/s))) + z, 0, 15); an
+//     all-zero group has s = 0, z = 0, codes 0.
+// ---------------------------------------------------------------------------
+void orc_calibrate_smooth(int64_t Mc, int64_t N, int64_t K, const uint16_t* x, const uint16_t* w,
+                          uint16_t* lam) {
+  for (int64_t k = 0; k < K; ++k) {
+    float a = 0.0f, b = 0.0f;
+    for (int64_t m = 0; m < Mc; ++m) a = std::max(a, std::fabs(bf16_to_f32(x[m * K + k])));
+    for (int64_t n = 0; n < N; ++n) b = std::max(b, std::fabs(bf16_to_f32(w[n * K + k])));
+    float l = 1.0f;
+    if (a > 0.0f && b > 0.0f) l = std::sqrt(a / b);
+    lam[k] = f32_to_bf16(l);
+  }
+}
+
+void orc_quantize_weight(int prec, int64_t N, int64_t K, const float* r, float alpha, uint8_t* codes,
+                         void* scales) {
+  const int64_t G = prec == 0 ? 64 : 16, ng = K / G;
+  for (int64_t n = 0; n < N; ++n) {
+    const float* rr = r + n * K;
+    uint8_t* cr = codes + n * (K / 2);
+    for (int64_t g = 0; g < ng; ++g) {
+      float a = 0.0f;
+      for (int64_t j = 0; j < G; ++j) a = std::max(a, std::fabs(rr[g * G + j]));
+      if (prec == 0) {
+        const uint16_t sbits = f32_to_f16_sat(a / 7.0f);
+        ((uint16_t*)scales)[n * ng + g] = sbits;
+        const float s = f16_to_f32(sbits);
+        const float t = s == 0.0f ? 0.0f : 1.0f / s;
+        for (int64_t j = 0; j < G; ++j) {
+          int q = 0;
+          if (s != 0.0f) q = (int)std::min(7.0f, std::max(-8.0f, std::nearbyint(rr[g * G + j] * t)));
+          put_nibble(cr, g * G + j, (uint8_t)(q & 0xF));
+        }
+      } else {
+        const float d6 = 6.0f * alpha;
+        const uint8_t sbits = f32_to_e4m3_sat(a / d6);
+        ((uint8_t*)scales)[n * ng + g] = sbits;
+        const float s = e4m3_to_f32(sbits);
+        const float t = s == 0.0f ? 0.0f : 1.0f / (s * alpha);
+        for (int64_t j = 0; j < G; ++j) {
+          const uint8_t c = s == 0.0f ? 0 : f32_to_e2m1_sat(rr[g * G + j] * t);
+          put_nibble(cr, g * G + j, c);
+        }
+      }
+    }
+  }
+}
+
+void orc_awq_quantize_weight(int64_t N, int64_t K, const uint16_t* w, uint8_t* codes, uint16_t* scales,
+                             uint16_t* zeros) {
+  const int64_t G = 64, ng = K / G;
+  for (int64_t n = 0; n < N; ++n) {
+    const uint16_t* wr = w + n * K;
+    uint8_t* cr = codes + n * (K / 2);
+    for (int64_t g = 0; g < ng; ++g) {
+      float lo = 0.0f, hi = 0.0f;
+      for (int64_t j = 0; j < G; ++j) {
+        lo = std::min(lo, bf16_to_f32(wr[g * G + j]));
+        hi = std::max(hi, bf16_to_f32(wr[g * G + j]));
+      }
+      const uint16_t sbits = f32_to_f16_sat((hi - lo) / 15.0f);
+      const float s = f16_to_f32(sbits);
+      const float t = s == 0.0f ? 0.0f : 1.0f / s;
+      const float z = s == 0.0f ? 0.0f : std::min(15.0f, std::max(0.0f, std::nearbyint(-lo * t)));
+      scales[n * ng + g] = sbits;
+      zeros[n * ng + g] = f32_to_f16_sat(z);
+      for (int64_t j = 0; j < G; ++j) {
+        float q = z;
+        if (s != 0.0f) q = std::min(15.0f, std::max(0.0f, std::nearbyint(bf16_to_f32(wr[g * G + j]) * t) + z));
+        put_nibble(cr, g * G + j, (uint8_t)((int)q & 0xF));
+      }
+    }
+  }
+}
+
+void orc_vec_f64_to_bf16(const double* in, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f64_to_bf16(in[i]);
+}
+
 }  // extern "C"
