@@ -26,7 +26,8 @@ _STATUS = {0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARG", 2: "SVDQ_ERR_UNSUPPORTED",
            3: "SVDQ_ERR_ALIGNMENT", 4: "SVDQ_ERR_DEVICE"}
 
 EXPORTS = ["svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_qkv_norm_rope", "svdq_w4a4_gemm_gelu_quant",
-           "awq_w4a16_gemv",
+           "awq_w4a16_gemv", "svdq_calibrate_smooth", "svdq_lowrank_workspace_bytes", "svdq_lowrank_decompose",
+           "svdq_quantize_weight", "awq_quantize_weight",
            "svdq_w4a4_group_psums", "svdq_last_error", "svdq_abi_version", "svdq_test_set_arch_override"]
 
 
@@ -56,9 +57,16 @@ def lib() -> ctypes.CDLL:
         L.svdq_w4a4_gemm_gelu_quant.argtypes = [i32, i32, i32, i64, i64, i64, vp, vp, f32, vp, vp, f32, vp, vp,
                                                 vp, vp, vp, i32, vp, vp, vp, vp]
         L.awq_w4a16_gemv.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        L.svdq_calibrate_smooth.argtypes = [i64, i64, i64, vp, vp, vp, vp]
+        L.svdq_lowrank_workspace_bytes.argtypes = [i64, i64, i32, i32]
+        L.svdq_lowrank_workspace_bytes.restype = i64
+        L.svdq_lowrank_decompose.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp]
+        L.svdq_quantize_weight.argtypes = [i32, i32, i64, i64, vp, f32, vp, vp, vp]
+        L.awq_quantize_weight.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
         L.svdq_w4a4_group_psums.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp]
         for f in ("svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_qkv_norm_rope",
-                  "svdq_w4a4_gemm_gelu_quant", "awq_w4a16_gemv", "svdq_w4a4_group_psums"):
+                  "svdq_w4a4_gemm_gelu_quant", "awq_w4a16_gemv", "svdq_w4a4_group_psums", "svdq_calibrate_smooth",
+                  "svdq_lowrank_decompose", "svdq_quantize_weight", "awq_quantize_weight"):
             getattr(L, f).restype = i32
         L.svdq_last_error.restype = ctypes.c_char_p
         L.svdq_abi_version.restype = i32
@@ -166,6 +174,58 @@ def w4a4_gemm_gelu_quant(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bia
         _ptr(xl1), _ptr(l2t), _ptr(bias), _ptr(smooth_out), _ptr(l1t_out), ro, _ptr(codes), _ptr(scales),
         _ptr(xo), _stream(stream)))
     return codes, scales, xo
+
+
+def calibrate_smooth(x_cal, w, out=None, stream=None):
+    """svdq_calibrate_smooth: lambda bf16 [K] from calibration activations and the dense weight."""
+    Mc, K = x_cal.shape
+    N = w.shape[0]
+    lam = out if out is not None else torch.empty(K, dtype=torch.bfloat16, device=w.device)
+    _check(lib().svdq_calibrate_smooth(Mc, N, K, _ptr(x_cal), _ptr(w), _ptr(lam), _stream(stream)))
+    return lam
+
+
+def lowrank_decompose(w, smooth, omega, rank: int, iters: int = 4, stream=None):
+    """svdq_lowrank_decompose: returns (l1t bf16 [rank, K], l2t bf16 [N, rank], residual fp32 [N, K]).
+    omega: fp32 [K, rank + oversample] test matrix."""
+    N, K = w.shape
+    p = omega.shape[1]
+    nbytes = lib().svdq_lowrank_workspace_bytes(N, K, rank, p - rank)
+    if nbytes < 0:
+        raise SvdqError(2, f"unsupported decomposition sizes N={N} K={K} rank={rank} p={p}")
+    dev = w.device
+    work = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    l1t = torch.empty((rank, K), dtype=torch.bfloat16, device=dev)
+    l2t = torch.empty((N, rank), dtype=torch.bfloat16, device=dev)
+    res = torch.empty((N, K), dtype=torch.float32, device=dev)
+    _check(lib().svdq_lowrank_decompose(N, K, rank, p - rank, iters, _ptr(w), _ptr(smooth), _ptr(omega), _ptr(l1t),
+                                        _ptr(l2t), _ptr(res), _ptr(work), nbytes, _stream(stream)))
+    return l1t, l2t, res
+
+
+def quantize_weight(precision: int, residual, w_global_scale: float = 1.0, out=None, stream=None):
+    """svdq_quantize_weight: (codes u8 [N, K/2], scales) of an fp32 residual [N, K]."""
+    N, K = residual.shape
+    G = GROUP.get(precision, 64)
+    if out is None:
+        out = (torch.empty((N, K // 2), dtype=torch.uint8, device=residual.device),
+               torch.empty((N, K // G), dtype=torch.float16 if precision == SVDQ_INT4 else torch.uint8,
+                           device=residual.device))
+    _check(lib().svdq_quantize_weight(precision, G, N, K, _ptr(residual), float(w_global_scale), _ptr(out[0]),
+                                      _ptr(out[1]), _stream(stream)))
+    return out
+
+
+def awq_quantize_weight(w, out=None, stream=None):
+    """awq_quantize_weight: (codes u8 [N, K/2], scales fp16 [N, K/64], zeros fp16 [N, K/64])."""
+    N, K = w.shape
+    if out is None:
+        dev = w.device
+        out = (torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
+               torch.empty((N, K // 64), dtype=torch.float16, device=dev),
+               torch.empty((N, K // 64), dtype=torch.float16, device=dev))
+    _check(lib().awq_quantize_weight(64, N, K, _ptr(w), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _stream(stream)))
+    return out
 
 
 def group_psums(precision: int, act_codes, w_codes, out=None, stream=None):

@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsvdq.so")
-SOURCES = ["svdq_api.hip", "quant_act.hip", "gemm_int4.hip", "gemm_nvfp4.hip", "awq_gemv.hip"]
+SOURCES = ["svdq_api.hip", "quant_act.hip", "gemm_int4.hip", "gemm_nvfp4.hip", "awq_gemv.hip", "offline.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -73,7 +73,26 @@ struct AwqArgs {
   void* y;
 };
 
+struct LowrankArgs {
+  int64_t N, K;
+  int rank, p, iters;
+  const void* w;
+  const void* lam;
+  const float* omega;
+  void* l1t;
+  void* l2t;
+  float* residual;
+  void* work;
+};
+
 hipError_t launch_quantize_act(const QuantArgs& a, hipStream_t st);
+hipError_t launch_calibrate(int64_t Mc, int64_t N, int64_t K, const void* x, const void* w, void* lam, hipStream_t st);
+size_t lowrank_workspace_bytes(int64_t N, int64_t K, int p);
+hipError_t launch_lowrank(const LowrankArgs& a, hipStream_t st);
+hipError_t launch_quantize_weight(int precision, int64_t N, int64_t K, const float* r, float alpha, void* codes,
+                                  void* scales, hipStream_t st);
+hipError_t launch_awq_quantize(int64_t N, int64_t K, const void* w, void* codes, void* scales, void* zeros,
+                               hipStream_t st);
 hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st);
 hipError_t launch_awq(const AwqArgs& a, hipStream_t st);

@@ -310,6 +310,109 @@ svdq_status svdq_w4a4_group_psums(int precision, int group_size, int64_t M, int6
                                          : svdq::launch_gemm_nvfp4(a, (hipStream_t)stream));
 }
 
+svdq_status svdq_calibrate_smooth(int64_t Mc, int64_t N, int64_t K, const void* x_cal, const void* w,
+                                  void* smooth_out, void* stream) {
+  if (Mc < 0 || N < 0 || K <= 0 || Mc > kMaxDim || N > kMaxDim || K > kMaxDim || K % 2 != 0)
+    return fail(SVDQ_ERR_INVALID_ARG, "bad shape Mc=%lld N=%lld K=%lld", (long long)Mc, (long long)N, (long long)K);
+  if (Mc * K > ((int64_t)1 << 31) || N * K > ((int64_t)1 << 31)) return fail(SVDQ_ERR_UNSUPPORTED, "operand above 2^31 elements");
+  if (!smooth_out || (Mc > 0 && !x_cal) || (N > 0 && !w))
+    return fail(SVDQ_ERR_INVALID_ARG, "x_cal, w and smooth_out are required");
+  if (!aligned16(x_cal) || !aligned16(w) || !aligned16(smooth_out))
+    return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
+  if (overlaps(smooth_out, (size_t)K * 2, x_cal, (size_t)Mc * K * 2) || overlaps(smooth_out, (size_t)K * 2, w, (size_t)N * K * 2))
+    return fail(SVDQ_ERR_INVALID_ARG, "smooth_out must not overlap an input");
+  svdq_status s;
+  if ((s = check_arch()) != SVDQ_OK) return s;
+  if ((s = check_sticky()) != SVDQ_OK) return s;
+  return launched(svdq::launch_calibrate(Mc, N, K, x_cal, w, smooth_out, (hipStream_t)stream));
+}
+
+int64_t svdq_lowrank_workspace_bytes(int64_t N, int64_t K, int rank, int oversample) {
+  if (N <= 0 || K <= 0 || rank <= 0 || oversample < 0 || rank + oversample > 64) return -1;
+  return (int64_t)svdq::lowrank_workspace_bytes(N, K, rank + oversample);
+}
+
+svdq_status svdq_lowrank_decompose(int64_t N, int64_t K, int rank, int oversample, int iters, const void* w,
+                                   const void* smooth, const float* omega, void* l1t, void* l2t, float* residual,
+                                   void* work, int64_t work_bytes, void* stream) {
+  if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || K % 64 != 0)
+    return fail(SVDQ_ERR_INVALID_ARG, "bad shape N=%lld K=%lld (K %% 64 == 0)", (long long)N, (long long)K);
+  if (N * K > ((int64_t)1 << 31)) return fail(SVDQ_ERR_UNSUPPORTED, "N*K above 2^31");
+  if (rank <= 0 || rank % 16 != 0 || rank > 64 || oversample < 0 || rank + oversample > 64 ||
+      rank + oversample > N || rank + oversample > K)
+    return fail(SVDQ_ERR_UNSUPPORTED, "rank %d (multiple of 16) + oversample %d must be <= 64 and <= min(N, K)",
+                rank, oversample);
+  if (iters < 0 || iters > 64) return fail(SVDQ_ERR_INVALID_ARG, "iters %d not in [0, 64]", iters);
+  if (!w || !omega || !l1t || !l2t || !residual || !work)
+    return fail(SVDQ_ERR_INVALID_ARG, "w, omega, l1t, l2t, residual and work are required");
+  const int p = rank + oversample;
+  if (work_bytes < (int64_t)svdq::lowrank_workspace_bytes(N, K, p))
+    return fail(SVDQ_ERR_INVALID_ARG, "work_bytes %lld below svdq_lowrank_workspace_bytes()", (long long)work_bytes);
+  if (!aligned16(w) || !aligned16(smooth) || !aligned16(omega) || !aligned16(l1t) || !aligned16(l2t) ||
+      !aligned16(residual) || !aligned16(work))
+    return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
+  const size_t nr = (size_t)N * K * 4, nw = (size_t)work_bytes, n1 = (size_t)rank * K * 2, n2 = (size_t)N * rank * 2;
+  const void* outs[] = {l1t, l2t, residual, work};
+  const size_t nouts[] = {n1, n2, nr, nw};
+  const void* ins[] = {w, smooth, omega};
+  const size_t nins[] = {(size_t)N * K * 2, (size_t)K * 2, (size_t)K * p * 4};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(outs[i], nouts[i], ins[j], nins[j])) return fail(SVDQ_ERR_INVALID_ARG, "outputs must not overlap an input");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], nouts[i], outs[j], nouts[j])) return fail(SVDQ_ERR_INVALID_ARG, "outputs must not overlap each other");
+  }
+  svdq_status s;
+  if ((s = check_arch()) != SVDQ_OK) return s;
+  if ((s = check_sticky()) != SVDQ_OK) return s;
+  svdq::LowrankArgs a{N, K, rank, p, iters, w, smooth, omega, l1t, l2t, residual, work};
+  return launched(svdq::launch_lowrank(a, (hipStream_t)stream));
+}
+
+svdq_status svdq_quantize_weight(int precision, int group_size, int64_t N, int64_t K, const float* residual,
+                                 float w_global_scale, void* codes, void* scales, void* stream) {
+  svdq_status s;
+  if ((s = check_precision(precision, group_size)) != SVDQ_OK) return s;
+  if (N < 0 || K <= 0 || N > kMaxDim || K > kMaxDim || K % 64 != 0)
+    return fail(SVDQ_ERR_INVALID_ARG, "bad shape N=%lld K=%lld (K %% 64 == 0)", (long long)N, (long long)K);
+  if (N * K > ((int64_t)1 << 31)) return fail(SVDQ_ERR_UNSUPPORTED, "N*K above 2^31");
+  if (precision == SVDQ_NVFP4 && !(w_global_scale > 0.0f && w_global_scale < 3.0e38f))
+    return fail(SVDQ_ERR_INVALID_ARG, "w_global_scale must be finite and > 0 for nvfp4");
+  if (N == 0) return ok();
+  if (!residual || !codes || !scales) return fail(SVDQ_ERR_INVALID_ARG, "residual, codes and scales are required");
+  if (!aligned16(residual) || !aligned16(codes) || !aligned16(scales))
+    return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
+  const size_t nr = (size_t)N * K * 4, nc = (size_t)N * K / 2;
+  const size_t ns = precision == SVDQ_INT4 ? (size_t)N * (K / 64) * 2 : (size_t)N * (K / 16);
+  if (overlaps(codes, nc, residual, nr) || overlaps(scales, ns, residual, nr) || overlaps(codes, nc, scales, ns))
+    return fail(SVDQ_ERR_INVALID_ARG, "outputs must not overlap each other or the input");
+  if ((s = check_arch()) != SVDQ_OK) return s;
+  if ((s = check_sticky()) != SVDQ_OK) return s;
+  return launched(svdq::launch_quantize_weight(precision, N, K, residual, w_global_scale, codes, scales,
+                                               (hipStream_t)stream));
+}
+
+svdq_status awq_quantize_weight(int group_size, int64_t N, int64_t K, const void* w, void* codes, void* scales,
+                                void* zeros, void* stream) {
+  if (group_size != 64)
+    return fail(SVDQ_ERR_UNSUPPORTED, "awq_w4a16 supports int4 with group 64; got group %d", group_size);
+  if (N < 0 || K <= 0 || N > kMaxDim || K > kMaxDim || K % 64 != 0)
+    return fail(SVDQ_ERR_INVALID_ARG, "bad shape N=%lld K=%lld (K %% 64 == 0)", (long long)N, (long long)K);
+  if (N * K > ((int64_t)1 << 31)) return fail(SVDQ_ERR_UNSUPPORTED, "N*K above 2^31");
+  if (N == 0) return ok();
+  if (!w || !codes || !scales || !zeros) return fail(SVDQ_ERR_INVALID_ARG, "w, codes, scales and zeros are required");
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) || !aligned16(zeros))
+    return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
+  const size_t nw = (size_t)N * K * 2, nc = (size_t)N * K / 2, ng = (size_t)N * (K / 64) * 2;
+  if (overlaps(codes, nc, w, nw) || overlaps(scales, ng, w, nw) || overlaps(zeros, ng, w, nw) ||
+      overlaps(codes, nc, scales, ng) || overlaps(codes, nc, zeros, ng) || overlaps(scales, ng, zeros, ng))
+    return fail(SVDQ_ERR_INVALID_ARG, "outputs must not overlap each other or the input");
+  svdq_status s;
+  if ((s = check_arch()) != SVDQ_OK) return s;
+  if ((s = check_sticky()) != SVDQ_OK) return s;
+  return launched(svdq::launch_awq_quantize(N, K, w, codes, scales, zeros, (hipStream_t)stream));
+}
+
 svdq_status awq_w4a16_gemv(int group_size, int64_t M, int64_t N, int64_t K, const void* x,
                            const void* w_codes, const void* w_scales, const void* w_zeros,
                            const void* bias, void* y, void* stream) {

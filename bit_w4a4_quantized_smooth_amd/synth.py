@@ -172,6 +172,29 @@ def mlp_layer(seed: int, M: int, hidden: int, dim: int, rank: int, prec: int = I
     return dict(up=up, down=down)
 
 
+def dense_layer(seed: int, N: int, K: int, Mc: int = 256, planted_rank: int = 32) -> dict:
+    """A dense bf16 weight and a calibration batch for the offline weight side:
+    w = N(0, 0.02^2) noise + a planted rank-`planted_rank` part whose singular values
+    e * (3 + 5 exp(-i/16)) stand well above the noise's largest singular value
+    e = 0.02 (sqrt N + sqrt K) (random orthonormal directions): a weight whose hardest
+    part a low-rank branch can carry; x_cal bf16 [Mc, K] ~ N(0, 1) with 1% of the
+    channels multiplied by 25 (activation outliers); omega fp32 [K, 48] ~ N(0, 1), the
+    test matrix of the randomized range finder (48 = rank 32 + oversampling 16)."""
+    g = _rng(seed, 31)
+    w = g.standard_normal((N, K)) * 0.02
+    if planted_rank:
+        u, _ = np.linalg.qr(_rng(seed, 32).standard_normal((N, planted_rank)))
+        v, _ = np.linalg.qr(_rng(seed, 33).standard_normal((K, planted_rank)))
+        e = 0.02 * (np.sqrt(N) + np.sqrt(K))
+        s = e * (3.0 + 5.0 * np.exp(-np.arange(planted_rank) / 16.0))
+        w += (u * s[None, :]) @ v.T
+    x = _rng(seed, 34).standard_normal((Mc, K))
+    ch = _rng(seed, 35).choice(K, size=max(1, K // 100), replace=False)
+    x[:, ch] *= 25.0
+    omega = _rng(seed, 36).standard_normal((K, 48)).astype(np.float32)
+    return dict(w=to_bf16_bits(w), x_cal=to_bf16_bits(x), omega=omega, N=N, K=K)
+
+
 def awq_layer(seed: int, M: int, N: int, K: int, with_bias: bool = True) -> dict:
     """All inputs of one awq_w4a16 linear: x bf16 ~ N(0,1) [M, K]; unsigned codes
     uniform in 0..15 [N, K]; fp16 scales ~ U(0.005, 0.02) and fp16 zero-points

@@ -205,6 +205,80 @@ svdq_status awq_w4a16_gemv(int group_size, int64_t M, int64_t N, int64_t K, cons
                            const void* w_codes, const void* w_scales, const void* w_zeros,
                            const void* bias, void* y, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Offline weight side (blog "Nunchaku 4-bit inference in Diffusers",
+ * "Background: SVDQuant and Nunchaku": activation outliers move into the
+ * weights, the hardest part of each weight becomes a 16-bit low-rank branch,
+ * the residual is quantized to 4 bits; "Nunchaku Lite", quantization
+ * walkthrough: the checkpoint is produced offline from the dense weights).
+ * ------------------------------------------------------------------------- */
+
+/*
+ * svdq_calibrate_smooth -- the smoothing factor of one linear:
+ *   lambda_k = bf16(sqrt(fl32(a_k / b_k))), a_k = max_m |x_cal[m, k]|,
+ *   b_k = max_n |w[n, k]|; lambda_k = 1 when a_k or b_k is 0
+ * (a migration of strength 1/2 between activations and weights).
+ *   Mc, N, K    calibration rows, weight rows, channels; K even
+ *   x_cal       bf16 [Mc, K] calibration activations
+ *   w           bf16 [N, K] dense weight (nn.Linear layout)
+ *   smooth_out  out bf16 [K]
+ */
+svdq_status svdq_calibrate_smooth(int64_t Mc, int64_t N, int64_t K, const void* x_cal, const void* w,
+                                  void* smooth_out, void* stream);
+
+/* Workspace bytes svdq_lowrank_decompose needs (-1 for unsupported sizes). */
+int64_t svdq_lowrank_workspace_bytes(int64_t N, int64_t K, int rank, int oversample);
+
+/*
+ * svdq_lowrank_decompose -- the 16-bit low-rank branch and the residual:
+ *   W_hat = w diag(smooth) (fp32, exact), so (X / lambda) W_hat^T = X w^T;
+ *   the rank-`rank` approximation of W_hat by randomized subspace iteration
+ *   (Halko, Martinsson and Tropp 2011, Algorithm 4.4): Y = W_hat Omega, then
+ *   `iters` rounds of Z = orth(W_hat^T Q), Q = orth(W_hat Z) (CholeskyQR2), and
+ *   Rayleigh-Ritz on B = Q^T W_hat (eigen-decomposition of B B^T) giving
+ *   W_hat ~ U_r S_r V_r^T;
+ *   l1t = bf16(L1^T), L1 = diag(1/lambda) V_r S_r^(1/2)   [rank, K] (applied to raw X)
+ *   l2t = bf16(L2^T), L2 = S_r^(1/2) U_r^T                [N, rank]
+ *   residual = W_hat - (diag(lambda) L1 L2)^T with the stored bf16 factors, fp32
+ *   [N, K] (what svdq_quantize_weight turns into the 4-bit weight).
+ *   rank        16, 32, 48 or 64; oversample >= 0 with rank + oversample <= 64
+ *               and <= min(N, K); iters 0..64 (more = closer to the exact SVD)
+ *   w           bf16 [N, K]; smooth bf16 [K] or NULL (lambda = 1); K % 64 == 0
+ *   omega       fp32 [K, rank + oversample] test matrix (caller-drawn, e.g.
+ *               standard normal)
+ *   residual    out fp32 [N, K] (also the smoothed-weight workspace)
+ *   work        device workspace of work_bytes >= svdq_lowrank_workspace_bytes()
+ * The outputs depend on omega and on floating-point order; the product
+ * L1 L2 approaches the exact rank-r truncation as iters grows.
+ */
+svdq_status svdq_lowrank_decompose(int64_t N, int64_t K, int rank, int oversample, int iters, const void* w,
+                                   const void* smooth, const float* omega, void* l1t, void* l2t, float* residual,
+                                   void* work, int64_t work_bytes, void* stream);
+
+/*
+ * svdq_quantize_weight -- the 4-bit residual weight, per (row n, group):
+ *   int4 (group 64):  s = fp16_sat(fl32(amax / 7)), q = clamp(rne(fl32(r * fl32(1/s))), -8, 7)
+ *   nvfp4 (group 16): s = e4m3_sat(fl32(amax / fl32(6 * alpha_w))),
+ *                     c = e2m1_sat(fl32(r * fl32(1 / fl32(s * alpha_w))))
+ * (the activation quantizer's steps on an fp32 input, no smoothing).
+ *   residual    fp32 [N, K], K % 64 == 0
+ *   codes       out u8 [N, K/2]; scales out int4: fp16 [N, K/64], nvfp4: E4M3 u8 [N, K/16]
+ */
+svdq_status svdq_quantize_weight(int precision, int group_size, int64_t N, int64_t K, const float* residual,
+                                 float w_global_scale, void* codes, void* scales, void* stream);
+
+/*
+ * awq_quantize_weight -- AWQ int4 weight-only quantization per (row, 64-group),
+ * min-max over a range containing 0: lo = min(0, min w), hi = max(0, max w),
+ * s = fp16(fl32((hi - lo) / 15)), z = clamp(rne(fl32(-lo * fl32(1/s))), 0, 15)
+ * (fp16), q = clamp(rne(fl32(w * fl32(1/s))) + z, 0, 15); all-zero group:
+ * s = z = 0, codes 0.  Output layout as awq_w4a16_gemv consumes it.
+ *   w           bf16 [N, K], K % 64 == 0
+ *   codes out u8 [N, K/2]; scales, zeros out fp16 [N, K/64]
+ */
+svdq_status awq_quantize_weight(int group_size, int64_t N, int64_t K, const void* w, void* codes, void* scales,
+                                void* zeros, void* stream);
+
 /*
  * svdq_w4a4_group_psums -- test support: the per-group partial products of
  * the 4-bit GEMM, P[m,n,g] = sum_{k in g} a_code * w_code, computed by the

@@ -184,3 +184,26 @@ def test_mlp_entry_point_validation(L):
     assert mlp(L, xo=12 * A) == INVALID                # xl1_out aliases scales_out
     L.svdq_test_set_arch_override(b"gfx950")
     assert mlp(L, M=0) == OK
+
+
+def test_offline_entry_points_validation(L):
+    assert L.svdq_calibrate_smooth(64, 128, 256, A, 2 * A, 3 * A, None) == UNSUPPORTED
+    assert L.svdq_calibrate_smooth(64, 128, 255, A, 2 * A, 3 * A, None) == INVALID   # K even
+    assert L.svdq_calibrate_smooth(64, 128, 256, A, 2 * A, A, None) == INVALID       # output aliases x
+    assert L.svdq_lowrank_workspace_bytes(512, 256, 32, 16) > 0
+    assert L.svdq_lowrank_workspace_bytes(512, 256, 32, 40) == -1                    # rank + oversample > 64
+    ws = L.svdq_lowrank_workspace_bytes(512, 256, 32, 16)
+    dec = lambda **k: L.svdq_lowrank_decompose(k.get("N", 512), k.get("K", 256), k.get("rank", 32), k.get("os", 16),
+                                               k.get("it", 4), A, 2 * A, 3 * A, 4 * A, 5 * A, 8 * A, 16 * A,
+                                               k.get("ws", ws), None)
+    assert dec() == UNSUPPORTED
+    assert dec(rank=24) == UNSUPPORTED
+    assert dec(K=200) == INVALID
+    assert dec(ws=ws - 1) == INVALID
+    assert dec(it=-1) == INVALID
+    assert L.svdq_quantize_weight(0, 64, 128, 256, A, 1.0, 2 * A, 3 * A, None) == UNSUPPORTED
+    assert L.svdq_quantize_weight(1, 16, 128, 256, A, 0.0, 2 * A, 3 * A, None) == INVALID
+    assert L.svdq_quantize_weight(0, 16, 128, 256, A, 1.0, 2 * A, 3 * A, None) == UNSUPPORTED
+    assert L.awq_quantize_weight(64, 128, 256, A, 2 * A, 3 * A, 4 * A, None) == UNSUPPORTED
+    assert L.awq_quantize_weight(32, 128, 256, A, 2 * A, 3 * A, 4 * A, None) == UNSUPPORTED
+    assert L.awq_quantize_weight(64, 128, 256, A, A, 3 * A, 4 * A, None) == INVALID
