@@ -378,6 +378,40 @@ def extras(args, torch, sq, synth, t, bf, f16, stream):
         "speedup_vs_unfused": round(unfused_ms / fused_ms, 3)}
     del codes, scales, xl1, wc, ws, l2t, bias, lam_d, l1t_d, outs, y
 
+    # offline weight side at the QKV projection's size (9216 x 3072, rank 32) and the
+    # AWQ modulation weight (18432 x 3072): one call each (they run once per checkpoint)
+    d = synth.dense_layer(1006, 9216, 3072, Mc=4608)
+    w, xc, om = bf(d["w"]), bf(d["x_cal"]), t(d["omega"])
+
+    def once_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    lam = sq.calibrate_smooth(xc, w, stream=stream)
+    cal_ms = once_ms(lambda: sq.calibrate_smooth(xc, w, out=lam, stream=stream))
+    dec = {}
+    dec_ms = once_ms(lambda: dec.update(r=sq.lowrank_decompose(w, lam, om, 32, iters=4, stream=stream)))
+    resid = dec["r"][2]
+    qw_ms = median_ms(lambda i: sq.quantize_weight(sq.SVDQ_INT4, resid, stream=stream), n, stream, torch)
+    wa = bf(synth.dense_layer(1007, 18432, 3072, Mc=16, planted_rank=0)["w"])
+    aq_ms = median_ms(lambda i: sq.awq_quantize_weight(wa, stream=stream), n, stream, torch)
+    qw_bytes = 9216 * 3072 * 4 + 9216 * 3072 // 2 + 9216 * 48 * 2
+    aq_bytes = 18432 * 3072 * 2 + 18432 * 3072 // 2 + 2 * 18432 * 48 * 2
+    res["offline_weight_side"] = {
+        "calibrate_ms_9216x3072_calib4608": round(cal_ms, 4),
+        "lowrank_decompose_ms_9216x3072_r32_it4": round(dec_ms, 3),
+        "quantize_weight_int4_ms": round(qw_ms, 5),
+        "quantize_weight_int4_GBps": round(qw_bytes / (qw_ms * 1e-3) / 1e9, 1),
+        "awq_quantize_18432x3072_ms": round(aq_ms, 5),
+        "awq_quantize_GBps": round(aq_bytes / (aq_ms * 1e-3) / 1e9, 1)}
+    del d, w, xc, om, lam, dec, resid, wa
+
     # AWQ at M=64 over >= 512 MB of weight copies
     d = synth.awq_layer(1005, 64, 18432, 3072)
     A = max(1, args.awq_copies)
