@@ -232,8 +232,314 @@ __global__ __launch_bounds__(QuantCfg<RB>::NT) void quant_act_kernel(
   }
 }
 
+// Second kernel, for ranks 16 and 32 on calls with more 16-row blocks than
+// the device has CUs: the step operands travel through LDS.  Both operands
+// of X.L1 are row-major with rows K*2 bytes apart, so loading them straight
+// in the matrix-core lane layout (lane = row l%16, as the kernel above does)
+// makes every lane of a load touch a different row: one cache access per
+// lane, and the address units saturate.  Here X and L1^T slices are copied
+// global -> LDS with buffer_load ... lds, lanes 8i .. 8i+7 reading one
+// 128-byte row segment (whole-line accesses, no registers), and the lanes
+// then read their fragments from LDS.  Codes and scales are the same
+// function of the inputs as above (the same fp32 steps); XL1 sums its fp32
+// partial products in another fixed order.
+//
+// Workgroup = 32 rows of X (two 16-row blocks) x 8 waves: wave w takes row
+// block w/4 and the steps w%4, w%4 + 4, ... of each chunk, so the two waves
+// of a step lane work on the same steps and share one L1^T slice.  A ring of
+// three LDS slots per wave (X) and per step lane (L1^T) keeps two steps in
+// flight; one barrier per step publishes a slot and frees the oldest.  In LDS
+// the 16-byte pieces of a 128-byte row segment are stored XOR-swizzled by the
+// row (piece p of row i at slot p ^ (i & 7)), so the fragment reads of 16
+// rows spread over the banks.
+namespace dma {
+constexpr int KC = 2048;  // channels per chunk: 32 steps, 8 per step lane
+constexpr int NT = 512;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt with vmcnt = n (0..63), lgkmcnt = 0, expcnt untouched
+#define SVDQ_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0070)
+
+__device__ __forceinline__ int swz(int row, int piece) { return (piece ^ (row & 7)) << 4; }
+
+// 16 bytes per lane, global (buffer offset off) -> LDS at dst + 16 * lane
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t res, uint8_t* dst, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)dst, 16, off, 0, 0, 0);
+}
+}  // namespace dma
+
+template <int PREC, int RB>
+__global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
+    int M, int K, const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
+    const uint16_t* __restrict__ l1t, float alpha, uint8_t* __restrict__ codes,
+    void* __restrict__ scales, float* __restrict__ xl1) {
+  using namespace dma;
+  static_assert(RB <= 2, "LDS holds L1^T slices of at most 32 ranks");
+  constexpr int RBX = RB > 0 ? RB : 1;
+  constexpr int LSL = RBX * 2048;   // bytes of one step's L1^T slice (16*RB rows x 128 B)
+  constexpr int NDMA = 2 + RB;      // copies per wave per step: 2 for X, RB for L1^T (8 rows each)
+  constexpr int kOut = 0x7FFFFFF0;  // offset past num_records: zeros, no memory access
+  constexpr int CROW = KC / 2 + 16; // bytes per codes row in LDS
+  __shared__ __align__(16) float rl[KC];                    // lambda reciprocals of the chunk
+  __shared__ __align__(16) uint8_t ctile[32][CROW];         // codes of the chunk (XL1 partials at the end)
+  __shared__ __align__(16) uint8_t stile[32][KC / 16];      // scales of the chunk
+  __shared__ __align__(16) uint8_t xs0[8][2048], xs1[8][2048], xs2[8][2048];  // X slices per wave
+  __shared__ __align__(16) uint8_t ls0[4][LSL], ls1[4][LSL], ls2[4][LSL];     // L1^T slices per step lane
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rbk = wave >> 2, sl = wave & 3;  // row block, step lane
+  const int row0 = blockIdx.x * 32;
+  const int r = lane & 15, c = lane >> 4;
+  const int m = row0 + 16 * rbk + r;         // this lane's row in the quantization
+
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t lres = __builtin_amdgcn_make_buffer_rsrc((void*)l1t, (short)0, RB * 16 * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t lamres = __builtin_amdgcn_make_buffer_rsrc((void*)lam, (short)0, lam ? K * 2 : 0, 0x00020000);
+  // copy lanes: lane l moves piece (l%8) ^ swizzle of row l/8 of an 8-row group
+  const int cr = lane >> 3;
+  u32 xdo[2], ldo[RBX];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ri = 8 * i + cr;  // row within the 16-row X slice
+    xdo[i] = (u32)(row0 + 16 * rbk + ri) * (u32)K * 2u + (u32)(((lane & 7) ^ (ri & 7)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < RBX; ++i) {
+    const int ri = 8 * (RB * rbk + i) + cr;  // L1^T row: this wave copies rows 8*RB*rbk .. +8*RB
+    ldo[i] = (u32)ri * (u32)K * 2u + (u32)(((lane & 7) ^ (ri & 7)) << 4);
+  }
+
+  v4f acc[RBX];
+#pragma unroll
+  for (int i = 0; i < RBX; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  const float d6 = 6.0f * alpha;
+
+  for (int c0 = 0; c0 < K; c0 += KC) {
+    const int kc = K - c0 < KC ? K - c0 : KC;
+    const int nsteps = kc >> 6;
+    const int nst = nsteps > sl ? (nsteps - sl + 3) >> 2 : 0;  // this step lane's steps
+    const int J = (nsteps + 3) >> 2;                           // rounds (the step lane 0 count)
+
+    // copy local step j of this wave into slot buffers (xb, lb); past the end:
+    // out-of-range offsets (zeros, no memory access), so every wave issues the
+    // same number of copies in every round and the waits count exactly
+    auto issue = [&](int j, uint8_t(*xb)[2048], uint8_t(*lb)[LSL]) __attribute__((always_inline)) {
+      const bool live = j < nst;
+      const u32 sb = 128u * (u32)((c0 >> 6) + sl + 4 * j);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        copy16(xres, xb[wave] + 1024 * i, live ? (int)(xdo[i] + sb) : kOut);
+      if constexpr (RB > 0) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+          copy16(lres, lb[sl] + 1024 * (RB * rbk + i), live ? (int)(ldo[i] + sb) : kOut);
+      }
+    };
+
+    // quantize local step j from slot buffers (xb, lb) and add its X.L1 share
+    auto compute = [&](int j, uint8_t(*xb)[2048], uint8_t(*lb)[LSL]) __attribute__((always_inline)) {
+      const int ls = sl + 4 * j;             // step within the chunk
+      const int k0 = (ls << 6) + (c << 4);   // this lane's first channel within the chunk
+      const uint8_t* xrow = xb[wave] + r * 128;
+      const uint4 va = *(const uint4*)(xrow + swz(r, 2 * c));
+      const uint4 vb = *(const uint4*)(xrow + swz(r, 2 * c + 1));
+      const u32 xw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+      float rk[16];
+      *(float4*)&rk[0] = *(const float4*)&rl[k0];
+      *(float4*)&rk[4] = *(const float4*)&rl[k0 + 4];
+      *(float4*)&rk[8] = *(const float4*)&rl[k0 + 8];
+      *(float4*)&rk[12] = *(const float4*)&rl[k0 + 12];
+      float xh[16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xh[2 * i] = bf16_bits_to_f32(xw[i] & 0xFFFFu) * rk[2 * i];
+        xh[2 * i + 1] = bf16_bits_to_f32(xw[i] >> 16) * rk[2 * i + 1];
+        amax = fmaxf(amax, fmaxf(fabsf(xh[2 * i]), fabsf(xh[2 * i + 1])));
+      }
+      u32 pk0 = 0u, pk1 = 0u;
+      const int trow = 16 * rbk + r;  // row within the workgroup's 32
+      if constexpr (PREC == 0) {
+        amax = max_over_rows(amax);  // one 64-channel group = lanes l, l^16, l^32, l^48
+        const u32 sbits = f32_to_f16_sat_bits(amax / 7.0f);
+        const float sf = f16_bits_to_f32(sbits);
+        const float t = sf == 0.0f ? 0.0f : 1.0f / sf;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float q = __builtin_rintf(xh[i] * t);
+          q = fminf(fmaxf(q, -8.0f), 7.0f);
+          const u32 nib = (u32)(int)q & 0xFu;
+          if (i < 8) pk0 |= nib << (4 * i);
+          else pk1 |= nib << (4 * (i - 8));
+        }
+        if (c == 0) *(uint16_t*)(&stile[trow][2 * ls]) = (uint16_t)sbits;
+      } else {
+        // one 16-channel group = this lane's 16 channels
+        const u32 sbits = f32_to_e4m3_sat_pos(amax / d6);
+        const float sf = e4m3_to_f32(sbits);
+        float t = 0.0f;
+        if (sf != 0.0f) {
+          const float sa = sf * alpha;
+          t = 1.0f / sa;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const u32 nib = sf == 0.0f ? 0u : f32_to_e2m1_sat(xh[i] * t);
+          if (i < 8) pk0 |= nib << (4 * i);
+          else pk1 |= nib << (4 * (i - 8));
+        }
+        stile[trow][4 * ls + c] = (uint8_t)sbits;
+      }
+      *(uint2*)(&ctile[trow][k0 >> 1]) = uint2{pk0, pk1};
+      if constexpr (RB > 0) {
+        // XL1 += X[16 rows, these 64 channels] . L1[these channels, 16*RB]
+        const v8bf a0 = __builtin_bit_cast(v8bf, va);
+        const v8bf a1 = __builtin_bit_cast(v8bf, vb);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int lr = rb * 16 + r;  // L1^T row = rank
+          const uint8_t* lrow = lb[sl] + lr * 128;
+          const uint4 b0 = *(const uint4*)(lrow + swz(lr, 2 * c));
+          const uint4 b1 = *(const uint4*)(lrow + swz(lr, 2 * c + 1));
+          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, b0), acc[rb], 0, 0, 0);
+          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, b1), acc[rb], 0, 0, 0);
+        }
+      }
+    };
+
+    // the first two steps in flight while the reciprocal table is built
+    issue(0, xs0, ls0);
+    issue(1, xs1, ls1);
+    if (tid * 8 < kc) {
+      const uint4 lv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lamres, (c0 + tid * 8) * 2, 0, 0));
+      const u32 w4[4] = {lv.x, lv.y, lv.z, lv.w};
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = lam ? 1.0f / bf16_bits_to_f32(w4[e] & 0xFFFFu) : 1.0f;
+        o[2 * e + 1] = lam ? 1.0f / bf16_bits_to_f32(w4[e] >> 16) : 1.0f;
+      }
+      *(float4*)&rl[tid * 8] = float4{o[0], o[1], o[2], o[3]};
+      *(float4*)&rl[tid * 8 + 4] = float4{o[4], o[5], o[6], o[7]};
+    }
+
+    // Round j: wait for this wave's copies of step j (the NDMA copies of
+    // step j+1 may stay in flight) and its LDS reads, barrier (every wave's
+    // copies of step j have landed; every wave is done with the slot of step
+    // j-1), refill that slot with step j+2, compute step j.
+    auto round = [&](int j, uint8_t(*xa)[2048], uint8_t(*la)[LSL], uint8_t(*xc)[2048], uint8_t(*lc)[LSL])
+        __attribute__((always_inline)) {
+      SVDQ_WAIT_VM_LGKM0(NDMA);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(j + 2, xc, lc);
+      if (j < nst) compute(j, xa, la);  // wave-uniform
+    };
+    int j = 0;
+    for (; j + 3 <= J; j += 3) {
+      round(j, xs0, ls0, xs2, ls2);
+      round(j + 1, xs1, ls1, xs0, ls0);
+      round(j + 2, xs2, ls2, xs1, ls1);
+    }
+    if (j < J) round(j, xs0, ls0, xs2, ls2);
+    if (j + 1 < J) round(j + 1, xs1, ls1, xs0, ls0);
+    __syncthreads();  // every copy and every code and scale of the chunk in LDS
+
+    // the chunk's codes and scales out: LDS reads first, then the stores
+    {
+      const int cpr = kc >> 5;  // 16-byte code pieces per row
+      constexpr int CIT = 32 * (KC / 32) / NT;
+      uint4 cv[CIT];
+      int cdst[CIT];
+#pragma unroll
+      for (int i = 0; i < CIT; ++i) {
+        const int idx = tid + NT * i;
+        const int rr = idx / cpr, off = (idx - rr * cpr) << 4;
+        const bool ok = idx < 32 * cpr && row0 + rr < M;
+        cv[i] = ok ? *(const uint4*)(&ctile[rr][off]) : uint4{0u, 0u, 0u, 0u};
+        cdst[i] = ok ? (row0 + rr) * (K >> 1) + (c0 >> 1) + off : -1;
+      }
+      const int sb = PREC == 0 ? 2 * (kc >> 6) : (kc >> 4);   // scale bytes of the chunk per row (even)
+      const int sbr = PREC == 0 ? 2 * (K >> 6) : (K >> 4);    // scale bytes per row
+      const int s0b = PREC == 0 ? 2 * (c0 >> 6) : (c0 >> 4);  // first scale byte of the chunk
+      constexpr int SIT = 32 * ((PREC == 0 ? 2 * (KC >> 6) : (KC >> 4)) / 2) / NT;
+      uint16_t sv[SIT];
+      int sdst[SIT];
+#pragma unroll
+      for (int i = 0; i < SIT; ++i) {
+        const int idx = tid + NT * i;
+        const int rr = idx / (sb >> 1), off = (idx - rr * (sb >> 1)) << 1;
+        const bool ok = idx < 32 * (sb >> 1) && row0 + rr < M;
+        sv[i] = ok ? *(const uint16_t*)(&stile[rr][off]) : (uint16_t)0;
+        sdst[i] = ok ? (row0 + rr) * sbr + s0b + off : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < CIT; ++i)
+        if (cdst[i] >= 0) *(uint4*)(codes + cdst[i]) = cv[i];
+#pragma unroll
+      for (int i = 0; i < SIT; ++i)
+        if (sdst[i] >= 0) *(uint16_t*)((uint8_t*)scales + sdst[i]) = sv[i];
+    }
+    __syncthreads();  // rl, ctile, stile and the slots are rewritten by the next chunk
+  }
+
+  if constexpr (RB > 0) {
+    constexpr int R = RB * 16;
+    // per-wave partial XL1 tiles [16 rows][R] in the codes tile (free now),
+    // summed over the four step lanes of each row block in a fixed order;
+    // lane holds D[row 4*(lane/16) + v][col lane%16] of each 16x16 block
+    float* red = (float*)&ctile[0][0];
+    static_assert(8 * 16 * R * 4 <= 32 * CROW, "partial XL1 tiles fit in the codes tile");
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * c + v) * R + rb * 16 + r] = acc[rb][v];
+    __syncthreads();
+    for (int idx = tid; idx < 32 * R; idx += NT) {
+      const int rr = idx / R, col = idx - rr * R;  // row within the 32
+      const int b = rr >> 4, ri = rr & 15;
+      float sum = red[((4 * b) * 16 + ri) * R + col];
+#pragma unroll
+      for (int s2 = 1; s2 < 4; ++s2) sum += red[((4 * b + s2) * 16 + ri) * R + col];  // fixed order
+      if (row0 + rr < M) xl1[(size_t)(row0 + rr) * R + col] = sum;
+    }
+  }
+}
+
+template <int PREC, int RB>
+static hipError_t launch_quant_dma(const QuantArgs& a, hipStream_t st) {
+  const int blocks = (int)((a.M + 31) / 32);
+  hipLaunchKernelGGL((quant_act_dma_kernel<PREC, RB>), dim3(blocks), dim3(dma::NT), 0, st, (int)a.M, (int)a.K,
+                     (const uint16_t*)a.x, (const uint16_t*)a.smooth, (const uint16_t*)a.l1t,
+                     a.alpha, (uint8_t*)a.codes, a.scales, a.xl1);
+  return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <int PREC, int RB>
 static hipError_t launch_quant(const QuantArgs& a, hipStream_t st) {
+  // int4 with ranks 16 / 32: once the 16-row workgroups of the kernel above
+  // no longer fit one per CU, the LDS-staged kernel (32 rows per workgroup,
+  // coalesced copies) is faster; below that the one-row-block workgroups
+  // keep every CU busy.  nvfp4 stays on the kernel above (its per-step
+  // arithmetic, not the loads, sets the pace there).
+  if constexpr (PREC == 0 && (RB == 1 || RB == 2)) {
+    if ((a.M + 15) / 16 > device_cus()) return launch_quant_dma<PREC, RB>(a, st);
+  }
   const size_t red = RB > 0 ? (size_t)QuantCfg<RB>::WAVES * 16 * RB * 16 : 0;
   const size_t lds = sizeof(float) * ((size_t)a.K > red ? (size_t)a.K : red);
   auto kern = quant_act_kernel<PREC, RB>;

@@ -124,7 +124,7 @@ svdq_status svdq_quantize_act(int precision, int group_size, int rank, int64_t M
   if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxDim) return fail(SVDQ_ERR_INVALID_ARG, "bad shape M=%lld K=%lld", (long long)M, (long long)K);
   if (K % 64 != 0) return fail(SVDQ_ERR_UNSUPPORTED, "K=%lld must be a multiple of 64", (long long)K);
   if (K > 32768) return fail(SVDQ_ERR_UNSUPPORTED, "K=%lld above the supported 32768", (long long)K);
-  if (M * K > ((int64_t)1 << 31)) return fail(SVDQ_ERR_UNSUPPORTED, "M*K above 2^31");
+  if (M * K >= ((int64_t)1 << 30)) return fail(SVDQ_ERR_UNSUPPORTED, "M*K above 2^30 - 1 (x must stay below 2 GiB)");
   if (M == 0) return ok();  // empty call: nothing to read or write
   if (!x || !act_codes || !act_scales) return fail(SVDQ_ERR_INVALID_ARG, "x, act_codes and act_scales are required");
   if ((rank > 0) != (l1t != nullptr)) return fail(SVDQ_ERR_INVALID_ARG, "l1t must be given iff rank > 0");
@@ -424,6 +424,7 @@ svdq_status awq_w4a16_gemv(int group_size, int64_t M, int64_t N, int64_t K, cons
   if (K % 64 != 0) return fail(SVDQ_ERR_UNSUPPORTED, "K=%lld must be a multiple of 64", (long long)K);
   if (N % 64 != 0) return fail(SVDQ_ERR_UNSUPPORTED, "N=%lld must be a multiple of 64", (long long)N);
   if (N * K > ((int64_t)1 << 31)) return fail(SVDQ_ERR_UNSUPPORTED, "N*K above 2^31");
+  if (M * K >= ((int64_t)1 << 30)) return fail(SVDQ_ERR_UNSUPPORTED, "M*K above 2^30 - 1 (x must stay below 2 GiB)");
   if (M == 0) return ok();  // empty call: nothing to read or write
   if (!x || !w_codes || !w_scales || !w_zeros || !y)
     return fail(SVDQ_ERR_INVALID_ARG, "x, w_codes, w_scales, w_zeros and y are required");

@@ -73,7 +73,7 @@ typedef enum { SVDQ_INT4 = 0, SVDQ_NVFP4 = 1 } svdq_precision;
  *
  *   precision   SVDQ_INT4 (group_size must be 64) or SVDQ_NVFP4 (16)
  *   rank        0, 16, 32, ..., 128; 0 disables the low-rank branch
- *   M, K        rows and channels; K % 64 == 0, K <= 32768
+ *   M, K        rows and channels; K % 64 == 0, K <= 32768, M*K < 2^30
  *   x           bf16 [M, K]
  *   smooth      bf16 [K] smoothing factors lambda (finite, > 0), or NULL for 1
  *   l1t         bf16 [rank, K] (L1 transposed); NULL iff rank == 0
@@ -193,7 +193,7 @@ svdq_status svdq_w4a4_gemm_gelu_quant(int precision, int group_size, int rank, i
  *   y[m,n] = sum_g sum_{k in g} x[m,k] * (q[n,k] - z[n,g]) * s[n,g] + bias[n]
  *
  *   group_size  64
- *   M, N, K     0 <= M <= 64; N % 64 == 0; K % 64 == 0
+ *   M, N, K     0 <= M <= 64; N % 64 == 0; K % 64 == 0; M*K < 2^30
  *   x           bf16 [M, K]
  *   w_codes     u8 [N, K/2], unsigned codes 0..15
  *   w_scales    fp16 [N, K/64]

@@ -90,6 +90,13 @@ def test_rank_and_shape_limits(L):
     assert gemm(L, N=0) == INVALID
     assert awq(L, M=65) == UNSUPPORTED
     assert awq(L, N=96) == UNSUPPORTED
+    # x stays below 2 GiB (32-bit buffer ranges): M*K < 2^30
+    assert q(L, M=1 << 15, K=1 << 15) == UNSUPPORTED and b"2^30" in L.svdq_last_error()
+    q(L, M=(1 << 15) - 1, K=1 << 15)
+    assert b"2^30" not in L.svdq_last_error()
+    assert awq(L, M=64, N=64, K=1 << 24) == UNSUPPORTED and b"2^30" in L.svdq_last_error()
+    awq(L, M=63, N=64, K=1 << 24)
+    assert b"2^30" not in L.svdq_last_error()
 
 
 def test_required_pointers(L):

@@ -155,6 +155,26 @@ def test_linear_end_to_end_small(small):
     assert max_abs_rel(y, ref) <= Y_TOL
 
 
+# --------------------------------------------------------------------------- quantizer, many rows
+# int4 with ranks 16 / 32 on more 16-row blocks than the device has CUs goes to
+# the LDS-staged quantizer (32 rows per workgroup, 2048-channel chunks): the
+# DiT attention input, ragged rows and channels (a partial last workgroup, a
+# partial last chunk, a one-step chunk) and a single 64-channel step.
+MANY_ROWS = {
+    "int4_4608x3072_r32": lambda: synth.svdq_layer(1002, 4608, 128, 3072, 32, synth.INT4, 0.005, 30.0),
+    "int4_ragged_4100x4160_r16": lambda: synth.svdq_layer(31, 4100, 128, 4160, 16, synth.INT4, 0.02, 30.0),
+    "int4_ragged_4130x2112_r32": lambda: synth.svdq_layer(32, 4130, 128, 2112, 32, synth.INT4, 0.02, 30.0),
+    "int4_4200x64_r32": lambda: synth.svdq_layer(33, 4200, 128, 64, 32, synth.INT4, 0.02, 30.0),
+    "nvfp4_4608x3072_r32": lambda: synth.svdq_layer(1004, 4608, 128, 3072, 32, synth.NVFP4, 0.005, 30.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MANY_ROWS))
+def test_quantize_many_rows(name):
+    print(f"[parity] quantize {name}", flush=True)
+    check_quant(MANY_ROWS[name]())
+
+
 # --------------------------------------------------------------------------- quantizer edge cases
 def _bits(a):
     return synth.to_bf16_bits(np.asarray(a, np.float64))
