@@ -101,7 +101,7 @@ __device__ __forceinline__ uint4 nib_hi16(uint4 v) {  // 16*q of odd channels
 // attention projection (Q/K RMSNorm and rotary embedding in the epilogue);
 // 3: fused MLP up-projection (no Y: GELU, then the down projection's
 // quantization and low-rank input)
-template <int MODE>
+template <int MODE, bool SCD>
 __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
     int M, int N, int K, int rank, const uint8_t* __restrict__ ac, const uint16_t* __restrict__ as,
     const uint8_t* __restrict__ wc, const uint16_t* __restrict__ ws, const float* __restrict__ xl1,
@@ -177,16 +177,30 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
     for (int r = 0; r < CHUNKS; ++r)
       rc[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r < WCH ? wres : xres, coff[r] + kbyte, 0, 0));
     if constexpr (MODE != 1) {
+      if constexpr (KG == 2 && SCD) {
+        // both groups' fp16 scales of a row are adjacent and 4-byte aligned
+        // (even group count): one dword per row instead of two shorts
 #pragma unroll
-      for (int r = 0; r < SROWS; ++r) {
-#pragma unroll
-        for (int gg = 0; gg < KG; ++gg) {
-          const int g = s * KG + gg;
-          uint32_t h = 0u;
+        for (int r = 0; r < SROWS; ++r) {
+          const int g = s * KG;
+          uint32_t v = 0u;
           if (s_live[r] && g < G)  // wave-uniform
-            h = s_is_w[r] ? __builtin_amdgcn_raw_buffer_load_b16(wsres, soff[r] + 2 * g, 0, 0)
-                          : __builtin_amdgcn_raw_buffer_load_b16(asres, soff[r] + 2 * g, 0, 0);
-          rs[r][gg] = h;
+            v = s_is_w[r] ? __builtin_amdgcn_raw_buffer_load_b32(wsres, soff[r] + 2 * g, 0, 0)
+                          : __builtin_amdgcn_raw_buffer_load_b32(asres, soff[r] + 2 * g, 0, 0);
+          rs[r][0] = v;  // both groups: split at the LDS store
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < SROWS; ++r) {
+#pragma unroll
+          for (int gg = 0; gg < KG; ++gg) {
+            const int g = s * KG + gg;
+            uint32_t h = 0u;
+            if (s_live[r] && g < G)  // wave-uniform
+              h = s_is_w[r] ? __builtin_amdgcn_raw_buffer_load_b16(wsres, soff[r] + 2 * g, 0, 0)
+                            : __builtin_amdgcn_raw_buffer_load_b16(asres, soff[r] + 2 * g, 0, 0);
+            rs[r][gg] = h;
+          }
         }
       }
     }
@@ -205,8 +219,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
       for (int r = 0; r < SROWS; ++r) {
         const int row = tid + NT * r;
         if (s_live[r]) {
+          if constexpr (KG == 2 && SCD) {
+            ssc[buf * SC_STAGE + row] = f16_bits_to_f32(rs[r][0] & 0xFFFFu);
+            ssc[buf * SC_STAGE + NROWS + row] = f16_bits_to_f32(rs[r][0] >> 16);
+          } else {
 #pragma unroll
-          for (int gg = 0; gg < KG; ++gg) ssc[buf * SC_STAGE + gg * NROWS + row] = f16_bits_to_f32(rs[r][gg]);
+            for (int gg = 0; gg < KG; ++gg) ssc[buf * SC_STAGE + gg * NROWS + row] = f16_bits_to_f32(rs[r][gg]);
+          }
         }
       }
     }
@@ -655,10 +674,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
 hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
   const int m_tiles = (int)((a.M + BM - 1) / BM);
   const int blocks = m_tiles * (int)((a.N + BN - 1) / BN);
-  auto k0 = gemm_int4_kernel<0>;
-  auto k1 = gemm_int4_kernel<1>;
-  auto k2 = gemm_int4_kernel<2>;
-  auto k3 = gemm_int4_kernel<3>;
+  // an even group count puts both groups' scales of a stage in one aligned dword
+  const bool scd = (a.K / 64) % 2 == 0;
+  auto k0 = scd ? gemm_int4_kernel<0, true> : gemm_int4_kernel<0, false>;
+  auto k1 = gemm_int4_kernel<1, false>;
+  auto k2 = scd ? gemm_int4_kernel<2, true> : gemm_int4_kernel<2, false>;
+  auto k3 = scd ? gemm_int4_kernel<3, true> : gemm_int4_kernel<3, false>;
   const void* kf = a.psums ? (const void*)k1 : a.qkv ? (const void*)k2 : a.mlp ? (const void*)k3 : (const void*)k0;
   hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
   if (e != hipSuccess) return e;
