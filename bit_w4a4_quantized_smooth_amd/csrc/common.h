@@ -74,6 +74,37 @@ __device__ __forceinline__ uint32_t f32_to_e2m1_sat(float v) {
   return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
+// fl32(a / 7) for every non-negative finite a, without a division: q0 =
+// fl32(a * fl32(1/7)), the residual a - 7 q0 exactly by an fma, then one fma
+// correction.  Equal to the IEEE quotient for all 2^31 - 2^23 such a,
+// subnormals included (checked exhaustively by tests/test_div7_exhaustive.py).
+// a = +inf gives NaN, which the saturating fp16 conversion of the int4 scale
+// maps to 65504 as it does inf.
+__device__ __forceinline__ float div7_rn(float a) {
+  const float r7 = 0.142857149f;  // fl32(1/7)
+  const float q0 = __fmul_rn(a, r7);
+  const float r = __builtin_fmaf(-q0, 7.0f, a);
+  return __builtin_fmaf(r, r7, q0);
+}
+
+// Eight int4 codes q_i = clamp(rne(fl32(v_i * t)), -8, 7) as two's complement
+// nibbles of one word (code i in bits 4i .. 4i+3).  Clamping to the integer
+// bounds first gives the same result as clamping after rounding; then one add
+// of 2^23 + 8 rounds (ties to even: the even offset keeps the parity) and
+// leaves q + 8 in 0..15 as the low bits of the sum's bit pattern, with only
+// exponent bits above them; those shift out for codes 2..7 and are masked
+// for codes 0 and 1; one xor with 8 per nibble turns q + 8 into q's nibble.
+__device__ __forceinline__ uint32_t int4_codes8(const float* v, float t) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float c = __builtin_amdgcn_fmed3f(__fmul_rn(v[i], t), -8.0f, 7.0f);
+    const uint32_t b = __float_as_uint(__fadd_rn(c, 8388616.0f));  // 2^23 + 8 + rne(c)
+    w |= (i < 2 ? (b & 0xFu) : b) << (4 * i);
+  }
+  return w ^ 0x88888888u;
+}
+
 // ---- lane helpers ------------------------------------------------------------
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, 64);

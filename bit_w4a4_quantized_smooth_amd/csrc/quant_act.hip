@@ -162,17 +162,11 @@ __global__ __launch_bounds__(QuantCfg<RB>::NT) void quant_act_kernel(
       u32 pk0 = 0u, pk1 = 0u;
       if constexpr (PREC == 0) {
         amax = max_over_rows(amax);  // one 64-channel group = lanes l, l^16, l^32, l^48
-        const u32 sbits = f32_to_f16_sat_bits(amax / 7.0f);
+        const u32 sbits = f32_to_f16_sat_bits(div7_rn(amax));
         const float sf = f16_bits_to_f32(sbits);
         const float t = sf == 0.0f ? 0.0f : 1.0f / sf;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float q = __builtin_rintf(xh[i] * t);
-          q = fminf(fmaxf(q, -8.0f), 7.0f);
-          const u32 nib = (u32)(int)q & 0xFu;
-          if (i < 8) pk0 |= nib << (4 * i);
-          else pk1 |= nib << (4 * (i - 8));
-        }
+        pk0 = int4_codes8(xh, t);
+        pk1 = int4_codes8(xh + 8, t);
         if (valid) {
           *(uint2*)(codes + (size_t)m * (K >> 1) + (k0 >> 1)) = uint2{pk0, pk1};
           if (c == 0) ((uint16_t*)scales)[(size_t)m * (K >> 6) + st] = (uint16_t)sbits;
@@ -362,17 +356,11 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
       const int trow = 16 * rbk + r;  // row within the workgroup's 32
       if constexpr (PREC == 0) {
         amax = max_over_rows(amax);  // one 64-channel group = lanes l, l^16, l^32, l^48
-        const u32 sbits = f32_to_f16_sat_bits(amax / 7.0f);
+        const u32 sbits = f32_to_f16_sat_bits(div7_rn(amax));
         const float sf = f16_bits_to_f32(sbits);
         const float t = sf == 0.0f ? 0.0f : 1.0f / sf;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float q = __builtin_rintf(xh[i] * t);
-          q = fminf(fmaxf(q, -8.0f), 7.0f);
-          const u32 nib = (u32)(int)q & 0xFu;
-          if (i < 8) pk0 |= nib << (4 * i);
-          else pk1 |= nib << (4 * (i - 8));
-        }
+        pk0 = int4_codes8(xh, t);
+        pk1 = int4_codes8(xh + 8, t);
         if (c == 0) *(uint16_t*)(&stile[trow][2 * ls]) = (uint16_t)sbits;
       } else {
         // one 16-channel group = this lane's 16 channels
