@@ -421,12 +421,7 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(int N, int K, cons
       tt = 1.0f / sa;
     }
 #pragma unroll
-    for (int i = 0; i < G; i += 8) {
-      u32 w = 0u;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w |= (s == 0.f ? 0u : f32_to_e2m1_sat(v[i + e] * tt)) << (4 * e);
-      *(u32*)(dst + i / 2) = w;
-    }
+    for (int i = 0; i < G; i += 8) *(u32*)(dst + i / 2) = s == 0.f ? 0u : e2m1_codes8(v + i, tt);
   }
 }
 

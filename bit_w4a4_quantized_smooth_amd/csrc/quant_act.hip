@@ -180,12 +180,9 @@ __global__ __launch_bounds__(QuantCfg<RB>::NT) void quant_act_kernel(
           const float sa = sf * alpha;
           t = 1.0f / sa;
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const u32 nib = sf == 0.0f ? 0u : f32_to_e2m1_sat(xh[i] * t);
-          if (i < 8) pk0 |= nib << (4 * i);
-          else pk1 |= nib << (4 * (i - 8));
-        }
+        // a zero scale writes code 0 (t = 0 would give -0 codes for negative xh)
+        pk0 = sf == 0.0f ? 0u : e2m1_codes8(xh, t);
+        pk1 = sf == 0.0f ? 0u : e2m1_codes8(xh + 8, t);
         if (valid) {
           *(uint2*)(codes + (size_t)m * (K >> 1) + (k0 >> 1)) = uint2{pk0, pk1};
           ((uint8_t*)scales)[(size_t)m * (K >> 4) + (st << 2) + c] = (uint8_t)sbits;
@@ -371,12 +368,9 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
           const float sa = sf * alpha;
           t = 1.0f / sa;
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const u32 nib = sf == 0.0f ? 0u : f32_to_e2m1_sat(xh[i] * t);
-          if (i < 8) pk0 |= nib << (4 * i);
-          else pk1 |= nib << (4 * (i - 8));
-        }
+        // a zero scale writes code 0 (t = 0 would give -0 codes for negative xh)
+        pk0 = sf == 0.0f ? 0u : e2m1_codes8(xh, t);
+        pk1 = sf == 0.0f ? 0u : e2m1_codes8(xh + 8, t);
         stile[trow][4 * ls + c] = (uint8_t)sbits;
       }
       *(uint2*)(&ctile[trow][k0 >> 1]) = uint2{pk0, pk1};

@@ -197,12 +197,29 @@ def _edge_case(prec, kind):
     elif kind == "zeros":
         x = np.zeros((M, K))
         x[1::2, :G] = rng.standard_normal((M // 2, G))
-    return dict(prec=prec, x=_bits(x), lam=None, rank=0, alpha_a=1.0 if prec == sq.SVDQ_INT4 else
+    elif kind == "grid":
+        # E2M1 values and the midpoints between them, both signs, and signed
+        # zeros, times a power-of-two scale s per group whose first entry is
+        # 6 s: with alpha = 1 the NVFP4 scale is s exactly and x / s is exact,
+        # so every code decision is a tie or an exact grid point.  Rows 0 mod 5
+        # hold groups of -0 only (scale 0: code 0, not the negative zero).
+        mags = np.array([0.0, 0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0])
+        s = 2.0 ** rng.integers(-6, 8, size=(M, K // G))
+        x = rng.choice(mags, size=(M, K)) * np.where(rng.random((M, K)) < 0.5, -1.0, 1.0)
+        x[:, ::G] = 6.0 * np.where(rng.random((M, K // G)) < 0.5, -1.0, 1.0)
+        x = x * np.repeat(s, G, axis=1)
+        x[::5, :] = -0.0
+    elif kind == "inf":
+        x = rng.standard_normal((M, K))
+        x[rng.random((M, K)) < 0.01] = np.inf
+        x[rng.random((M, K)) < 0.01] = -np.inf
+    fixed_alpha = prec == sq.SVDQ_INT4 or kind in ("grid", "inf")
+    return dict(prec=prec, x=_bits(x), lam=None, rank=0, alpha_a=1.0 if fixed_alpha else
                 synth.nvfp4_act_global_scale(_bits(x), None), l1t=np.zeros((0, K), np.uint16))
 
 
 @pytest.mark.parametrize("prec", [sq.SVDQ_INT4, sq.SVDQ_NVFP4])
-@pytest.mark.parametrize("kind", ["ties", "tiny", "huge", "zeros"])
+@pytest.mark.parametrize("kind", ["ties", "tiny", "huge", "zeros", "grid", "inf"])
 def test_quantize_edge_cases(prec, kind):
     print(f"[parity] quantize edge {kind} prec {prec}", flush=True)
     check_quant(_edge_case(prec, kind), smooth=False)
