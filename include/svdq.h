@@ -74,7 +74,9 @@ typedef enum { SVDQ_INT4 = 0, SVDQ_NVFP4 = 1 } svdq_precision;
  *   precision   SVDQ_INT4 (group_size must be 64) or SVDQ_NVFP4 (16)
  *   rank        0, 16, 32, ..., 128; 0 disables the low-rank branch
  *   M, K        rows and channels; K % 64 == 0, K <= 32768, M*K < 2^30
- *   x           bf16 [M, K]
+ *   x           bf16 [M, K]; +-inf quantizes to the saturated code of its sign
+ *               (int4 -8 / 7, nvfp4 -6 / 6) and counts as the group's maximum;
+ *               codes and scales of a group holding a NaN are unspecified
  *   smooth      bf16 [K] smoothing factors lambda (finite, > 0), or NULL for 1
  *   l1t         bf16 [rank, K] (L1 transposed); NULL iff rank == 0
  *   act_global_scale  NVFP4 per-tensor scale alpha > 0 (static); ignored for int4
