@@ -282,7 +282,6 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
   const int rbk = wave >> 2, sl = wave & 3;  // row block, step lane
   const int row0 = blockIdx.x * 32;
   const int r = lane & 15, c = lane >> 4;
-  const int m = row0 + 16 * rbk + r;         // this lane's row in the quantization
 
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t lres = __builtin_amdgcn_make_buffer_rsrc((void*)l1t, (short)0, RB * 16 * K * 2, 0x00020000);
@@ -514,12 +513,11 @@ static int device_cus() {
 
 template <int PREC, int RB>
 static hipError_t launch_quant(const QuantArgs& a, hipStream_t st) {
-  // int4 with ranks 16 / 32: once the 16-row workgroups of the kernel above
-  // no longer fit one per CU, the LDS-staged kernel (32 rows per workgroup,
-  // coalesced copies) is faster; below that the one-row-block workgroups
-  // keep every CU busy.  nvfp4 stays on the kernel above (its per-step
-  // arithmetic, not the loads, sets the pace there).
-  if constexpr (PREC == 0 && (RB == 1 || RB == 2)) {
+  // Ranks 16 / 32: once the 16-row workgroups of the kernel above no longer
+  // fit one per CU, the LDS-staged kernel (32 rows per workgroup, coalesced
+  // copies) is faster, for both precisions; below that the one-row-block
+  // workgroups keep every CU busy.
+  if constexpr (RB == 1 || RB == 2) {
     if ((a.M + 15) / 16 > device_cus()) return launch_quant_dma<PREC, RB>(a, st);
   }
   const size_t red = RB > 0 ? (size_t)QuantCfg<RB>::WAVES * 16 * RB * 16 : 0;
