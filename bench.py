@@ -20,7 +20,7 @@ is the HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE
 counter summary, reported only while the kernel source still matches the
 hash recorded there.
 
-Prints one JSON line.  --gpus above 1 exits: this build measures one GPU.
+Prints one JSON line.  --gpus above 1 exits with a message: the benchmark runs on one GPU.
 """
 import argparse
 import hashlib
@@ -111,8 +111,9 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(each box has a single MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the linear shards "
+              "on tokens with no communication, so each GPU would repeat this one-GPU step)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
