@@ -20,10 +20,15 @@
 // 1/4) for the partial-product test mode.
 //
 // Tiling: 128(n) x 128(m) per 256-thread workgroup, wave tiles of 64x64,
-// K steps of 64 channels (four NVFP4 groups) double buffered in LDS; the
-// next step's codes and scales are loaded (branch-free buffer loads, rows
-// past M read as zero) while the current step computes.  Tiles are assigned
+// K steps of 64 channels (four NVFP4 groups) double buffered in LDS; codes
+// and scales are loaded two steps ahead into two register sets (branch-free
+// buffer loads, rows past M read as zero), and scheduling barriers keep the
+// loads at the top of a step and their expansion into LDS at its end (left
+// to itself the compiler moves the expansion up to the loads, which makes
+// the step wait for them at once).  Tiles are assigned
 // so that each XCD works on a contiguous part of a banded order.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "qkv_epi.h"
@@ -100,40 +105,53 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  uint4 wv, xv;
-  u32 wsb = 0x3838u, xsb = 0x3838u;  // two E4M3 scales (1.0, 1.0 in test mode)
-  auto gload = [&](int st) {
-    wv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, woff + st * 32, 0, 0));
-    xv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff + st * 32, 0, 0));
+  // Two register sets: the loads for stage st + 2 are issued at the start of
+  // stage st, while the set loaded one stage earlier is expanded into LDS at
+  // its end.  Loads of stages past the end use an offset beyond every
+  // buffer's range (they return zeros without touching memory), so every
+  // stage issues the same loads and the waits stay exact.
+  constexpr int kOffOut = 0x7FFFFFF0;
+  uint4 wv[2], xv[2];
+  u32 wsb[2] = {0x3838u, 0x3838u}, xsb[2] = {0x3838u, 0x3838u};  // two E4M3 scales (1.0, 1.0 in test mode)
+  auto gload = [&](int st, auto setc) {
+    constexpr int set = decltype(setc)::value;
+    const bool live = st < steps;
+    wv[set] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, live ? woff + st * 32 : kOffOut, 0, 0));
+    xv[set] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, live ? xoff + st * 32 : kOffOut, 0, 0));
     if constexpr (MODE != 1) {
-      wsb = __builtin_amdgcn_raw_buffer_load_b16(wsres, wsoff + st * 4, 0, 0);
-      xsb = __builtin_amdgcn_raw_buffer_load_b16(asres, xsoff + st * 4, 0, 0);
+      wsb[set] = __builtin_amdgcn_raw_buffer_load_b16(wsres, live ? wsoff + st * 4 : kOffOut, 0, 0);
+      xsb[set] = __builtin_amdgcn_raw_buffer_load_b16(asres, live ? xsoff + st * 4 : kOffOut, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, auto setc) {
+    constexpr int set = decltype(setc)::value;
     h2 w0, w1, x0, x1;
-    scale_pairs(wsb, w0, w1);
-    scale_pairs(xsb, x0, x1);
+    scale_pairs(wsb[set], w0, w1);
+    scale_pairs(xsb[set], x0, x1);
     uint16_t* dw = &sW[buf][srow * ROW + shalf * 32];
-    *(uint4*)(dw + 0) = dequant8(wv.x, w0);
-    *(uint4*)(dw + 8) = dequant8(wv.y, w0);
-    *(uint4*)(dw + 16) = dequant8(wv.z, w1);
-    *(uint4*)(dw + 24) = dequant8(wv.w, w1);
+    *(uint4*)(dw + 0) = dequant8(wv[set].x, w0);
+    *(uint4*)(dw + 8) = dequant8(wv[set].y, w0);
+    *(uint4*)(dw + 16) = dequant8(wv[set].z, w1);
+    *(uint4*)(dw + 24) = dequant8(wv[set].w, w1);
     uint16_t* dx = &sX[buf][srow * ROW + shalf * 32];
-    *(uint4*)(dx + 0) = dequant8(xv.x, x0);
-    *(uint4*)(dx + 8) = dequant8(xv.y, x0);
-    *(uint4*)(dx + 16) = dequant8(xv.z, x1);
-    *(uint4*)(dx + 24) = dequant8(xv.w, x1);
+    *(uint4*)(dx + 0) = dequant8(xv[set].x, x0);
+    *(uint4*)(dx + 8) = dequant8(xv[set].y, x0);
+    *(uint4*)(dx + 16) = dequant8(xv[set].z, x1);
+    *(uint4*)(dx + 24) = dequant8(xv[set].w, x1);
   };
 
   const int lr = lane & 31, lh = lane >> 5;
-  gload(0);
-  sstore(0);
+  gload(0, std::integral_constant<int, 0>{});
+  gload(1, std::integral_constant<int, 1>{});
+  sstore(0, std::integral_constant<int, 0>{});
   __syncthreads();
 
-  for (int st = 0; st < steps; ++st) {
+  // stage st computes from LDS buffer st & 1 with register set st & 1 free
+  auto stage = [&](int st, auto setc) __attribute__((always_inline)) {
+    constexpr int set = decltype(setc)::value;
     const int buf = st & 1;
-    if (st + 1 < steps) gload(st + 1);
+    gload(st + 2, setc);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {  // one NVFP4 group per 16-channel MFMA step
       v8h a[2], b[2];
@@ -164,8 +182,18 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
           }
         }
     }
-    if (st + 1 < steps) sstore(buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // past the last stage this fills the idle buffer, which nothing reads
+    sstore(buf ^ 1, std::integral_constant<int, set ^ 1>{});
     __syncthreads();
+  };
+  {
+    int st = 0;
+    for (; st + 1 < steps; st += 2) {
+      stage(st, std::integral_constant<int, 0>{});
+      stage(st + 1, std::integral_constant<int, 1>{});
+    }
+    if (st < steps) stage(st, std::integral_constant<int, 0>{});
   }
 
   if constexpr (MODE != 1) {
