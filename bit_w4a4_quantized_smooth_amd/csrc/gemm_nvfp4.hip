@@ -20,12 +20,16 @@
 // 1/4) for the partial-product test mode.
 //
 // Tiling: 128(n) x 128(m) per 256-thread workgroup, wave tiles of 64x64,
-// K steps of 64 channels (four NVFP4 groups) double buffered in LDS; codes
-// and scales are loaded two steps ahead into two register sets (branch-free
-// buffer loads, rows past M read as zero), and scheduling barriers keep the
-// loads at the top of a step and their expansion into LDS at its end (left
-// to itself the compiler moves the expansion up to the loads, which makes
-// the step wait for them at once).  Tiles are assigned
+// K steps of 64 channels (four NVFP4 groups) double buffered in LDS.  Codes
+// are loaded a pair of steps at a time, four lanes per 64-byte row segment
+// (a load instruction with two lanes per 32-byte segment touches twice the
+// rows, and those per-lane cache accesses, not bytes, were a third of the
+// kernel's time), and scales four steps at a time, 16 bytes per row; both
+// arrive about two steps before use (branch-free buffer loads, rows past M
+// read as zero), and scheduling barriers keep the loads at the top of a step
+// and their expansion into LDS at its end (left to itself the compiler moves
+// the expansion up to the loads, which makes the step wait for them at
+// once).  Tiles are assigned
 // so that each XCD works on a contiguous part of a banded order.
 #include <type_traits>
 
@@ -88,14 +92,24 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   const int steps = K >> 6, G = K >> 4;
   const int rowb = K >> 1;
 
-  // staging: thread -> (row, 16-byte half = 32 channels = two NVFP4 groups)
-  const int srow = tid >> 1, shalf = tid & 1;
+  // Staging.  Two K steps (128 channels) are 64 contiguous bytes of codes per
+  // row; a load gives each lane 16 of them, four lanes per row, so one load
+  // instruction covers 16 whole 64-byte row segments.  Thread t owns rows
+  // r0 = t/4 and r0 + 64 of both operands: part p = t%4 of the weight rows
+  // and part p^2 of the activation rows.  Parts 0, 1 are the first step of
+  // the pair and parts 2, 3 the second, so for either step every thread holds
+  // two 32-channel chunks (of the weights for one step, of the activations
+  // for the other) and the expansion work is the same on every lane.  The 16
+  // E4M3 scale bytes of four steps of a row are one 16-byte load, issued once
+  // every four steps.
+  const int p = tid & 3, r0 = tid >> 2;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wc, (short)0, N * rowb, kBufDword3);
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)ac, (short)0, M * rowb, kBufDword3);
   const __amdgpu_buffer_rsrc_t wsres = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, MODE != 1 ? N * G : 0, kBufDword3);
   const __amdgpu_buffer_rsrc_t asres = __builtin_amdgcn_make_buffer_rsrc((void*)as, (short)0, MODE != 1 ? M * G : 0, kBufDword3);
-  const int woff = (n0 + srow) * rowb + shalf * 16, xoff = (m0 + srow) * rowb + shalf * 16;  // rows past M: zeros
-  const int wsoff = (n0 + srow) * G + 2 * shalf, xsoff = (m0 + srow) * G + 2 * shalf;
+  // rows past M read as zero (codes and scales)
+  const int wco = (n0 + r0) * rowb + 16 * p, xco = (m0 + r0) * rowb + 16 * (p ^ 2);
+  const int wso = (n0 + r0) * G, xso = (m0 + r0) * G;
 
   v16f acc[2][2];
 #pragma unroll
@@ -105,52 +119,71 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // Two register sets: the loads for stage st + 2 are issued at the start of
-  // stage st, while the set loaded one stage earlier is expanded into LDS at
-  // its end.  Loads of stages past the end use an offset beyond every
-  // buffer's range (they return zeros without touching memory), so every
-  // stage issues the same loads and the waits stay exact.
+  // Codes of step pair P (steps 2P, 2P+1) go to register set P & 1: pair
+  // P + 1 is loaded at the start of step 2P and expanded at the ends of steps
+  // 2P + 1 and 2P + 2.  Scale blocks of step quad Q (steps 4Q .. 4Q+3) are
+  // loaded at the start of step 4Q - 2 into `nxt` and used from `cur` after
+  // the rotation at the end of step 4Q - 1.  Loads past the last step use an
+  // offset beyond every buffer's range (zeros, no memory access), so every
+  // step issues the same loads and the compiler's waits stay exact.
   constexpr int kOffOut = 0x7FFFFFF0;
-  uint4 wv[2], xv[2];
-  u32 wsb[2] = {0x3838u, 0x3838u}, xsb[2] = {0x3838u, 0x3838u};  // two E4M3 scales (1.0, 1.0 in test mode)
-  auto gload = [&](int st, auto setc) {
+  uint4 cw[2][2], cx[2][2];  // [set][row r0 + 64 j]
+  uint4 cur[2][2], nxt[2][2];  // scale blocks [weight / activation][row r0 + 64 j]
+  auto cload = [&](int P, auto setc) {
     constexpr int set = decltype(setc)::value;
-    const bool live = st < steps;
-    wv[set] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, live ? woff + st * 32 : kOffOut, 0, 0));
-    xv[set] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, live ? xoff + st * 32 : kOffOut, 0, 0));
-    if constexpr (MODE != 1) {
-      wsb[set] = __builtin_amdgcn_raw_buffer_load_b16(wsres, live ? wsoff + st * 4 : kOffOut, 0, 0);
-      xsb[set] = __builtin_amdgcn_raw_buffer_load_b16(asres, live ? xsoff + st * 4 : kOffOut, 0, 0);
+    const bool live = 2 * P < steps;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      cw[set][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, live ? wco + 64 * j * rowb + 64 * P : kOffOut, 0, 0));
+      cx[set][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, live ? xco + 64 * j * rowb + 64 * P : kOffOut, 0, 0));
     }
   };
-  auto sstore = [&](int buf, auto setc) {
-    constexpr int set = decltype(setc)::value;
-    h2 w0, w1, x0, x1;
-    scale_pairs(wsb[set], w0, w1);
-    scale_pairs(xsb[set], x0, x1);
-    uint16_t* dw = &sW[buf][srow * ROW + shalf * 32];
-    *(uint4*)(dw + 0) = dequant8(wv[set].x, w0);
-    *(uint4*)(dw + 8) = dequant8(wv[set].y, w0);
-    *(uint4*)(dw + 16) = dequant8(wv[set].z, w1);
-    *(uint4*)(dw + 24) = dequant8(wv[set].w, w1);
-    uint16_t* dx = &sX[buf][srow * ROW + shalf * 32];
-    *(uint4*)(dx + 0) = dequant8(xv[set].x, x0);
-    *(uint4*)(dx + 8) = dequant8(xv[set].y, x0);
-    *(uint4*)(dx + 16) = dequant8(xv[set].z, x1);
-    *(uint4*)(dx + 24) = dequant8(xv[set].w, x1);
+  auto sload = [&](int Q, uint4 (&blk)[2][2]) {
+    if constexpr (MODE != 1) {
+      const bool live = 4 * Q < steps;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        blk[0][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wsres, live ? wso + 64 * j * G + 16 * Q : kOffOut, 0, 0));
+        blk[1][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(asres, live ? xso + 64 * j * G + 16 * Q : kOffOut, 0, 0));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) blk[0][j] = blk[1][j] = uint4{0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u};  // E4M3 1.0
+    }
+  };
+  // Expand step t into LDS buffer buf: H = t & 1 (step of its pair), CS = its
+  // code set, KD = t & 3 (its dword of the scale blocks).
+  auto sstore = [&](int buf, auto Hc, auto CSc, auto KDc, const uint4 (&blk)[2][2]) {
+    constexpr int H = decltype(Hc)::value, CS = decltype(CSc)::value, KD = decltype(KDc)::value;
+    const bool wside = (p < 2) == (H == 0);  // this lane holds weight chunks of step t
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint4 c = wside ? cw[CS][j] : cx[CS][j];
+      const uint4 bw = blk[0][j], bx = blk[1][j];
+      const u32 sd = wside ? (KD == 0 ? bw.x : KD == 1 ? bw.y : KD == 2 ? bw.z : bw.w)
+                           : (KD == 0 ? bx.x : KD == 1 ? bx.y : KD == 2 ? bx.z : bx.w);
+      h2 s0, s1;
+      scale_pairs(sd >> (16 * (p & 1)), s0, s1);  // the chunk's two groups
+      uint16_t* dst = (wside ? &sW[buf][0] : &sX[buf][0]) + (r0 + 64 * j) * ROW + 32 * (p & 1);
+      *(uint4*)(dst + 0) = dequant8(c.x, s0);
+      *(uint4*)(dst + 8) = dequant8(c.y, s0);
+      *(uint4*)(dst + 16) = dequant8(c.z, s1);
+      *(uint4*)(dst + 24) = dequant8(c.w, s1);
+    }
   };
 
   const int lr = lane & 31, lh = lane >> 5;
-  gload(0, std::integral_constant<int, 0>{});
-  gload(1, std::integral_constant<int, 1>{});
-  sstore(0, std::integral_constant<int, 0>{});
+  cload(0, std::integral_constant<int, 0>{});
+  sload(0, cur);
+  sstore(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, cur);
   __syncthreads();
 
-  // stage st computes from LDS buffer st & 1 with register set st & 1 free
-  auto stage = [&](int st, auto setc) __attribute__((always_inline)) {
-    constexpr int set = decltype(setc)::value;
-    const int buf = st & 1;
-    gload(st + 2, setc);
+  // step st = 4q + K computes from LDS buffer K & 1 and expands step st + 1
+  auto stage = [&](int st, auto Kc) __attribute__((always_inline)) {
+    constexpr int K4 = decltype(Kc)::value;
+    const int buf = K4 & 1;
+    if constexpr ((K4 & 1) == 0) cload((st >> 1) + 1, std::integral_constant<int, ((K4 >> 1) + 1) & 1>{});
+    if constexpr (K4 == 2) sload((st >> 2) + 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {  // one NVFP4 group per 16-channel MFMA step
@@ -183,17 +216,31 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // past the last stage this fills the idle buffer, which nothing reads
-    sstore(buf ^ 1, std::integral_constant<int, set ^ 1>{});
+    // past the last step this fills the idle buffer, which nothing reads
+    constexpr int T = K4 + 1;
+    if constexpr (T < 4)
+      sstore(buf ^ 1, std::integral_constant<int, T & 1>{}, std::integral_constant<int, (T >> 1) & 1>{},
+             std::integral_constant<int, T & 3>{}, cur);
+    else
+      sstore(buf ^ 1, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+             std::integral_constant<int, 0>{}, nxt);
     __syncthreads();
   };
   {
     int st = 0;
-    for (; st + 1 < steps; st += 2) {
+    for (; st + 3 < steps; st += 4) {
       stage(st, std::integral_constant<int, 0>{});
       stage(st + 1, std::integral_constant<int, 1>{});
+      stage(st + 2, std::integral_constant<int, 2>{});
+      stage(st + 3, std::integral_constant<int, 3>{});
+#pragma unroll
+      for (int o = 0; o < 2; ++o)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) cur[o][j] = nxt[o][j];
     }
     if (st < steps) stage(st, std::integral_constant<int, 0>{});
+    if (st + 1 < steps) stage(st + 1, std::integral_constant<int, 1>{});
+    if (st + 2 < steps) stage(st + 2, std::integral_constant<int, 2>{});
   }
 
   if constexpr (MODE != 1) {

@@ -105,6 +105,12 @@ SMALL = {
     "nvfp4_ragged_37x128x768_r16": lambda: synth.svdq_layer(8, 37, 128, 768, 16, synth.NVFP4, 0.02, 30.0),
     "int4_rank0_130x384x320": lambda: synth.svdq_layer(9, 130, 384, 320, 0, synth.INT4, 0.01, 20.0),
     "int4_rank128_64x128x256": lambda: synth.svdq_layer(10, 64, 128, 256, 128, synth.INT4, 0.01, 20.0),
+    # NVFP4 K steps of 64 channels not a multiple of four (1, 5, 6, 7): the
+    # GEMM stages codes two steps and scales four steps at a time
+    "nvfp4_k64_33x128x64_r16": lambda: synth.svdq_layer(11, 33, 128, 64, 16, synth.NVFP4, 0.02, 30.0),
+    "nvfp4_k320_ragged_45x256x320_r16": lambda: synth.svdq_layer(12, 45, 256, 320, 16, synth.NVFP4, 0.02, 30.0),
+    "nvfp4_k384_96x384x384_r32": lambda: synth.svdq_layer(13, 96, 384, 384, 32, synth.NVFP4, 0.01, 20.0),
+    "nvfp4_k448_rank0_70x128x448": lambda: synth.svdq_layer(14, 70, 128, 448, 0, synth.NVFP4, 0.01, 20.0),
 }
 
 

@@ -86,6 +86,7 @@ SMALL = {
     "nvfp4_d128_h2_256x512_r32": lambda: synth.qkv_layer(2005, 256, 2, 128, 512, 32, synth.NVFP4),
     "nvfp4_d64_h2_ragged37x768_r16": lambda: synth.qkv_layer(2006, 37, 2, 64, 768, 16, synth.NVFP4),
     "nvfp4_d128_h4_batch3_r16": lambda: synth.qkv_layer(2007, 3 * 64, 4, 128, 256, 16, synth.NVFP4, S=64),
+    "nvfp4_d64_h2_ragged50x448_r16": lambda: synth.qkv_layer(2008, 50, 2, 64, 448, 16, synth.NVFP4),
 }
 
 
