@@ -38,6 +38,8 @@
 // * Tiles are ordered so that each XCD (own L2) works on a contiguous range
 //   of a banded order: the tiles resident on one XCD at a time share a few
 //   activation and weight panels in that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "mlp_epi.h"
@@ -178,17 +180,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
       rc[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r < WCH ? wres : xres, coff[r] + kbyte, 0, 0));
     if constexpr (MODE != 1) {
       if constexpr (KG == 2 && SCD) {
-        // both groups' fp16 scales of a row are adjacent and 4-byte aligned
-        // (even group count): one dword per row instead of two shorts
-#pragma unroll
-        for (int r = 0; r < SROWS; ++r) {
-          const int g = s * KG;
-          uint32_t v = 0u;
-          if (s_live[r] && g < G)  // wave-uniform
-            v = s_is_w[r] ? __builtin_amdgcn_raw_buffer_load_b32(wsres, soff[r] + 2 * g, 0, 0)
-                          : __builtin_amdgcn_raw_buffer_load_b32(asres, soff[r] + 2 * g, 0, 0);
-          rs[r][0] = v;  // both groups: split at the LDS store
-        }
+        // scales come in blocks of four stages (sbload)
       } else {
 #pragma unroll
         for (int r = 0; r < SROWS; ++r) {
@@ -205,7 +197,26 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
       }
     }
   };
-  auto sstore = [&](int buf) {
+  // Even group count: the fp16 scales of four stages (eight groups) of a row
+  // are 16 contiguous, 4-byte aligned bytes, loaded once per four stages (a
+  // scale load gives every lane a different row, so its cost is per
+  // instruction, not per byte).  Groups past G in the last block belong to
+  // stages that are never computed.
+  uint4 sblk[SROWS];
+  auto sbload = [&](int s) {
+    if constexpr (MODE != 1 && KG == 2 && SCD) {
+#pragma unroll
+      for (int r = 0; r < SROWS; ++r) {
+        uint4 v = uint4{0u, 0u, 0u, 0u};
+        if (s_live[r])  // wave-uniform
+          v = __builtin_bit_cast(uint4, s_is_w[r] ? __builtin_amdgcn_raw_buffer_load_b128(wsres, soff[r] + 4 * s, 0, 0)
+                                                  : __builtin_amdgcn_raw_buffer_load_b128(asres, soff[r] + 4 * s, 0, 0));
+        sblk[r] = v;
+      }
+    }
+  };
+  auto sstore = [&](int buf, auto kdc) {
+    constexpr int KD = decltype(kdc)::value;  // this stage's dword of the scale block
     uint8_t* base = smem + buf * STAGE;
 #pragma unroll
     for (int r = 0; r < CHUNKS; ++r) {
@@ -220,8 +231,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
         const int row = tid + NT * r;
         if (s_live[r]) {
           if constexpr (KG == 2 && SCD) {
-            ssc[buf * SC_STAGE + row] = f16_bits_to_f32(rs[r][0] & 0xFFFFu);
-            ssc[buf * SC_STAGE + NROWS + row] = f16_bits_to_f32(rs[r][0] >> 16);
+            const uint32_t v = KD == 0 ? sblk[r].x : KD == 1 ? sblk[r].y : KD == 2 ? sblk[r].z : sblk[r].w;
+            ssc[buf * SC_STAGE + row] = f16_bits_to_f32(v & 0xFFFFu);
+            ssc[buf * SC_STAGE + NROWS + row] = f16_bits_to_f32(v >> 16);
           } else {
 #pragma unroll
             for (int gg = 0; gg < KG; ++gg) ssc[buf * SC_STAGE + gg * NROWS + row] = f16_bits_to_f32(rs[r][gg]);
@@ -255,12 +267,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
   }
 
   gload(0);
-  sstore(0);
+  sbload(0);
+  sstore(0, std::integral_constant<int, 0>{});
   __syncthreads();
 
-  for (int s = 0; s < stages; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < stages) gload(s + 1);
+  // stage s = 4q + K4 (the phase selects the scale block's dword statically)
+  auto stage = [&](int s, auto kc) __attribute__((always_inline)) {
+    constexpr int K4 = decltype(kc)::value;
+    const int buf = K4 & 1;
+    if (s + 1 < stages) {
+      gload(s + 1);
+      if constexpr (K4 == 3) sbload(s + 1);
+    }
     const uint8_t* base = smem + buf * STAGE;
 #pragma unroll 1
     for (int gg = 0; gg < KG; ++gg) {
@@ -334,8 +352,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
         }
       }
     }
-    if (s + 1 < stages) sstore(buf ^ 1);
+    if (s + 1 < stages) sstore(buf ^ 1, std::integral_constant<int, (K4 + 1) & 3>{});
     __syncthreads();
+  };
+  {
+    int s = 0;
+    for (; s + 3 < stages; s += 4) {
+      stage(s, std::integral_constant<int, 0>{});
+      stage(s + 1, std::integral_constant<int, 1>{});
+      stage(s + 2, std::integral_constant<int, 2>{});
+      stage(s + 3, std::integral_constant<int, 3>{});
+    }
+    if (s < stages) stage(s, std::integral_constant<int, 0>{});
+    if (s + 1 < stages) stage(s + 1, std::integral_constant<int, 1>{});
+    if (s + 2 < stages) stage(s + 2, std::integral_constant<int, 2>{});
   }
 
   if constexpr (MODE != 1) {
@@ -674,7 +704,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
 hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
   const int m_tiles = (int)((a.M + BM - 1) / BM);
   const int blocks = m_tiles * (int)((a.N + BN - 1) / BN);
-  // an even group count puts both groups' scales of a stage in one aligned dword
+  // an even group count makes a row's scales of four stages one 16-byte block
   const bool scd = (a.K / 64) % 2 == 0;
   auto k0 = scd ? gemm_int4_kernel<0, true> : gemm_int4_kernel<0, false>;
   auto k1 = gemm_int4_kernel<1, false>;

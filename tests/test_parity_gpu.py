@@ -105,6 +105,11 @@ SMALL = {
     "nvfp4_ragged_37x128x768_r16": lambda: synth.svdq_layer(8, 37, 128, 768, 16, synth.NVFP4, 0.02, 30.0),
     "int4_rank0_130x384x320": lambda: synth.svdq_layer(9, 130, 384, 320, 0, synth.INT4, 0.01, 20.0),
     "int4_rank128_64x128x256": lambda: synth.svdq_layer(10, 64, 128, 256, 128, synth.INT4, 0.01, 20.0),
+    # int4 with an even group count and 1, 5, 7 two-group stages: the GEMM
+    # loads scales in blocks of four stages
+    "int4_k128_40x128x128_r16": lambda: synth.svdq_layer(15, 40, 128, 128, 16, synth.INT4, 0.02, 30.0),
+    "int4_k640_ragged_77x256x640_r32": lambda: synth.svdq_layer(16, 77, 256, 640, 32, synth.INT4, 0.02, 30.0),
+    "int4_k896_rank0_130x128x896": lambda: synth.svdq_layer(17, 130, 128, 896, 0, synth.INT4, 0.01, 20.0),
     # NVFP4 K steps of 64 channels not a multiple of four (1, 5, 6, 7): the
     # GEMM stages codes two steps and scales four steps at a time
     "nvfp4_k64_33x128x64_r16": lambda: synth.svdq_layer(11, 33, 128, 64, 16, synth.NVFP4, 0.02, 30.0),
