@@ -88,6 +88,8 @@ constexpr uint32_t kBufDword3 = 0x00020000u;        // raw buffer, 32-bit data f
 static_assert(NROWS * PARTS % NT == 0, "stage loads must divide evenly");
 static_assert(BN % 128 == 0, "weight tile in halves of 128 rows");
 static_assert(BI % 2 == 0 && BJ % 2 == 0, "scale outer products cover 2x2 quads of blocks");
+static_assert((NT / 64) * BI * BJ * 64 * 16 <= LDS_BYTES, "K-split accumulator exchange fits a copy's LDS");
+static_assert(2 * LDS_BYTES <= 160 * 1024, "K-split workgroup fits the CU's LDS");
 
 __device__ __forceinline__ uint4 nib_lo16(uint4 v) {  // 16*q of even channels
   return uint4{(v.x << 4) & 0xF0F0F0F0u, (v.y << 4) & 0xF0F0F0F0u, (v.z << 4) & 0xF0F0F0F0u,
@@ -103,16 +105,26 @@ __device__ __forceinline__ uint4 nib_hi16(uint4 v) {  // 16*q of odd channels
 // attention projection (Q/K RMSNorm and rotary embedding in the epilogue);
 // 3: fused MLP up-projection (no Y: GELU, then the down projection's
 // quantization and low-rank input)
-template <int MODE, bool SCD>
-__global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
+//
+// SPLIT 2 (plain GEMM only): 2 NT threads per tile; threads [NT, 2 NT) are a
+// second copy of the workgroup that stages and multiplies the second half of
+// the K range in LDS of its own, and hands its fp32 accumulators to the first
+// copy through LDS before the epilogue.  A tile that has a CU to itself (grids
+// of at most one tile per CU) runs its chain of group products as two chains
+// of half the length on two waves per SIMD.
+template <int MODE, bool SCD, int SPLIT>
+__global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
     int M, int N, int K, int rank, const uint8_t* __restrict__ ac, const uint16_t* __restrict__ as,
     const uint8_t* __restrict__ wc, const uint16_t* __restrict__ ws, const float* __restrict__ xl1,
     const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
     int32_t* __restrict__ psums, QkvEpi qe, MlpEpi me) {
+  static_assert(SPLIT == 1 || (SPLIT == 2 && MODE == 0), "K split only for the plain GEMM");
   extern __shared__ __align__(16) uint8_t smem[];
-  float* ssc = (float*)(smem + 2 * STAGE);  // [2][KG][NROWS] fp32 scales
+  const int half = SPLIT == 2 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x / NT) : 0;
+  uint8_t* const sm = smem + half * LDS_BYTES;  // this copy's staging LDS
+  float* ssc = (float*)(sm + 2 * STAGE);  // [2][KG][NROWS] fp32 scales
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = (int)threadIdx.x & (NT - 1), wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;  // lane within a 16-lane group, group 0..3
 
   // Tile order.  Consecutive workgroup ids go round-robin over the 8 XCDs
@@ -132,6 +144,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
   const int wn = (wave / WAVES_M) * (BI * 16), wm = (wave % WAVES_M) * (BJ * 16);
   const int G = K >> 6;
   const int stages = (G + KG - 1) / KG;
+  const int lstages = stages / SPLIT;  // stages of this copy (SPLIT divides stages)
+  const int s_off = half * lstages;    // its first stage
   const int rowb = K >> 1;
 
   // Buffer resources: reads past the last row return zeros (the M and N tails).
@@ -174,7 +188,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
   uint32_t rs[SROWS][KG];  // raw fp16 bits: converted only at the LDS store, so
                            // no instruction waits on these loads before then
   auto gload = [&](int s) {
-    const int kbyte = s * 32 * KG;
+    const int kbyte = (s + s_off) * 32 * KG;
 #pragma unroll
     for (int r = 0; r < CHUNKS; ++r)
       rc[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r < WCH ? wres : xres, coff[r] + kbyte, 0, 0));
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
         for (int r = 0; r < SROWS; ++r) {
 #pragma unroll
           for (int gg = 0; gg < KG; ++gg) {
-            const int g = s * KG + gg;
+            const int g = (s + s_off) * KG + gg;
             uint32_t h = 0u;
             if (s_live[r] && g < G)  // wave-uniform
               h = s_is_w[r] ? __builtin_amdgcn_raw_buffer_load_b16(wsres, soff[r] + 2 * g, 0, 0)
@@ -209,15 +223,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
       for (int r = 0; r < SROWS; ++r) {
         uint4 v = uint4{0u, 0u, 0u, 0u};
         if (s_live[r])  // wave-uniform
-          v = __builtin_bit_cast(uint4, s_is_w[r] ? __builtin_amdgcn_raw_buffer_load_b128(wsres, soff[r] + 4 * s, 0, 0)
-                                                  : __builtin_amdgcn_raw_buffer_load_b128(asres, soff[r] + 4 * s, 0, 0));
+          v = __builtin_bit_cast(uint4, s_is_w[r] ? __builtin_amdgcn_raw_buffer_load_b128(wsres, soff[r] + 4 * (s + s_off), 0, 0)
+                                                  : __builtin_amdgcn_raw_buffer_load_b128(asres, soff[r] + 4 * (s + s_off), 0, 0));
         sblk[r] = v;
       }
     }
   };
   auto sstore = [&](int buf, auto kdc) {
     constexpr int KD = decltype(kdc)::value;  // this stage's dword of the scale block
-    uint8_t* base = smem + buf * STAGE;
+    uint8_t* base = sm + buf * STAGE;
 #pragma unroll
     for (int r = 0; r < CHUNKS; ++r) {
       const int row = (tid + NT * r) / PARTS;
@@ -275,14 +289,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
   auto stage = [&](int s, auto kc) __attribute__((always_inline)) {
     constexpr int K4 = decltype(kc)::value;
     const int buf = K4 & 1;
-    if (s + 1 < stages) {
+    if (s + 1 < lstages) {
       gload(s + 1);
       if constexpr (K4 == 3) sbload(s + 1);
     }
-    const uint8_t* base = smem + buf * STAGE;
+    const uint8_t* base = sm + buf * STAGE;
 #pragma unroll 1
     for (int gg = 0; gg < KG; ++gg) {
-      const int g = s * KG + gg;
+      const int g = (s + s_off) * KG + gg;
       // operand fragments of v_mfma_i32_16x16x64_i8: lane = (row l16 of the
       // block, channels 16*lg .. +16 of the group)
       v4i a[BI], b[BJ];
@@ -352,20 +366,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
         }
       }
     }
-    if (s + 1 < stages) sstore(buf ^ 1, std::integral_constant<int, (K4 + 1) & 3>{});
+    if (s + 1 < lstages) sstore(buf ^ 1, std::integral_constant<int, (K4 + 1) & 3>{});
     __syncthreads();
   };
   {
     int s = 0;
-    for (; s + 3 < stages; s += 4) {
+    for (; s + 3 < lstages; s += 4) {
       stage(s, std::integral_constant<int, 0>{});
       stage(s + 1, std::integral_constant<int, 1>{});
       stage(s + 2, std::integral_constant<int, 2>{});
       stage(s + 3, std::integral_constant<int, 3>{});
     }
-    if (s < stages) stage(s, std::integral_constant<int, 0>{});
-    if (s + 1 < stages) stage(s + 1, std::integral_constant<int, 1>{});
-    if (s + 2 < stages) stage(s + 2, std::integral_constant<int, 2>{});
+    if (s < lstages) stage(s, std::integral_constant<int, 0>{});
+    if (s + 1 < lstages) stage(s + 1, std::integral_constant<int, 1>{});
+    if (s + 2 < lstages) stage(s + 2, std::integral_constant<int, 2>{});
   }
 
   if constexpr (MODE != 1) {
@@ -379,6 +393,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_int4_kernel(
           acc[2 * pi + (q >> 1)][2 * pj + (q & 1)][v] =
               fmaf(sbuf[Qp & 1][4 * q + v], __int_as_float(dbuf[Qp & 1][q][v]),
                    acc[2 * pi + (q >> 1)][2 * pj + (q & 1)][v]);
+    }
+    if constexpr (SPLIT == 2) {
+      // the second copy's accumulators, through its own staging LDS (every
+      // wave passed the loop's last barrier, so that space is free; the
+      // epilogue below uses only the first copy's)
+      v4f* xch = (v4f*)(smem + LDS_BYTES) + wave * (BI * BJ * 64) + lane;
+      if (half == 1) {
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+#pragma unroll
+          for (int j = 0; j < BJ; ++j) xch[(i * BJ + j) * 64] = acc[i][j];
+      }
+      __syncthreads();
+      if (half == 1) return;
+#pragma unroll
+      for (int i = 0; i < BI; ++i)
+#pragma unroll
+        for (int j = 0; j < BJ; ++j) {
+          const v4f o = xch[(i * BJ + j) * 64];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][j][v] += o[v];
+        }
     }
     // Epilogue.  Every global load it needs (bias, the scale rows of the
     // sum_g S product, the first low-rank slices) is issued before any of them
@@ -706,10 +742,11 @@ hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
   const int blocks = m_tiles * (int)((a.N + BN - 1) / BN);
   // an even group count makes a row's scales of four stages one 16-byte block
   const bool scd = (a.K / 64) % 2 == 0;
-  auto k0 = scd ? gemm_int4_kernel<0, true> : gemm_int4_kernel<0, false>;
-  auto k1 = gemm_int4_kernel<1, false>;
-  auto k2 = scd ? gemm_int4_kernel<2, true> : gemm_int4_kernel<2, false>;
-  auto k3 = scd ? gemm_int4_kernel<3, true> : gemm_int4_kernel<3, false>;
+  auto k0 = scd ? gemm_int4_kernel<0, true, 1> : gemm_int4_kernel<0, false, 1>;
+  auto k1 = gemm_int4_kernel<1, false, 1>;
+  auto k2 = scd ? gemm_int4_kernel<2, true, 1> : gemm_int4_kernel<2, false, 1>;
+  auto k3 = scd ? gemm_int4_kernel<3, true, 1> : gemm_int4_kernel<3, false, 1>;
+  auto ks = gemm_int4_kernel<0, true, 2>;
   const void* kf = a.psums ? (const void*)k1 : a.qkv ? (const void*)k2 : a.mlp ? (const void*)k3 : (const void*)k0;
   hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
   if (e != hipSuccess) return e;
@@ -732,10 +769,23 @@ hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
                        (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
                        (const uint16_t*)a.l2t, (const uint16_t*)a.bias, nullptr, nullptr, qnone, *a.mlp);
   } else {
-    hipLaunchKernelGGL(k0, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
-                       (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
-                       (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
-                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, qnone, mnone);
+    // A grid of at most one tile per CU runs on the K-split kernel (needs an
+    // even number of two-group stages: K % 256 == 0).  Sending only the last
+    // partial round of a larger grid there measured slower: the second launch
+    // waits for the whole first grid, which costs more than the lone tiles.
+    if ((a.K / 64) % 4 == 0 && blocks <= device_cu_count()) {
+      e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * LDS_BYTES));
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(ks, dim3(blocks), dim3(2 * NT), 2 * LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
+                         (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
+                         (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
+                         (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, qnone, mnone);
+    } else {
+      hipLaunchKernelGGL(k0, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
+                         (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
+                         (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
+                         (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, qnone, mnone);
+    }
   }
   return hipGetLastError();
 }

@@ -498,19 +498,6 @@ static hipError_t launch_quant_dma(const QuantArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 template <int PREC, int RB>
 static hipError_t launch_quant(const QuantArgs& a, hipStream_t st) {
   // Ranks 16 / 32: once the 16-row workgroups of the kernel above no longer
@@ -518,7 +505,7 @@ static hipError_t launch_quant(const QuantArgs& a, hipStream_t st) {
   // copies) is faster, for both precisions; below that the one-row-block
   // workgroups keep every CU busy.
   if constexpr (RB == 1 || RB == 2) {
-    if ((a.M + 15) / 16 > device_cus()) return launch_quant_dma<PREC, RB>(a, st);
+    if ((a.M + 15) / 16 > device_cu_count()) return launch_quant_dma<PREC, RB>(a, st);
   }
   const size_t red = RB > 0 ? (size_t)QuantCfg<RB>::WAVES * 16 * RB * 16 : 0;
   const size_t lds = sizeof(float) * ((size_t)a.K > red ? (size_t)a.K : red);

@@ -166,6 +166,23 @@ def test_linear_end_to_end_small(small):
     assert max_abs_rel(y, ref) <= Y_TOL
 
 
+# --------------------------------------------------------------------------- int4 GEMM grid sizes
+# A grid of at most one 128x128 tile per CU (256 on MI355X) with K % 256 == 0
+# runs on the K-split kernel (two copies of the workgroup, each half of K);
+# one more tile row goes back to the plain grid.  Sampled rows (first, last,
+# and spread) and all columns against the oracle.
+@pytest.mark.parametrize("M", [2048, 2049])
+def test_gemm_split_boundary(M):
+    print(f"[parity] int4 GEMM {M}x2048x256 (tiles {((M + 127) // 128) * 16})", flush=True)
+    d = synth.svdq_layer(18, M, 2048, 256, 16, synth.INT4, 0.01, 20.0)
+    codes, scales = oracle.quantize_act(d["prec"], d["x"], d["lam"], alpha=d["alpha_a"])
+    xl1 = oracle.lowrank_down(d["x"], d["l1t"])
+    y = run_gemm(d, codes, scales, xl1)
+    rr, cc = np.meshgrid(np.unique(np.concatenate([np.arange(0, M, 61), [M - 1]])), np.arange(2048), indexing="ij")
+    ref = oracle_y(d, codes, scales, xl1, rows=rr.ravel(), cols=cc.ravel())
+    assert max_abs_rel(y[rr.ravel(), cc.ravel()], ref) <= Y_TOL
+
+
 # --------------------------------------------------------------------------- quantizer, many rows
 # int4 with ranks 16 / 32 on more 16-row blocks than the device has CUs goes to
 # the LDS-staged quantizer (32 rows per workgroup, 2048-channel chunks): the

@@ -102,7 +102,15 @@ def test_qkv_small(name):
     HD = d["heads"] * d["head_dim"]
     check_blocks(y, ref, HD)
     plain = run_plain(d, codes, scales, xl1)
-    assert np.array_equal(y[:, 2 * HD:], plain[:, 2 * HD:]), "V block differs from the plain GEMM"
+    M, K = d["x"].shape
+    tiles = -(-M // 128) * (3 * HD // 128)
+    if d["prec"] == sq.SVDQ_INT4 and K % 256 == 0 and tiles <= torch.cuda.get_device_properties(0).multi_processor_count:
+        # a plain int4 GEMM of at most one tile per CU runs on the K-split
+        # kernel (the two halves of K summed in another fp32 order)
+        g, r = synth.bf16_bits_to_f64(y[:, 2 * HD:]), synth.bf16_bits_to_f64(plain[:, 2 * HD:])
+        assert np.max(np.abs(g - r)) <= TOL * max(np.max(np.abs(r)), 1e-30), "V block vs the plain GEMM"
+    else:
+        assert np.array_equal(y[:, 2 * HD:], plain[:, 2 * HD:]), "V block differs from the plain GEMM"
 
 
 @pytest.mark.parametrize("prec", [sq.SVDQ_INT4, sq.SVDQ_NVFP4])
