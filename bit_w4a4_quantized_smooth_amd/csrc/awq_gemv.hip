@@ -25,6 +25,8 @@
 //    only for itself.  Needs K % 512 == 0 and K <= 8192.
 //  * other shapes (4 < M <= 64, or K outside that range): matrix-core
 //    kernel, see awq_gemm_mfma_kernel.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -261,8 +263,8 @@ __global__ __launch_bounds__(64 * W) void awq_gemv_kernel(
 // 0-3 take the first 64-channel group of every stage and waves 4-7 the
 // second, so two waves share each SIMD; their partial sums meet in LDS at
 // the end (fixed order).  Stages of two groups are double buffered in LDS;
-// the next stage's x, codes, scales and zero-points are loaded (branch-free
-// buffer loads) while the current one computes.  Within each 8-channel block both operands take the channel
+// x, codes, scales and zero-points are loaded two stages ahead into two
+// register sets (branch-free buffer loads).  Within each 8-channel block both operands take the channel
 // order (k0,k4) (k1,k5) (k2,k6) (k3,k7), which is the order the AND-OR code
 // expansion produces.
 namespace {
@@ -297,34 +299,42 @@ __global__ __launch_bounds__(512) void awq_gemm_mfma_kernel(
   // staging roles: x chunk c = tid + 512 r (r < 2) -> row c/16, 8-channel block
   // c%16; threads < 256: codes of row tid/4, 32 codes (tid%4); threads >= 256:
   // scale (t < 384) or zero-point of row t%64, group (t/64)%2
-  uint4 xv[2], wv;
-  u32 szv;
+  // Two register sets: the loads for stage st + 2 are issued at the start of
+  // stage st and expanded into LDS at the end of stage st + 1; loads past the
+  // last stage read zeros (offset beyond the buffer), and scheduling barriers
+  // keep the expansion at the end of a stage (the compiler would otherwise
+  // hoist it up to the loads and wait for them at once).
+  uint4 xv[2][2], wv[2];
+  u32 szv[2];
   const bool is_w = tid < 256;
-  auto gload = [&](int st) {
+  auto gload = [&](int st, auto setc) {
+    constexpr int set = decltype(setc)::value;
+    const bool live = st < stages;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int c = tid + 512 * r, row = c >> 4, blk = c & 15;
-      const bool ok = row < M && 2 * st + (blk >> 3) < G;
-      xv[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            xres, ok ? (row * K + 128 * st + 8 * blk) * 2 : kOut, 0, 0));
+      const bool ok = live && row < M && 2 * st + (blk >> 3) < G;
+      xv[set][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 xres, ok ? (row * K + 128 * st + 8 * blk) * 2 : kOut, 0, 0));
     }
     if (is_w) {  // wave-uniform
       const int row = tid >> 2, part = tid & 3;
-      const bool ok = 2 * st + (part >> 1) < G;
-      wv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                         wres, ok ? (n0 + row) * rowb + 64 * st + 16 * part : kOut, 0, 0));
+      const bool ok = live && 2 * st + (part >> 1) < G;
+      wv[set] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              wres, ok ? (n0 + row) * rowb + 64 * st + 16 * part : kOut, 0, 0));
     } else {
       const int row = tid & 63, g = 2 * st + ((tid >> 6) & 1);
-      const int off = g < G ? ((n0 + row) * G + g) * 2 : kOut;
-      szv = tid < 384 ? __builtin_amdgcn_raw_buffer_load_b16(sres, off, 0, 0)
-                      : __builtin_amdgcn_raw_buffer_load_b16(zres, off, 0, 0);
+      const int off = live && g < G ? ((n0 + row) * G + g) * 2 : kOut;
+      szv[set] = tid < 384 ? __builtin_amdgcn_raw_buffer_load_b16(sres, off, 0, 0)
+                           : __builtin_amdgcn_raw_buffer_load_b16(zres, off, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, auto setc) {
+    constexpr int set = decltype(setc)::value;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int c = tid + 512 * r, row = c >> 4, blk = c & 15;
-      const uint4 v = xv[r];
+      const uint4 v = xv[set][r];
       *(uint4*)&L.x[buf][row * AG_ROW + 8 * blk] =
           uint4{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
                 __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
@@ -341,7 +351,7 @@ __global__ __launch_bounds__(512) void awq_gemm_mfma_kernel(
     }
     if (is_w) {
       const int row = tid >> 2, part = tid & 3;
-      const u32 d4[4] = {wv.x, wv.y, wv.z, wv.w};
+      const u32 d4[4] = {wv[set].x, wv[set].y, wv[set].z, wv[set].w};
       u32 o[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -356,7 +366,7 @@ __global__ __launch_bounds__(512) void awq_gemm_mfma_kernel(
       for (int i = 0; i < 4; ++i) *(uint4*)(dst + 8 * i) = uint4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
     } else {
       const int row = tid & 63, g = (tid >> 6) & 1;
-      const float v = f16_bits_to_f32(szv);
+      const float v = f16_bits_to_f32(szv[set]);
       if (tid < 384) L.sc[buf][g][row] = v;
       else L.zp[buf][g][row] = v + 128.0f;
     }
@@ -366,12 +376,15 @@ __global__ __launch_bounds__(512) void awq_gemm_mfma_kernel(
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
 
-  gload(0);
-  sstore(0);
+  gload(0, std::integral_constant<int, 0>{});
+  gload(1, std::integral_constant<int, 1>{});
+  sstore(0, std::integral_constant<int, 0>{});
   __syncthreads();
-  for (int st = 0; st < stages; ++st) {
+  auto stage = [&](int st, auto setc) __attribute__((always_inline)) {
+    constexpr int set = decltype(setc)::value;
     const int buf = st & 1;
-    if (st + 1 < stages) gload(st + 1);
+    gload(st + 2, setc);
+    __builtin_amdgcn_sched_barrier(0);
     if (2 * st + half < G) {  // wave-uniform: a last stage may hold one group
       const int gg = half;
       v16f d;
@@ -393,8 +406,18 @@ __global__ __launch_bounds__(512) void awq_gemm_mfma_kernel(
           acc[4 * q + v] = fmaf(sc, fmaf(-zp, xs[v], d[4 * q + v]), acc[4 * q + v]);
       }
     }
-    if (st + 1 < stages) sstore(buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // past the last stage this fills the idle buffer, which nothing reads
+    sstore(buf ^ 1, std::integral_constant<int, set ^ 1>{});
     __syncthreads();
+  };
+  {
+    int st = 0;
+    for (; st + 1 < stages; st += 2) {
+      stage(st, std::integral_constant<int, 0>{});
+      stage(st + 1, std::integral_constant<int, 1>{});
+    }
+    if (st < stages) stage(st, std::integral_constant<int, 0>{});
   }
 
   // the second half's partial sums go through LDS (the staging space is free now)

@@ -273,6 +273,10 @@ AWQ = {
     "awq_3x8192x1024": lambda: synth.awq_layer(25, 3, 8192, 1024),
     "awq_2x3072x8192": lambda: synth.awq_layer(26, 2, 3072, 8192),
     "awq_4x192x1536": lambda: synth.awq_layer(27, 4, 192, 1536, with_bias=False),
+    # matrix-core kernel with an odd group count (a last stage of one group)
+    # and an odd number of two-group stages
+    "awq_7x320x1088": lambda: synth.awq_layer(28, 7, 320, 1088),
+    "awq_64x256x192": lambda: synth.awq_layer(29, 64, 256, 192),
 }
 
 
