@@ -166,6 +166,29 @@ def test_linear_end_to_end_small(small):
     assert max_abs_rel(y, ref) <= Y_TOL
 
 
+# --------------------------------------------------------------------------- largest K
+# The quantizer's largest K (32768): 16 chunks of 2048 channels in the
+# LDS-staged kernel (int4, 4112 rows), 512 steps in the first kernel (nvfp4,
+# 40 rows).  The GEMM over 512 groups: its fp32 accumulator carries
+# c0 * sum_g S for all of them until the epilogue removes it.
+@pytest.mark.parametrize("prec,M,rank", [(sq.SVDQ_INT4, 4112, 32), (sq.SVDQ_NVFP4, 40, 16)])
+def test_quantize_max_k(prec, M, rank):
+    print(f"[parity] quantize {M}x32768 prec {prec} r{rank}", flush=True)
+    check_quant(synth.svdq_layer(40 + prec, M, 128, 32768, rank, prec, 0.005, 30.0))
+
+
+@pytest.mark.parametrize("prec", [sq.SVDQ_INT4, sq.SVDQ_NVFP4])
+def test_gemm_max_k(prec):
+    print(f"[parity] GEMM 64x256x32768 prec {prec}", flush=True)
+    d = synth.svdq_layer(42 + prec, 64, 256, 32768, 16, prec, 0.01, 20.0)
+    codes, scales = oracle.quantize_act(d["prec"], d["x"], d["lam"], alpha=d["alpha_a"])
+    xl1 = oracle.lowrank_down(d["x"], d["l1t"])
+    y = run_gemm(d, codes, scales, xl1)
+    err = max_abs_rel(y, oracle_y(d, codes, scales, xl1))
+    print(f"[parity] max-abs-rel {err:.2e}", flush=True)
+    assert err <= Y_TOL
+
+
 # --------------------------------------------------------------------------- int4 GEMM grid sizes
 # A grid of at most one 128x128 tile per CU (256 on MI355X) with K % 256 == 0
 # runs on the K-split kernel (two copies of the workgroup, each half of K);
