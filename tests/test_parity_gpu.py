@@ -107,6 +107,7 @@ SMALL = {
     "int4_rank128_64x128x256": lambda: synth.svdq_layer(10, 64, 128, 256, 128, synth.INT4, 0.01, 20.0),
     # int4 with an even group count and 1, 5, 7 two-group stages: the GEMM
     # loads scales in blocks of four stages
+    "int4_k64_50x128x64_r16": lambda: synth.svdq_layer(19, 50, 128, 64, 16, synth.INT4, 0.02, 30.0),
     "int4_k128_40x128x128_r16": lambda: synth.svdq_layer(15, 40, 128, 128, 16, synth.INT4, 0.02, 30.0),
     "int4_k640_ragged_77x256x640_r32": lambda: synth.svdq_layer(16, 77, 256, 640, 32, synth.INT4, 0.02, 30.0),
     "int4_k896_rank0_130x128x896": lambda: synth.svdq_layer(17, 130, 128, 896, 0, synth.INT4, 0.01, 20.0),
@@ -276,14 +277,23 @@ def test_quantize_edge_cases(prec, kind):
     check_quant(_edge_case(prec, kind), smooth=False)
 
 
-def test_empty_inputs():
-    d = synth.svdq_layer(1, 0, 128, 256, 16, synth.INT4)
-    codes, scales, xl1 = sq.quantize_act(0, bf16_dev(np.zeros((0, 256), np.uint16)), None,
-                                         bf16_dev(d["l1t"]), 1.0)
-    y = sq.w4a4_gemm(0, codes, scales, dev(d["w_codes"]), f16_dev(d["w_scales"]), xl1,
-                     bf16_dev(d["l2t"]), None)
+@pytest.mark.parametrize("prec", [sq.SVDQ_INT4, sq.SVDQ_NVFP4])
+def test_empty_inputs(prec):
+    d = synth.svdq_layer(1, 0, 128, 256, 16, prec)
+    codes, scales, xl1 = sq.quantize_act(prec, bf16_dev(np.zeros((0, 256), np.uint16)), None,
+                                         bf16_dev(d["l1t"]), 1.0 if prec == sq.SVDQ_INT4 else 0.01)
+    y = sq.w4a4_gemm(prec, codes, scales, dev(d["w_codes"]), scales_dev(prec, d["w_scales"]), xl1,
+                     bf16_dev(d["l2t"]), None, d["alpha_a"], d["alpha_w"])
     torch.cuda.synchronize()
-    assert y.shape == (0, 128)
+    assert codes.shape == (0, 128) and xl1.shape == (0, 16) and y.shape == (0, 128)
+
+
+def test_awq_empty_input():
+    a = synth.awq_layer(2, 1, 256, 512)
+    y = sq.awq_gemv(bf16_dev(np.zeros((0, 512), np.uint16)), dev(a["w_codes"]), f16_dev(a["w_scales"]),
+                    f16_dev(a["w_zeros"]), bf16_dev(a["bias"]))
+    torch.cuda.synchronize()
+    assert y.shape == (0, 256)
 
 
 # --------------------------------------------------------------------------- AWQ
