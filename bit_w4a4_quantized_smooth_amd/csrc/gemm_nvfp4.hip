@@ -24,7 +24,8 @@
 // are loaded a pair of steps at a time, four lanes per 64-byte row segment
 // (a load instruction with two lanes per 32-byte segment touches twice the
 // rows, and those per-lane cache accesses, not bytes, were a third of the
-// kernel's time), and scales four steps at a time, 16 bytes per row; both
+// kernel's time), and scales sixteen steps at a time, 64 bytes per row split
+// over a lane quad (a step's scales reach the quad by a DPP broadcast); both
 // arrive about two steps before use (branch-free buffer loads, rows past M
 // read as zero), and scheduling barriers keep the loads at the top of a step
 // and their expansion into LDS at its end (left to itself the compiler moves
@@ -32,6 +33,7 @@
 // once).  Tiles are assigned
 // so that each XCD works on a contiguous part of a banded order.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "launch.h"
@@ -46,6 +48,12 @@ namespace {
 constexpr int BM = 128, BN = 128;
 constexpr int ROW = 72;  // fp16 per LDS row: 64 channels + 8 padding
 constexpr uint32_t kBufDword3 = 0x00020000u;  // raw buffer, 32-bit data format
+
+// f(integral_constant<int, I>) for I = 0, 1, ... in order
+template <typename F, int... I>
+__device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
 
 // 8 codes of one dword (channels 0..7, even channel in the low nibble) times
 // the scale pair s -> 8 fp16 (exact).
@@ -121,9 +129,13 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
 
   // Codes of step pair P (steps 2P, 2P+1) go to register set P & 1: pair
   // P + 1 is loaded at the start of step 2P and expanded at the ends of steps
-  // 2P + 1 and 2P + 2.  Scale blocks of step quad Q (steps 4Q .. 4Q+3) are
-  // loaded at the start of step 4Q - 2 into `nxt` and used from `cur` after
-  // the rotation at the end of step 4Q - 1.  Loads past the last step use an
+  // 2P + 1 and 2P + 2.  Scales: a row's 64 bytes of sixteen steps (steps
+  // 16Q .. 16Q+15) are one segment whose quarter p (steps 16Q+4p .. +3) lane p
+  // of each lane quad loads, so a load instruction covers 16 whole 64-byte
+  // row segments; a step's dword comes from the quad lane that holds it by a
+  // DPP broadcast.  They are loaded at the start of step 16Q - 2 into `nxt`
+  // and used from `cur` after the rotation at the end of step 16Q - 1.
+  // Loads past the last step use an
   // offset beyond every buffer's range (zeros, no memory access), so every
   // step issues the same loads and the compiler's waits stay exact.
   constexpr int kOffOut = 0x7FFFFFF0;
@@ -140,11 +152,11 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   };
   auto sload = [&](int Q, uint4 (&blk)[2][2]) {
     if constexpr (MODE != 1) {
-      const bool live = 4 * Q < steps;
+      const bool live = 16 * Q < steps;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        blk[0][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wsres, live ? wso + 64 * j * G + 16 * Q : kOffOut, 0, 0));
-        blk[1][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(asres, live ? xso + 64 * j * G + 16 * Q : kOffOut, 0, 0));
+        blk[0][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wsres, live ? wso + 64 * j * G + 64 * Q + 16 * p : kOffOut, 0, 0));
+        blk[1][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(asres, live ? xso + 64 * j * G + 64 * Q + 16 * p : kOffOut, 0, 0));
       }
     } else {
 #pragma unroll
@@ -152,16 +164,21 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
     }
   };
   // Expand step t into LDS buffer buf: H = t & 1 (step of its pair), CS = its
-  // code set, KD = t & 3 (its dword of the scale blocks).
-  auto sstore = [&](int buf, auto Hc, auto CSc, auto KDc, const uint4 (&blk)[2][2]) {
-    constexpr int H = decltype(Hc)::value, CS = decltype(CSc)::value, KD = decltype(KDc)::value;
+  // code set, T16 = t & 15 (quad lane T16 / 4 holds its scales, dword T16 % 4).
+  auto sstore = [&](int buf, auto Hc, auto CSc, auto T16c, const uint4 (&blk)[2][2]) {
+    constexpr int H = decltype(Hc)::value, CS = decltype(CSc)::value, T16 = decltype(T16c)::value;
+    constexpr int KD = T16 & 3, QL = T16 >> 2;
     const bool wside = (p < 2) == (H == 0);  // this lane holds weight chunks of step t
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const uint4 c = wside ? cw[CS][j] : cx[CS][j];
       const uint4 bw = blk[0][j], bx = blk[1][j];
-      const u32 sd = wside ? (KD == 0 ? bw.x : KD == 1 ? bw.y : KD == 2 ? bw.z : bw.w)
-                           : (KD == 0 ? bx.x : KD == 1 ? bx.y : KD == 2 ? bx.z : bx.w);
+      const u32 vw = KD == 0 ? bw.x : KD == 1 ? bw.y : KD == 2 ? bw.z : bw.w;
+      const u32 vx = KD == 0 ? bx.x : KD == 1 ? bx.y : KD == 2 ? bx.z : bx.w;
+      // quad_perm(QL, QL, QL, QL): every lane of the quad takes lane QL's dword
+      const u32 sw4 = (u32)__builtin_amdgcn_mov_dpp((int)vw, QL * 0x55, 0xF, 0xF, true);
+      const u32 sx4 = (u32)__builtin_amdgcn_mov_dpp((int)vx, QL * 0x55, 0xF, 0xF, true);
+      const u32 sd = wside ? sw4 : sx4;
       h2 s0, s1;
       scale_pairs(sd >> (16 * (p & 1)), s0, s1);  // the chunk's two groups
       uint16_t* dst = (wside ? &sW[buf][0] : &sX[buf][0]) + (r0 + 64 * j) * ROW + 32 * (p & 1);
@@ -178,12 +195,12 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   sstore(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, cur);
   __syncthreads();
 
-  // step st = 4q + K computes from LDS buffer K & 1 and expands step st + 1
+  // step st = 16q + K computes from LDS buffer K & 1 and expands step st + 1
   auto stage = [&](int st, auto Kc) __attribute__((always_inline)) {
-    constexpr int K4 = decltype(Kc)::value;
-    const int buf = K4 & 1;
-    if constexpr ((K4 & 1) == 0) cload((st >> 1) + 1, std::integral_constant<int, ((K4 >> 1) + 1) & 1>{});
-    if constexpr (K4 == 2) sload((st >> 2) + 1, nxt);
+    constexpr int K16 = decltype(Kc)::value;
+    const int buf = K16 & 1;
+    if constexpr ((K16 & 1) == 0) cload((st >> 1) + 1, std::integral_constant<int, ((K16 >> 1) + 1) & 1>{});
+    if constexpr (K16 == 14) sload((st >> 4) + 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {  // one NVFP4 group per 16-channel MFMA step
@@ -217,10 +234,10 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
     // past the last step this fills the idle buffer, which nothing reads
-    constexpr int T = K4 + 1;
-    if constexpr (T < 4)
+    constexpr int T = K16 + 1;
+    if constexpr (T < 16)
       sstore(buf ^ 1, std::integral_constant<int, T & 1>{}, std::integral_constant<int, (T >> 1) & 1>{},
-             std::integral_constant<int, T & 3>{}, cur);
+             std::integral_constant<int, T>{}, cur);
     else
       sstore(buf ^ 1, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
              std::integral_constant<int, 0>{}, nxt);
@@ -228,19 +245,15 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   };
   {
     int st = 0;
-    for (; st + 3 < steps; st += 4) {
-      stage(st, std::integral_constant<int, 0>{});
-      stage(st + 1, std::integral_constant<int, 1>{});
-      stage(st + 2, std::integral_constant<int, 2>{});
-      stage(st + 3, std::integral_constant<int, 3>{});
+    for (; st + 15 < steps; st += 16) {
+      static_for([&](auto ic) { stage(st + decltype(ic)::value, ic); }, std::make_integer_sequence<int, 16>{});
 #pragma unroll
       for (int o = 0; o < 2; ++o)
 #pragma unroll
         for (int j = 0; j < 2; ++j) cur[o][j] = nxt[o][j];
     }
-    if (st < steps) stage(st, std::integral_constant<int, 0>{});
-    if (st + 1 < steps) stage(st + 1, std::integral_constant<int, 1>{});
-    if (st + 2 < steps) stage(st + 2, std::integral_constant<int, 2>{});
+    static_for([&](auto ic) { if (st + decltype(ic)::value < steps) stage(st + decltype(ic)::value, ic); },
+               std::make_integer_sequence<int, 15>{});
   }
 
   if constexpr (MODE != 1) {

@@ -112,11 +112,14 @@ SMALL = {
     "int4_k640_ragged_77x256x640_r32": lambda: synth.svdq_layer(16, 77, 256, 640, 32, synth.INT4, 0.02, 30.0),
     "int4_k896_rank0_130x128x896": lambda: synth.svdq_layer(17, 130, 128, 896, 0, synth.INT4, 0.01, 20.0),
     # NVFP4 K steps of 64 channels not a multiple of four (1, 5, 6, 7): the
-    # GEMM stages codes two steps and scales four steps at a time
+    # GEMM stages codes two steps and scales sixteen steps at a time
     "nvfp4_k64_33x128x64_r16": lambda: synth.svdq_layer(11, 33, 128, 64, 16, synth.NVFP4, 0.02, 30.0),
     "nvfp4_k320_ragged_45x256x320_r16": lambda: synth.svdq_layer(12, 45, 256, 320, 16, synth.NVFP4, 0.02, 30.0),
     "nvfp4_k384_96x384x384_r32": lambda: synth.svdq_layer(13, 96, 384, 384, 32, synth.NVFP4, 0.01, 20.0),
     "nvfp4_k448_rank0_70x128x448": lambda: synth.svdq_layer(14, 70, 128, 448, 0, synth.NVFP4, 0.01, 20.0),
+    # and 15 (a whole remainder) and 17 (one 16-step scale block and one more)
+    "nvfp4_k960_ragged_33x256x960_r16": lambda: synth.svdq_layer(20, 33, 256, 960, 16, synth.NVFP4, 0.02, 30.0),
+    "nvfp4_k1088_64x128x1088_r32": lambda: synth.svdq_layer(21, 64, 128, 1088, 32, synth.NVFP4, 0.01, 20.0),
 }
 
 
