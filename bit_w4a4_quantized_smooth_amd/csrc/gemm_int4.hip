@@ -294,6 +294,12 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
       if constexpr (K4 == 3) sbload(s + 1);
     }
     const uint8_t* base = sm + buf * STAGE;
+    // Wave priority: low while multiplying, high while expanding the next
+    // stage into LDS and meeting the barrier, so that a wave whose partner
+    // on the SIMD (another workgroup) is multiplying gets through its
+    // staging first (1.2-2.7% on every shape against either fixed priority
+    // or high priority for the multiplications).
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll 1
     for (int gg = 0; gg < KG; ++gg) {
       const int g = (s + s_off) * KG + gg;
@@ -366,6 +372,7 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
         }
       }
     }
+    __builtin_amdgcn_s_setprio(1);
     if (s + 1 < lstages) sstore(buf ^ 1, std::integral_constant<int, (K4 + 1) & 3>{});
     __syncthreads();
   };
