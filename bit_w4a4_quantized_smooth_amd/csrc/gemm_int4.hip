@@ -678,8 +678,18 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
       // A = h [tokens x 32 channels] with this lane's own channels as its k
       // slots (16*(2c) + 4lg + 0..3, then 16*(2c+1) + 4lg + 0..3), B = L1 with
       // the same channel order; D[4lg + v][l16] = token 16j + 4lg + v, rank
-      // column rb*16 + l16
-      for (int rb = 0; rb < me.rank; rb += 16) {
+      // column rb*16 + l16.  The two column waves of a row block cover the
+      // same tokens: the second puts its partial in LDS, the first adds it to
+      // its own (a fixed order) and makes the one atomic add per element.  The
+      // exchange space alternates between two halves from one 16-rank block
+      // to the next, so one barrier per block keeps writes clear of reads.
+      static_assert(WAVES_N == 2, "column waves pair up for the XL1 exchange");
+      const int cw = wave / WAVES_M, rw = wave % WAVES_M;
+      float* const xx = (float*)(smem + (NT / 64) * (BJ * 16) * CROW);  // [2][WAVES_M][BJ*4][64]
+      static_assert((NT / 64) * (BJ * 16) * CROW + 2 * WAVES_M * BJ * 4 * 64 * 4 <= LDS_BYTES,
+                    "codes tiles and the XL1 exchange fit the staging LDS");
+      int par = 0;
+      for (int rb = 0; rb < me.rank; rb += 16, par ^= 1) {
         const int r = rb + l16;
         v8bf bl[2];
 #pragma unroll
@@ -688,20 +698,33 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
           const uint2 hi = *(const uint2*)(me.l1t + (size_t)r * N + nw + 32 * c + 16 + 4 * lg);
           bl[c] = __builtin_bit_cast(v8bf, uint4{lo.x, lo.y, hi.x, hi.y});
         }
+        v4f d[BJ];
 #pragma unroll
         for (int j = 0; j < BJ; ++j) {
-          v4f d = {0.f, 0.f, 0.f, 0.f};
+          d[j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const v8bf al = __builtin_bit_cast(
                 v8bf, uint4{hp[2 * c][j][0], hp[2 * c][j][1], hp[2 * c + 1][j][0], hp[2 * c + 1][j][1]});
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bl[c], d, 0, 0, 0);
+            d[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bl[c], d[j], 0, 0, 0);
           }
+        }
+        float* const xp = xx + (par * WAVES_M + rw) * (BJ * 4 * 64) + lane;
+        if (cw == 1) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int m = m0 + wm + 16 * j + 4 * lg + v;
-            if (m < M) unsafeAtomicAdd(me.xl1 + (size_t)m * me.rank + r, d[v]);
-          }
+          for (int j = 0; j < BJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) xp[(4 * j + v) * 64] = d[j][v];
+        }
+        __syncthreads();
+        if (cw == 0) {
+#pragma unroll
+          for (int j = 0; j < BJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int m = m0 + wm + 16 * j + 4 * lg + v;
+              if (m < M) unsafeAtomicAdd(me.xl1 + (size_t)m * me.rank + r, d[j][v] + xp[(4 * j + v) * 64]);
+            }
         }
       }
       return;
