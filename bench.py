@@ -47,17 +47,20 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_int4_dit_qkv_4608x92
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    # The GPU's clocks need tens of milliseconds of sustained load to settle
-    # (a 4608x9216x3072 GEMM runs ~15% slower for the first ~40 ms after idle),
-    # so the default warm-up is 200 untimed steps (~60 ms).
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    # The GPU's clocks need tens of milliseconds of sustained load to settle
+    # (a 4608x9216x3072 GEMM runs ~15% slower for the first ~40 ms after idle):
+    # before the warm-up steps, untimed steps run until this much wall time has
+    # passed with the GPU busy.  Reported in the JSON line as settle_ms and
+    # settle_steps; 0 disables it.
+    p.add_argument("--settle-ms", type=float, default=150.0)
     p.add_argument("--copies", type=int, default=4, help="input copies cycled for the linear")
     p.add_argument("--awq-copies", type=int, default=16, help="AWQ weight copies cycled (>= 512 MB)")
     p.add_argument("--calls", type=int, default=20, help="timed calls per extra workload")
     p.add_argument("--no-extras", action="store_true", help="time only the step")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=2304, help="rows of X in the oracle's timed sample")
+    p.add_argument("--cpu-rows", type=int, default=1152, help="rows of X in the oracle's timed sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of the benchmark, copy MIB MiB device-to-device a few times (the known-size "
                         "transfer that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -186,15 +189,23 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
+    settle_steps = 0
+    if args.settle_ms > 0:
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+            for _ in range(16):
+                step(settle_steps)
+                settle_steps += 1
+            torch.cuda.synchronize()
     for i in range(args.warmup):
-        step(i)
+        step(settle_steps + i)
     torch.cuda.synchronize()
 
     gevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, gemm_ev=gevs[i])
+        step(settle_steps + args.warmup + i, gemm_ev=gevs[i])
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t0
     t_gemm = np.array([e[0].elapsed_time(e[1]) for e in gevs])
@@ -203,7 +214,7 @@ def main():
     nc = min(args.steps, 50)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nc)]
     for i in range(nc):
-        step(args.warmup + args.steps + i, evs[i])
+        step(settle_steps + args.warmup + args.steps + i, evs[i])
     torch.cuda.synchronize()
     t_quant = np.array([e[0].elapsed_time(e[1]) for e in evs])
     t_awq = np.array([e[2].elapsed_time(e[3]) for e in evs])
@@ -238,6 +249,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -248,14 +261,14 @@ def main():
                    "M": M, "N": N, "K": K, "rank": R, "group": 64, "awq": [2, 18432, 3072]},
         "components": components,
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                     "unit": "TOPS", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
                      "kernel": "gemm_int4_kernel", "per_launch_ops": ops,
                      "algorithmic_bytes": int(M * K // 2 + M * K // 64 * 2 + N * K // 2 + N * K // 64 * 2
                                               + M * R * 4 + N * R * 2 + N * 2 + M * N * 2)},
     }
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(lin, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(lin, args.cpu_rows, synth)
     print(json.dumps(out), flush=True)
 
 
@@ -450,22 +463,46 @@ def extras(args, torch, sq, synth, t, bf, f16, stream):
     return res
 
 
-def cpu_baseline(lin, rows):
-    """The oracle, as it stands, on the first `rows` rows of the same workload:
-    quantize + X.L1 + the full linear for those rows against all N columns."""
+def cpu_baseline(lin, rows, synth):
+    """The oracle, as it stands, on bounded samples of the workloads, on the host's
+    cores: `value` is the QKV linear (quantize + X.L1 + the linear against all N
+    columns) on its first `rows` rows; `per_workload` adds the small int4
+    workload in full on one thread and on all, and the first rows of the MLP
+    projections, the NVFP4 QKV projection and the AWQ modulation projections."""
     import oracle
     nthreads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    x = np.ascontiguousarray(lin["x"][:rows])
-    t0 = time.perf_counter()
-    codes, scales = oracle.quantize_act(oracle.INT4, x, lin["lam"], nthreads=nthreads)
-    xl1 = oracle.lowrank_down(x, lin["l1t"], nthreads=nthreads)
-    oracle.w4a4_linear(oracle.INT4, codes, scales, lin["w_codes"], lin["w_scales"], xl1, lin["l2t"],
-                       lin["bias"], nthreads=nthreads)
-    dt = time.perf_counter() - t0
-    ops = 2.0 * rows * lin["N"] * lin["K"]
-    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": nthreads, "kind": "oracle",
-            "sample": f"first {rows} of {lin['M']} rows of the linear (quantize + X.L1 + all "
-                      f"{lin['N']} outputs), {dt:.2f} s"}
+
+    def linear(d, r, nt):
+        x = np.ascontiguousarray(d["x"][:r])
+        t0 = time.perf_counter()
+        codes, scales = oracle.quantize_act(d["prec"], x, d["lam"], alpha=d["alpha_a"], nthreads=nt)
+        xl1 = oracle.lowrank_down(x, d["l1t"], nthreads=nt)
+        oracle.w4a4_linear(d["prec"], codes, scales, d["w_codes"], d["w_scales"], xl1, d["l2t"], d["bias"],
+                           alpha_a=d["alpha_a"], alpha_w=d["alpha_w"], nthreads=nt)
+        dt = time.perf_counter() - t0
+        ops = 2.0 * r * d["N"] * d["K"]
+        return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "threads": nt, "seconds": round(dt, 3),
+                "sample": f"first {r} of {d['M']} rows"}
+
+    res = linear(lin, rows, nthreads)
+    per = {}
+    small = synth.WORKLOADS["svdq_int4_256x512x512_r16"]()
+    per["svdq_int4_256x512x512_r16_1thread"] = linear(small, small["M"], 1)
+    per["svdq_int4_256x512x512_r16"] = linear(small, small["M"], nthreads)
+    for name in ("dit_mlp_up_int4_4608x12288x3072_r32", "dit_mlp_down_int4_4608x3072x12288_r32",
+                 "dit_qkv_nvfp4_4608x9216x3072_r32"):
+        per[name] = linear(synth.WORKLOADS[name](), 576, nthreads)
+    for name in ("awq_mod_2x18432x3072", "awq_mod_64x18432x3072"):
+        d = synth.WORKLOADS[name]()
+        t0 = time.perf_counter()
+        oracle.awq_linear(d["x"], d["w_codes"], d["w_scales"], d["w_zeros"], d["bias"], nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        byts = d["N"] * d["K"] // 2 + 2 * d["N"] * (d["K"] // 64) * 2 + d["M"] * d["K"] * 2 + d["N"] * 2 + d["M"] * d["N"] * 2
+        per[name] = {"value": round(byts / dt / 1e9, 3), "unit": "GB/s", "threads": nthreads, "seconds": round(dt, 3),
+                     "sample": "all rows"}
+    return {"value": res["value"], "unit": "TOPS", "cores": nthreads, "kind": "oracle",
+            "sample": f"first {rows} of {lin['M']} rows of the QKV linear (quantize + X.L1 + all {lin['N']} "
+                      f"outputs), {res['seconds']:.2f} s", "per_workload": per}
 
 
 if __name__ == "__main__":

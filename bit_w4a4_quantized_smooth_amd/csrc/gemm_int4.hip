@@ -38,6 +38,7 @@
 // * Tiles are ordered so that each XCD (own L2) works on a contiguous range
 //   of a banded order: the tiles resident on one XCD at a time share a few
 //   activation and weight panels in that XCD's L2.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -767,6 +768,10 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
   }
 }
 
+// Test hook: when set, the plain GEMM never takes the K-split instance.
+static std::atomic<int> g_no_ksplit{0};
+void set_no_ksplit(int v) { g_no_ksplit.store(v ? 1 : 0); }
+
 hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
   const int m_tiles = (int)((a.M + BM - 1) / BM);
   const int blocks = m_tiles * (int)((a.N + BN - 1) / BN);
@@ -803,7 +808,7 @@ hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
     // even number of two-group stages: K % 256 == 0).  Sending only the last
     // partial round of a larger grid there measured slower: the second launch
     // waits for the whole first grid, which costs more than the lone tiles.
-    if ((a.K / 64) % 4 == 0 && blocks <= device_cu_count()) {
+    if ((a.K / 64) % 4 == 0 && blocks <= device_cu_count() && !g_no_ksplit.load()) {
       e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * LDS_BYTES));
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(ks, dim3(blocks), dim3(2 * NT), 2 * LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,

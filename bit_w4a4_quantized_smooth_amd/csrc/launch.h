@@ -107,6 +107,7 @@ hipError_t launch_quantize_weight(int precision, int64_t N, int64_t K, const flo
 hipError_t launch_awq_quantize(int64_t N, int64_t K, const void* w, void* codes, void* scales, void* zeros,
                                hipStream_t st);
 hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st);
+void set_no_ksplit(int v);
 hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st);
 hipError_t launch_awq(const AwqArgs& a, hipStream_t st);
 

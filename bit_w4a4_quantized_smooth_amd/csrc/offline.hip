@@ -201,11 +201,15 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(int n, int p, const f
 
 // One workgroup: sum the partial Grams in chunk order, shift (first pass only),
 // Cholesky G = R^T R (R upper triangular), then Rinv = R^-1, written to rinv [p][p].
+// A pivot that is not positive (possible only where the Gram matrix has a zero
+// row: an all-zero input, or a column zeroed by the previous pass) marks a dead
+// column: its row of R becomes e_i and its column of Rinv zero, so its basis
+// vector is zero and the other columns are orthonormalized without it.
 __global__ __launch_bounds__(256) void chol_inv_kernel(int p, int nparts, const float* __restrict__ part,
-                                                       float shift_rel, float* __restrict__ rinv,
-                                                       int* __restrict__ status) {
+                                                       float shift_rel, float* __restrict__ rinv) {
   __shared__ float g[TS_P][TS_P + 1];
   __shared__ float ri[TS_P][TS_P + 1];
+  __shared__ int dead[TS_P];
   __shared__ float tr;
   const int tid = threadIdx.x;
   for (int e = tid; e < p * p; e += 256) {
@@ -227,12 +231,13 @@ __global__ __launch_bounds__(256) void chol_inv_kernel(int p, int nparts, const 
   for (int i = 0; i < p; ++i) {
     if (tid == 0) {
       const float d = g[i][i];
-      if (!(d > 0.f)) atomicExch(status, 1);
-      g[i][i] = __builtin_sqrtf(fmaxf(d, 1e-30f));
+      dead[i] = !(d > 0.f);
+      g[i][i] = dead[i] ? 1.0f : __builtin_sqrtf(d);
     }
     __syncthreads();
     const float rii = g[i][i];
-    for (int j = i + 1 + tid; j < p; j += 256) g[i][j] /= rii;
+    const bool di = dead[i];
+    for (int j = i + 1 + tid; j < p; j += 256) g[i][j] = di ? 0.0f : g[i][j] / rii;
     __syncthreads();
     // trailing update g[a][b] -= g[i][a] g[i][b], a, b > i, b >= a
     for (int e = tid; e < (p - i - 1) * (p - i - 1); e += 256) {
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(256) void chol_inv_kernel(int p, int nparts, const 
   // Rinv: upper triangular inverse by columns, thread j owns column j
   for (int e = tid; e < p * p; e += 256) ri[e / p][e % p] = 0.f;
   __syncthreads();
-  if (tid < p) {
+  if (tid < p && !dead[tid]) {
     const int j = tid;
     ri[j][j] = 1.0f / g[j][j];
     for (int i = j - 1; i >= 0; --i) {
@@ -481,8 +486,7 @@ size_t lowrank_workspace_bytes(int64_t N, int64_t K, int p) {
                           + (size_t)K * p          // Z
                           + parts * TS_P * TS_P    // partial Grams
                           + TS_P * TS_P            // Rinv
-                          + TS_P + TS_P * TS_P)    // evals, evecs
-         + 64;                                     // status word
+                          + TS_P + TS_P * TS_P);   // evals, evecs
 }
 
 hipError_t launch_calibrate(int64_t Mc, int64_t N, int64_t K, const void* x, const void* w, void* lam, hipStream_t st) {
@@ -493,12 +497,12 @@ hipError_t launch_calibrate(int64_t Mc, int64_t N, int64_t K, const void* x, con
 
 // Orthonormalize Y [n, p] in place (CholeskyQR2; a small diagonal shift on the
 // first pass keeps the Gram matrix positive definite in fp32).
-static void orth(int n, int p, float* Y, float* part, float* rinv, int* status, hipStream_t st) {
+static void orth(int n, int p, float* Y, float* part, float* rinv, hipStream_t st) {
   const int nparts = (n + GR_ROWS - 1) / GR_ROWS;
   for (int pass = 0; pass < 2; ++pass) {
     hipLaunchKernelGGL(gram_partial_kernel, dim3(nparts), dim3(256), 0, st, n, p, (const float*)Y, part);
     hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(256), 0, st, p, nparts, (const float*)part,
-                       pass == 0 ? 1e-6f : 0.0f, rinv, status);
+                       pass == 0 ? 1e-6f : 0.0f, rinv);
     hipLaunchKernelGGL(apply_rinv_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, n, p, (const float*)rinv, Y);
   }
 }
@@ -514,7 +518,6 @@ hipError_t launch_lowrank(const LowrankArgs& a, hipStream_t st) {
   float* rinv = part + parts * TS_P * TS_P;   // [64][64]
   float* evals = rinv + TS_P * TS_P;          // [64]
   float* evecs = evals + TS_P;                // [64][64]
-  int* status = (int*)(evecs + TS_P * TS_P);
   float* wh = a.residual;
   hipLaunchKernelGGL(smooth_weight_kernel, dim3(blocks_for((size_t)N * K / 2, 256)), dim3(256), 0, st, N, K,
                      (const uint16_t*)a.w, (const uint16_t*)a.lam, wh);
@@ -522,14 +525,14 @@ hipError_t launch_lowrank(const LowrankArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(tsmm_nn_kernel, dim3(blocks_for(N, 32)), dim3(256), 0, st, N, K, p, (const float*)wh,
                      (const float*)Z, Y);
-  orth(N, p, Y, part, rinv, status, st);
+  orth(N, p, Y, part, rinv, st);
   for (int it = 0; it < a.iters; ++it) {
     hipLaunchKernelGGL(tsmm_tn_kernel, dim3(blocks_for(K, 32)), dim3(256), 0, st, N, K, p, (const float*)wh,
                        (const float*)Y, Z);
-    orth(K, p, Z, part, rinv, status, st);
+    orth(K, p, Z, part, rinv, st);
     hipLaunchKernelGGL(tsmm_nn_kernel, dim3(blocks_for(N, 32)), dim3(256), 0, st, N, K, p, (const float*)wh,
                        (const float*)Z, Y);
-    orth(N, p, Y, part, rinv, status, st);
+    orth(N, p, Y, part, rinv, st);
   }
   // Rayleigh-Ritz: Zb = W_hat^T Q [K, p]; C = Zb^T Zb; C = E diag(ev) E^T
   hipLaunchKernelGGL(tsmm_tn_kernel, dim3(blocks_for(K, 32)), dim3(256), 0, st, N, K, p, (const float*)wh,

@@ -7,6 +7,7 @@
 // 64, awq_w4a16 int4 64.  A device that is not gfx950 is rejected with an
 // error before any launch, never run into wrong results (blog "Nunchaku 4-bit
 // inference in Diffusers", "Hardware support": the capability check at load).
+#include <float.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -99,6 +100,10 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMax32 = (int64_t)1 << 31;  // 32-bit byte offsets inside the kernels
+// Largest channel count: the quantizer's limit, and the largest K at which the
+// GEMMs' fp32 accumulation is parity-tested.
+constexpr int64_t kMaxK = 32768;
 
 }  // namespace
 
@@ -114,6 +119,8 @@ void svdq_test_set_arch_override(const char* arch) {
   g_arch_override = arch ? arch : "";
 }
 
+void svdq_test_set_no_ksplit(int on) { svdq::set_no_ksplit(on); }
+
 svdq_status svdq_quantize_act(int precision, int group_size, int rank, int64_t M, int64_t K,
                               const void* x, const void* smooth, const void* l1t,
                               float act_global_scale, void* act_codes, void* act_scales,
@@ -123,8 +130,9 @@ svdq_status svdq_quantize_act(int precision, int group_size, int rank, int64_t M
   if (!valid_rank(rank)) return fail(SVDQ_ERR_UNSUPPORTED, "rank %d not in {0, 16, ..., 128}", rank);
   if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxDim) return fail(SVDQ_ERR_INVALID_ARG, "bad shape M=%lld K=%lld", (long long)M, (long long)K);
   if (K % 64 != 0) return fail(SVDQ_ERR_UNSUPPORTED, "K=%lld must be a multiple of 64", (long long)K);
-  if (K > 32768) return fail(SVDQ_ERR_UNSUPPORTED, "K=%lld above the supported 32768", (long long)K);
+  if (K > kMaxK) return fail(SVDQ_ERR_UNSUPPORTED, "K=%lld above the supported %lld", (long long)K, (long long)kMaxK);
   if (M * K >= ((int64_t)1 << 30)) return fail(SVDQ_ERR_UNSUPPORTED, "M*K above 2^30 - 1 (x must stay below 2 GiB)");
+  if (M * rank * 4 >= kMax32) return fail(SVDQ_ERR_UNSUPPORTED, "M*rank*4 must stay below 2^31 bytes");
   if (M == 0) return ok();  // empty call: nothing to read or write
   if (!x || !act_codes || !act_scales) return fail(SVDQ_ERR_INVALID_ARG, "x, act_codes and act_scales are required");
   if ((rank > 0) != (l1t != nullptr)) return fail(SVDQ_ERR_INVALID_ARG, "l1t must be given iff rank > 0");
@@ -156,9 +164,13 @@ static svdq_status gemm_common(int precision, int group_size, int rank, int64_t 
   if (M < 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return fail(SVDQ_ERR_INVALID_ARG, "bad shape M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
   if (K % 64 != 0) return fail(SVDQ_ERR_UNSUPPORTED, "K=%lld must be a multiple of 64", (long long)K);
+  if (K > kMaxK) return fail(SVDQ_ERR_UNSUPPORTED, "K=%lld above the supported %lld", (long long)K, (long long)kMaxK);
   if (N % 128 != 0) return fail(SVDQ_ERR_UNSUPPORTED, "N=%lld must be a multiple of 128", (long long)N);
   if (M * K > ((int64_t)1 << 31) || N * K > ((int64_t)1 << 31) || M * N > ((int64_t)1 << 31))
     return fail(SVDQ_ERR_UNSUPPORTED, "operand above 2^31 elements");
+  // the kernels address xl1 [M, rank] fp32 and l2t [N, rank] bf16 with 32-bit byte offsets
+  if (M * rank * 4 >= kMax32 || N * rank * 2 >= kMax32)
+    return fail(SVDQ_ERR_UNSUPPORTED, "M*rank*4 and N*rank*2 must stay below 2^31 bytes");
   if (M > 0 && !act_codes) return fail(SVDQ_ERR_INVALID_ARG, "act_codes is required");
   if (!w_codes) return fail(SVDQ_ERR_INVALID_ARG, "w_codes is required");
   return SVDQ_OK;
@@ -181,6 +193,14 @@ static svdq_status gemm_y(int precision, int group_size, int rank, int64_t M, in
   if (precision == SVDQ_NVFP4 && !(act_global_scale > 0.0f && w_global_scale > 0.0f &&
                                    act_global_scale < 3.0e38f && w_global_scale < 3.0e38f))
     return fail(SVDQ_ERR_INVALID_ARG, "global scales must be finite and > 0 for nvfp4");
+  // the epilogue applies the single factor fl32(alpha_a * alpha_w): it must be a
+  // finite normal number, or y would come out inf, NaN or flushed
+  if (precision == SVDQ_NVFP4) {
+    const float prod = act_global_scale * w_global_scale;
+    if (!(prod >= FLT_MIN && prod <= FLT_MAX))
+      return fail(SVDQ_ERR_INVALID_ARG, "fl32(act_global_scale * w_global_scale) = %g is not a finite normal float",
+                  (double)prod);
+  }
   if (!aligned16(act_codes) || !aligned16(act_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
       !aligned16(xl1) || !aligned16(l2t) || !aligned16(bias) || !aligned16(y))
     return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
@@ -255,6 +275,7 @@ svdq_status svdq_w4a4_gemm_gelu_quant(int precision, int group_size, int rank, i
     return fail(SVDQ_ERR_UNSUPPORTED, "the fused MLP up-projection supports int4 (group 64) only");
   if ((s = gemm_common(precision, group_size, rank, M, N, K, act_codes, w_codes)) != SVDQ_OK) return s;
   if (!valid_rank(rank_out)) return fail(SVDQ_ERR_UNSUPPORTED, "rank_out %d not in {0, 16, ..., 128}", rank_out);
+  if (M * rank_out * 4 >= kMax32) return fail(SVDQ_ERR_UNSUPPORTED, "M*rank_out*4 must stay below 2^31 bytes");
   if (M == 0) return ok();
   if (!act_scales || !w_scales || !codes_out || !scales_out)
     return fail(SVDQ_ERR_INVALID_ARG, "act_scales, w_scales, codes_out and scales_out are required");

@@ -73,7 +73,8 @@ typedef enum { SVDQ_INT4 = 0, SVDQ_NVFP4 = 1 } svdq_precision;
  *
  *   precision   SVDQ_INT4 (group_size must be 64) or SVDQ_NVFP4 (16)
  *   rank        0, 16, 32, ..., 128; 0 disables the low-rank branch
- *   M, K        rows and channels; K % 64 == 0, K <= 32768, M*K < 2^30
+ *   M, K        rows and channels; K % 64 == 0, K <= 32768, M*K < 2^30,
+ *               M*rank*4 < 2^31 (32-bit byte offsets into xl1)
  *   x           bf16 [M, K]; +-inf quantizes to the saturated code of its sign
  *               (int4 -8 / 7, nvfp4 -6 / 6) and counts as the group's maximum;
  *               codes and scales of a group holding a NaN are unspecified
@@ -100,9 +101,13 @@ svdq_status svdq_quantize_act(int precision, int group_size, int rank, int64_t M
  *
  *   precision, group_size   as for svdq_quantize_act
  *   rank        0, 16, ..., 128
- *   M, N, K     M >= 0; N % 128 == 0; K % 64 == 0
+ *   M, N, K     M >= 0; N % 128 == 0; K % 64 == 0, K <= 32768 (the largest K
+ *               parity-tested); M*K, N*K, M*N <= 2^31; M*rank*4 and N*rank*2
+ *               below 2^31 (32-bit byte offsets into xl1 and l2t)
  *   act_codes, act_scales   as written by svdq_quantize_act
- *   act_global_scale, w_global_scale   NVFP4 alpha_a, alpha_w; ignored for int4
+ *   act_global_scale, w_global_scale   NVFP4 alpha_a, alpha_w (each finite and
+ *               > 0, and their fp32 product a finite normal float: the epilogue
+ *               applies that one factor); ignored for int4
  *   w_codes     u8 [N, K/2] (same nibble order and encoding as act_codes)
  *   w_scales    int4: fp16 [N, K/64]; nvfp4: E4M3 u8 [N, K/16]
  *   xl1         fp32 [M, rank]; NULL iff rank == 0
@@ -175,7 +180,7 @@ svdq_status svdq_w4a4_gemm_qkv_norm_rope(int precision, int group_size, int rank
  *   smooth_out  bf16 [N] smoothing factors of the down projection, or NULL for 1
  *   l1t_out     bf16 [rank_out, N] (L1 of the down projection, transposed);
  *               NULL iff rank_out == 0
- *   rank_out    0, 16, ..., 128
+ *   rank_out    0, 16, ..., 128; M*rank_out*4 < 2^31
  *   codes_out   out u8 [M, N/2]; scales_out out fp16 [M, N/64];
  *   xl1_out     out fp32 [M, rank_out] (NULL iff rank_out == 0)
  * No output may overlap an input or another output.
@@ -251,7 +256,13 @@ int64_t svdq_lowrank_workspace_bytes(int64_t N, int64_t K, int rank, int oversam
  *   residual    out fp32 [N, K] (also the smoothed-weight workspace)
  *   work        device workspace of work_bytes >= svdq_lowrank_workspace_bytes()
  * The outputs depend on omega and on floating-point order; the product
- * L1 L2 approaches the exact rank-r truncation as iters grows.
+ * L1 L2 approaches the exact rank-r truncation as iters grows.  A rank-deficient
+ * W_hat is valid input: the first CholeskyQR pass shifts the Gram matrix's
+ * diagonal by 1e-6 of its mean, so every pivot stays positive and the basis
+ * vectors beyond the rank are rounding noise, to which Rayleigh-Ritz gives
+ * singular values near zero (for a W_hat of rank below `rank`, L1 L2 reproduces
+ * it).  A pivot that is not positive (an all-zero W_hat) zeroes its basis
+ * vector, so an all-zero W_hat gives all-zero factors and residual.
  */
 svdq_status svdq_lowrank_decompose(int64_t N, int64_t K, int rank, int oversample, int iters, const void* w,
                                    const void* smooth, const float* omega, void* l1t, void* l2t, float* residual,
@@ -305,6 +316,16 @@ int svdq_abi_version(void);
  * test prove that a non-gfx950 device gets SVDQ_ERR_UNSUPPORTED and no launch.
  */
 void svdq_test_set_arch_override(const char* arch);
+
+/*
+ * Test hook: `on` != 0 makes every later int4 svdq_w4a4_gemm run its one-copy
+ * kernel instance, also on a grid of at most one 128x128 tile per compute unit
+ * (which otherwise runs a K-split instance: two copies of the workgroup, each
+ * over half of K).  Lets a test compare both instances on a small shape; 0
+ * restores the automatic choice.  Results differ between the instances only in
+ * the fp32 summation order.
+ */
+void svdq_test_set_no_ksplit(int on);
 
 #ifdef __cplusplus
 }

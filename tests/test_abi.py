@@ -214,3 +214,31 @@ def test_offline_entry_points_validation(L):
     assert L.awq_quantize_weight(64, 128, 256, A, 2 * A, 3 * A, 4 * A, None) == UNSUPPORTED
     assert L.awq_quantize_weight(32, 128, 256, A, 2 * A, 3 * A, 4 * A, None) == UNSUPPORTED
     assert L.awq_quantize_weight(64, 128, 256, A, A, 3 * A, 4 * A, None) == INVALID
+
+
+def test_offset_and_k_limits(L):
+    B = 1 << 36  # fake buffers far enough apart not to overlap at these sizes
+    big = dict(ac=B, as_=2 * B, wc=3 * B, ws=4 * B, xl1=5 * B, l2t=6 * B, bias=7 * B, y=8 * B)
+    # the GEMMs take K up to 32768, the largest K they are parity-tested at
+    assert gemm(L, K=32768, **big) == UNSUPPORTED and b"gfx942" in L.svdq_last_error()
+    assert gemm(L, K=32768 + 64, **big) == UNSUPPORTED and b"32768" in L.svdq_last_error()
+    # xl1 [M, rank] fp32 and l2t [N, rank] bf16 are addressed with 32-bit byte offsets
+    assert gemm(L, M=1 << 22, N=128, K=64, r=128, **big) == UNSUPPORTED and b"rank" in L.svdq_last_error()
+    assert gemm(L, M=(1 << 22) - 1, N=128, K=64, r=128, **big) == UNSUPPORTED and b"gfx942" in L.svdq_last_error()
+    assert gemm(L, M=64, N=1 << 23, K=64, r=128, **big) == UNSUPPORTED and b"rank" in L.svdq_last_error()
+    bq = dict(x=B, smooth=2 * B, l1t=3 * B, codes=4 * B, scales=5 * B, xl1=6 * B)
+    assert q(L, M=1 << 22, K=64, r=128, **bq) == UNSUPPORTED and b"rank" in L.svdq_last_error()
+    assert q(L, M=(1 << 22) - 1, K=64, r=128, **bq) == UNSUPPORTED and b"gfx942" in L.svdq_last_error()
+    assert mlp(L, M=1 << 22, N=128, K=64, r=0, ac=B, as_=2 * B, wc=3 * B, ws=4 * B, xl1=None, l2t=None, bias=7 * B,
+               lam=9 * B, l1t=10 * B, ro=128, co=11 * B, so=12 * B, xo=13 * B) == UNSUPPORTED
+    assert b"rank_out" in L.svdq_last_error()
+
+
+def test_nvfp4_global_scale_product(L):
+    # each scale is valid alone, but the factor fl32(alpha_a * alpha_w) the
+    # epilogue applies overflows or underflows
+    assert gemm(L, prec=1, G=16, aa=1e20, aw=1e20) == INVALID and b"normal" in L.svdq_last_error()
+    assert gemm(L, prec=1, G=16, aa=1e-20, aw=1e-20) == INVALID
+    assert gemm(L, prec=1, G=16, aa=1e-18, aw=1e-18) == UNSUPPORTED      # 1e-36 is normal: valid
+    assert qkv(L, prec=1, G=16, aa=3e38, aw=2.0) == INVALID
+    assert gemm(L, prec=0, G=64, aa=1e20, aw=1e20) == UNSUPPORTED        # int4 ignores them

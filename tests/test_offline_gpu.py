@@ -118,3 +118,35 @@ def test_offline_to_online_roundtrip():
     e = np.linalg.norm(synth.bf16_bits_to_f64(bits(y)) - yd) / np.linalg.norm(yd)
     print(f"[offline] W4A4 layer vs dense: relative Frobenius error {e:.3g}", flush=True)
     assert e <= 0.1
+
+
+@pytest.mark.parametrize("kind", ["rank8", "zero"])
+def test_lowrank_decompose_rank_deficient(kind):
+    # a weight of rank 8 decomposed at rank 16 (the branch reproduces it, the
+    # residual is rounding), and an all-zero weight (zero factors, no NaN)
+    N, K, rank = 640, 384, 16
+    print(f"[offline] lowrank rank-deficient {kind}", flush=True)
+    d = synth.dense_layer(4006, N, K, planted_rank=0)
+    if kind == "rank8":
+        g = np.random.default_rng(4007)
+        w = (g.standard_normal((N, 8)) @ g.standard_normal((8, K))) * 0.05
+    else:
+        w = np.zeros((N, K))
+    wb = synth.to_bf16_bits(w)
+    lam_b = oracle.calibrate_smooth(d["x_cal"], wb)
+    l1t, l2t, res = sq.lowrank_decompose(b16(wb), b16(lam_b), dev(d["omega"][:, :rank + 16]), rank, iters=4)
+    torch.cuda.synchronize()
+    l1 = synth.bf16_bits_to_f64(bits(l1t)).T
+    l2 = synth.bf16_bits_to_f64(bits(l2t)).T
+    R = res.cpu().numpy().astype(np.float64)
+    lam = synth.bf16_bits_to_f64(lam_b)
+    assert np.isfinite(l1).all() and np.isfinite(l2).all() and np.isfinite(R).all()
+    w_hat = synth.bf16_bits_to_f64(wb) * lam[None, :]
+    prod = ((lam[:, None] * l1) @ l2).T
+    if kind == "zero":
+        assert not prod.any() and not R.any()
+    else:
+        e = np.linalg.norm(prod - w_hat) / np.linalg.norm(w_hat)
+        print(f"[offline] rank-8 weight: branch rel err {e:.3g}", flush=True)
+        assert e <= 1e-2
+        assert np.linalg.norm(R) <= 1e-2 * np.linalg.norm(w_hat)
