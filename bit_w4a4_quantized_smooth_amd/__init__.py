@@ -30,6 +30,7 @@ _STATUS = {0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARG", 2: "SVDQ_ERR_UNSUPPORTED",
 
 EXPORTS = ["svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_qkv_norm_rope", "svdq_w4a4_gemm_gelu_quant",
            "awq_w4a16_gemv", "svdq_calibrate_smooth", "svdq_lowrank_workspace_bytes", "svdq_lowrank_decompose",
+           "svdq_lowrank_decompose_noalloc",
            "svdq_quantize_weight", "awq_quantize_weight",
            "svdq_w4a4_group_psums", "svdq_last_error", "svdq_abi_version", "svdq_test_set_arch_override",
            "svdq_test_set_no_ksplit"]
@@ -65,12 +66,13 @@ def lib() -> ctypes.CDLL:
         L.svdq_lowrank_workspace_bytes.argtypes = [i64, i64, i32, i32]
         L.svdq_lowrank_workspace_bytes.restype = i64
         L.svdq_lowrank_decompose.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp]
+        L.svdq_lowrank_decompose_noalloc.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.svdq_quantize_weight.argtypes = [i32, i32, i64, i64, vp, f32, vp, vp, vp]
         L.awq_quantize_weight.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
         L.svdq_w4a4_group_psums.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp]
         for f in ("svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_qkv_norm_rope",
                   "svdq_w4a4_gemm_gelu_quant", "awq_w4a16_gemv", "svdq_w4a4_group_psums", "svdq_calibrate_smooth",
-                  "svdq_lowrank_decompose", "svdq_quantize_weight",
+                  "svdq_lowrank_decompose", "svdq_lowrank_decompose_noalloc", "svdq_quantize_weight",
                   "awq_quantize_weight"):
             getattr(L, f).restype = i32
         L.svdq_last_error.restype = ctypes.c_char_p

@@ -101,6 +101,10 @@ struct LowrankArgs {
 hipError_t launch_quantize_act(const QuantArgs& a, hipStream_t st);
 hipError_t launch_calibrate(int64_t Mc, int64_t N, int64_t K, const void* x, const void* w, void* lam, hipStream_t st);
 size_t lowrank_workspace_bytes(int64_t N, int64_t K, int p);
+// The allocation-free decomposition's fixed workspace: its size, and its device
+// address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_lowrank(const LowrankArgs& a, hipStream_t st);
 hipError_t launch_quantize_weight(int precision, int64_t N, int64_t K, const float* r, float alpha, void* codes,
                                   void* scales, hipStream_t st);

@@ -22,6 +22,8 @@
 // that layer checked.
 #pragma clang fp contract(off)
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -478,6 +480,30 @@ __global__ __launch_bounds__(256) void awq_weight_kernel(int N, int K, const uin
 inline unsigned blocks_for(size_t n, unsigned per) { return (unsigned)((n + per - 1) / per); }
 
 }  // namespace
+
+// Fixed workspace of the allocation-free decomposition entry point: one copy
+// per GPU, held until the process ends.  Host code never uses this name as an
+// address (on the host it is only a stand-in for the symbol); the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t lowrank_workspace_bytes(int64_t N, int64_t K, int p) {
   const int64_t rows = N > K ? N : K;

@@ -353,9 +353,9 @@ int64_t svdq_lowrank_workspace_bytes(int64_t N, int64_t K, int rank, int oversam
   return (int64_t)svdq::lowrank_workspace_bytes(N, K, rank + oversample);
 }
 
-svdq_status svdq_lowrank_decompose(int64_t N, int64_t K, int rank, int oversample, int iters, const void* w,
-                                   const void* smooth, const float* omega, void* l1t, void* l2t, float* residual,
-                                   void* work, int64_t work_bytes, void* stream) {
+static svdq_status lowrank_common(int64_t N, int64_t K, int rank, int oversample, int iters, const void* w,
+                                  const void* smooth, const float* omega, void* l1t, void* l2t, float* residual,
+                                  void* work, int64_t work_bytes, void* stream) {
   if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || K % 64 != 0)
     return fail(SVDQ_ERR_INVALID_ARG, "bad shape N=%lld K=%lld (K %% 64 == 0)", (long long)N, (long long)K);
   if (N * K > ((int64_t)1 << 31)) return fail(SVDQ_ERR_UNSUPPORTED, "N*K above 2^31");
@@ -364,15 +364,23 @@ svdq_status svdq_lowrank_decompose(int64_t N, int64_t K, int rank, int oversampl
     return fail(SVDQ_ERR_UNSUPPORTED, "rank %d (multiple of 16) + oversample %d must be <= 64 and <= min(N, K)",
                 rank, oversample);
   if (iters < 0 || iters > 64) return fail(SVDQ_ERR_INVALID_ARG, "iters %d not in [0, 64]", iters);
-  if (!w || !omega || !l1t || !l2t || !residual || !work)
-    return fail(SVDQ_ERR_INVALID_ARG, "w, omega, l1t, l2t, residual and work are required");
+  if (!w || !omega || !l1t || !l2t || !residual)
+    return fail(SVDQ_ERR_INVALID_ARG, "w, omega, l1t, l2t and residual are required");
+  const bool noalloc = work == nullptr && work_bytes < 0;  // the allocation-free entry
+  if (!work && !noalloc) return fail(SVDQ_ERR_INVALID_ARG, "work is required");
   const int p = rank + oversample;
-  if (work_bytes < (int64_t)svdq::lowrank_workspace_bytes(N, K, p))
+  const int64_t need = (int64_t)svdq::lowrank_workspace_bytes(N, K, p);
+  if (noalloc) {
+    if (need > (int64_t)svdq::kNoAllocScratchBytes)
+      return fail(SVDQ_ERR_UNSUPPORTED, "workspace of %lld bytes above the allocation-free limit of %lld bytes",
+                  (long long)need, (long long)svdq::kNoAllocScratchBytes);
+  } else if (work_bytes < need) {
     return fail(SVDQ_ERR_INVALID_ARG, "work_bytes %lld below svdq_lowrank_workspace_bytes()", (long long)work_bytes);
+  }
   if (!aligned16(w) || !aligned16(smooth) || !aligned16(omega) || !aligned16(l1t) || !aligned16(l2t) ||
       !aligned16(residual) || !aligned16(work))
     return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
-  const size_t nr = (size_t)N * K * 4, nw = (size_t)work_bytes, n1 = (size_t)rank * K * 2, n2 = (size_t)N * rank * 2;
+  const size_t nr = (size_t)N * K * 4, nw = noalloc ? 0 : (size_t)work_bytes, n1 = (size_t)rank * K * 2, n2 = (size_t)N * rank * 2;
   const void* outs[] = {l1t, l2t, residual, work};
   const size_t nouts[] = {n1, n2, nr, nw};
   const void* ins[] = {w, smooth, omega};
@@ -386,8 +394,27 @@ svdq_status svdq_lowrank_decompose(int64_t N, int64_t K, int rank, int oversampl
   svdq_status s;
   if ((s = check_arch()) != SVDQ_OK) return s;
   if ((s = check_sticky()) != SVDQ_OK) return s;
+  if (noalloc) {
+    const hipError_t e = svdq::noalloc_scratch(&work);
+    if (e != hipSuccess) return fail(SVDQ_ERR_DEVICE, "scratch address: %s", hipGetErrorString(e));
+  }
   svdq::LowrankArgs a{N, K, rank, p, iters, w, smooth, omega, l1t, l2t, residual, work};
   return launched(svdq::launch_lowrank(a, (hipStream_t)stream));
+}
+
+svdq_status svdq_lowrank_decompose(int64_t N, int64_t K, int rank, int oversample, int iters, const void* w,
+                                   const void* smooth, const float* omega, void* l1t, void* l2t, float* residual,
+                                   void* work, int64_t work_bytes, void* stream) {
+  if (!work) return fail(SVDQ_ERR_INVALID_ARG, "work is required");
+  if (work_bytes < 0) return fail(SVDQ_ERR_INVALID_ARG, "work_bytes must be >= 0");
+  return lowrank_common(N, K, rank, oversample, iters, w, smooth, omega, l1t, l2t, residual, work, work_bytes,
+                        stream);
+}
+
+svdq_status svdq_lowrank_decompose_noalloc(int64_t N, int64_t K, int rank, int oversample, int iters,
+                                           const void* w, const void* smooth, const float* omega, void* l1t,
+                                           void* l2t, float* residual, void* stream) {
+  return lowrank_common(N, K, rank, oversample, iters, w, smooth, omega, l1t, l2t, residual, nullptr, -1, stream);
 }
 
 svdq_status svdq_quantize_weight(int precision, int group_size, int64_t N, int64_t K, const float* residual,

@@ -269,6 +269,23 @@ svdq_status svdq_lowrank_decompose(int64_t N, int64_t K, int rank, int oversampl
                                    void* work, int64_t work_bytes, void* stream);
 
 /*
+ * svdq_lowrank_decompose_noalloc -- svdq_lowrank_decompose without the `work`
+ * argument and without any allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, kernels and results (bit for bit) as
+ * svdq_lowrank_decompose; the workspace is the library's fixed per-GPU scratch
+ * area of 16 MiB (held on each GPU the library runs on until the process
+ * ends), so sizes whose svdq_lowrank_workspace_bytes() exceeds 16 MiB are
+ * rejected with SVDQ_ERR_UNSUPPORTED.  Every call on a GPU uses that GPU's one
+ * scratch area: calls that overlap on one GPU (on different streams, or from
+ * several threads) race and must not be issued; calls in sequence on one
+ * stream are fine (every part of the workspace is written before it is read).
+ */
+svdq_status svdq_lowrank_decompose_noalloc(int64_t N, int64_t K, int rank, int oversample, int iters,
+                                           const void* w, const void* smooth, const float* omega, void* l1t,
+                                           void* l2t, float* residual, void* stream);
+
+/*
  * svdq_quantize_weight -- the 4-bit residual weight, per (row n, group):
  *   int4 (group 64):  s = fp16_sat(fl32(amax / 7)), q = clamp(rne(fl32(r * fl32(1/s))), -8, 7)
  *   nvfp4 (group 16): s = e4m3_sat(fl32(amax / fl32(6 * alpha_w))),

@@ -242,3 +242,16 @@ def test_nvfp4_global_scale_product(L):
     assert gemm(L, prec=1, G=16, aa=1e-18, aw=1e-18) == UNSUPPORTED      # 1e-36 is normal: valid
     assert qkv(L, prec=1, G=16, aa=3e38, aw=2.0) == INVALID
     assert gemm(L, prec=0, G=64, aa=1e20, aw=1e20) == UNSUPPORTED        # int4 ignores them
+
+
+def test_noalloc_decompose_limits(L):
+    B = 1 << 40
+    na = lambda N, K, r=32, os=16: L.svdq_lowrank_decompose_noalloc(N, K, r, os, 4, B, 2 * B, 3 * B, 4 * B, 5 * B,
+                                                                    6 * B, None)
+    assert na(1536, 768) == UNSUPPORTED and b"gfx942" in L.svdq_last_error()    # fits: reaches the arch check
+    # a workspace above the fixed 16 MiB scratch is rejected, not run
+    assert L.svdq_lowrank_workspace_bytes(1 << 17, 3072, 48, 16) > (16 << 20)
+    assert na(1 << 17, 3072, 48, 16) == UNSUPPORTED and b"allocation-free limit" in L.svdq_last_error()
+    assert na(1536, 768, r=24) == UNSUPPORTED                                   # the same rank rules
+    assert L.svdq_lowrank_decompose_noalloc(1536, 768, 32, 16, 4, None, 2 * B, 3 * B, 4 * B, 5 * B, 6 * B,
+                                            None) == INVALID
