@@ -309,10 +309,22 @@ AWQ = {
     "awq_3x8192x1024": lambda: synth.awq_layer(25, 3, 8192, 1024),
     "awq_2x3072x8192": lambda: synth.awq_layer(26, 2, 3072, 8192),
     "awq_4x192x1536": lambda: synth.awq_layer(27, 4, 192, 1536, with_bias=False),
-    # matrix-core kernel with an odd group count (a last stage of one group)
-    # and an odd number of two-group stages
+    # K not a multiple of 512 (the LDS-staged matrix-core kernel): an odd
+    # group count (a last stage of one group), an odd number of two-group
+    # stages, and many 64-row workgroups
     "awq_7x320x1088": lambda: synth.awq_layer(28, 7, 320, 1088),
     "awq_64x256x192": lambda: synth.awq_layer(29, 64, 256, 192),
+    "awq_8x24576x256": lambda: synth.awq_layer(30, 8, 24576, 256),
+    # streamed kernel: 34 chunks of K (more than the ring holds) on 8 CUs
+    "awq_6x128x17408": lambda: synth.awq_layer(31, 6, 128, 17408),
+    "awq_33x4096x3072_nobias": lambda: synth.awq_layer(32, 33, 4096, 3072, with_bias=False),
+    # the streamed kernel's batch shapes on 256 CUs: 4 units per workgroup,
+    # 5 + 3 (two batches), 5 units at two m-blocks, 2 at three, 2-3 (ragged)
+    "awq_16x16384x1024": lambda: synth.awq_layer(33, 16, 16384, 1024),
+    "awq_8x32768x512": lambda: synth.awq_layer(34, 8, 32768, 512),
+    "awq_24x20480x512": lambda: synth.awq_layer(35, 24, 20480, 512),
+    "awq_48x8192x2048": lambda: synth.awq_layer(36, 48, 8192, 2048),
+    "awq_12x9216x1536": lambda: synth.awq_layer(37, 12, 9216, 1536),
 }
 
 
