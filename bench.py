@@ -489,9 +489,11 @@ def cpu_baseline(lin, rows, synth):
     small = synth.WORKLOADS["svdq_int4_256x512x512_r16"]()
     per["svdq_int4_256x512x512_r16_1thread"] = linear(small, small["M"], 1)
     per["svdq_int4_256x512x512_r16"] = linear(small, small["M"], nthreads)
-    for name in ("dit_mlp_up_int4_4608x12288x3072_r32", "dit_mlp_down_int4_4608x3072x12288_r32",
-                 "dit_qkv_nvfp4_4608x9216x3072_r32"):
-        per[name] = linear(synth.WORKLOADS[name](), 576, nthreads)
+    # row counts sized to a few seconds each (the NVFP4 oracle decodes E2M1 and
+    # E4M3 per product, about four times the int4 cost per row)
+    for name, r in (("dit_mlp_up_int4_4608x12288x3072_r32", 576), ("dit_mlp_down_int4_4608x3072x12288_r32", 576),
+                    ("dit_qkv_nvfp4_4608x9216x3072_r32", 144)):
+        per[name] = linear(synth.WORKLOADS[name](), r, nthreads)
     for name in ("awq_mod_2x18432x3072", "awq_mod_64x18432x3072"):
         d = synth.WORKLOADS[name]()
         t0 = time.perf_counter()

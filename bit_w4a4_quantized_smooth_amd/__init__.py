@@ -21,7 +21,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsvdq.so")
+# SVDQ_LIB: another build of the library (the sanitizer test loads a
+# host-only ASan/UBSan build of the C ABI layer this way)
+LIB_PATH = os.environ.get("SVDQ_LIB") or os.path.join(_HERE, "libsvdq.so")
 
 SVDQ_INT4, SVDQ_NVFP4 = 0, 1
 GROUP = {SVDQ_INT4: 64, SVDQ_NVFP4: 16}

@@ -61,18 +61,7 @@ typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 
 // Tile configuration: WAVES_N x WAVES_M waves, each owning a (16*BI) x (16*BJ)
 // tile of 16x16 blocks; KG 64-channel groups per pipeline stage.
-#ifndef SVDQ_INT4_CFG
-#define SVDQ_INT4_CFG 0
-#endif
-#if SVDQ_INT4_CFG == 0
 constexpr int WAVES_N = 2, WAVES_M = 2, BI = 4, BJ = 4, KG = 2;
-#elif SVDQ_INT4_CFG == 1
-constexpr int WAVES_N = 2, WAVES_M = 2, BI = 8, BJ = 4, KG = 2;
-#elif SVDQ_INT4_CFG == 2
-constexpr int WAVES_N = 2, WAVES_M = 2, BI = 4, BJ = 8, KG = 2;
-#elif SVDQ_INT4_CFG == 3
-constexpr int WAVES_N = 4, WAVES_M = 2, BI = 4, BJ = 4, KG = 2;
-#endif
 
 namespace {
 constexpr int BN = WAVES_N * BI * 16, BM = WAVES_M * BJ * 16;

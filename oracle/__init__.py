@@ -24,9 +24,14 @@ INT4, NVFP4 = 0, 1
 def _lib():
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        _LIB = ctypes.CDLL(_build.LIB)
+        # SVDQ_ORACLE_LIB: another build of svdq_oracle.cpp (the sanitizer
+        # test loads an ASan/UBSan build this way)
+        path = os.environ.get("SVDQ_ORACLE_LIB")
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        _LIB = ctypes.CDLL(path)
     return _LIB
 
 
