@@ -439,20 +439,21 @@ def extras(args, torch, sq, synth, t, bf, f16, stream):
         "awq_quantize_GBps": round(aq_bytes / (aq_ms * 1e-3) / 1e9, 1)}
     del d, w, xc, om, lam, dec, resid, wa
 
-    # AWQ at M=64 over >= 512 MB of weight copies
+    # AWQ at M=16 and M=64 (the streamed matrix-core kernel) over >= 512 MB of weight copies
     d = synth.awq_layer(1005, 64, 18432, 3072)
     A = max(1, args.awq_copies)
-    x = bf(d["x"])
     wc = [t(d["w_codes"]) for _ in range(A)]
     ws = [f16(d["w_scales"]) for _ in range(A)]
     wz = [f16(d["w_zeros"]) for _ in range(A)]
     b = bf(d["bias"])
-    y = torch.empty((64, 18432), dtype=torch.bfloat16, device=dev)
-    ms = median_ms(lambda i: sq.awq_gemv(x, wc[i % A], ws[i % A], wz[i % A], b, out=y, stream=stream),
-                   n, stream, torch)
-    byts = 18432 * 3072 // 2 + 2 * 18432 * 48 * 2 + 64 * 3072 * 2 + 18432 * 2 + 64 * 18432 * 2
-    res["awq_m64"] = {"ms": round(ms, 5), "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
-                      "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    for m in (16, 64):
+        x = bf(d["x"][:m])
+        y = torch.empty((m, 18432), dtype=torch.bfloat16, device=dev)
+        ms = median_ms(lambda i: sq.awq_gemv(x, wc[i % A], ws[i % A], wz[i % A], b, out=y, stream=stream),
+                       n, stream, torch)
+        byts = 18432 * 3072 // 2 + 2 * 18432 * 48 * 2 + m * 3072 * 2 + 18432 * 2 + m * 18432 * 2
+        res[f"awq_m{m}"] = {"ms": round(ms, 5), "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del wc, ws, wz
 
     # attainable HBM: a 1 GiB device-to-device copy (read + write)
