@@ -5,14 +5,16 @@ The pages say the quantized linear layers work under torch.compile ("Nunchaku
 Lite", section "torch.compile"; blog "Nunchaku 4-bit inference in Diffusers",
 "Benchmarks").  Here each library entry point becomes one opaque operator
 (`svdq::quantize_act`, `svdq::w4a4_gemm`, `svdq::w4a4_gemm_qkv_norm_rope`,
-`svdq::awq_gemv`) with a fake
+`svdq::w4a4_gemm_gelu_quant`, `svdq::awq_gemv`) with a fake
 (meta) implementation that only computes output shapes and dtypes, so the
 tracer never runs a kernel; the real implementation is the ctypes call into
 libsvdq.so on the tensors' current stream.  Nothing here computes: every
 arithmetic step stays in the library's kernels.
 
-`SVDQLinear` and `AWQLinear` are nn.Modules holding the packed layer tensors
-(as buffers) whose forward uses these operators.
+`SVDQLinear`, `SVDQMLP` and `AWQLinear` are nn.Modules holding the packed
+layer tensors (as buffers) whose forward uses these operators; `SVDQMLP` is
+the DiT MLP with the fused up-projection ("Nunchaku Lite", "Fused kernels":
+the GELU-MLP fusion), three operators per call.
 """
 from __future__ import annotations
 
@@ -21,7 +23,8 @@ from typing import Optional, Tuple
 import torch
 from torch import Tensor
 
-from . import SVDQ_INT4, SVDQ_NVFP4, GROUP, awq_gemv, quantize_act, w4a4_gemm, w4a4_gemm_qkv_norm_rope
+from . import (SVDQ_INT4, SVDQ_NVFP4, GROUP, awq_gemv, quantize_act, w4a4_gemm, w4a4_gemm_gelu_quant,
+               w4a4_gemm_qkv_norm_rope)
 
 _SCALE_DTYPE = {SVDQ_INT4: torch.float16, SVDQ_NVFP4: torch.uint8}
 
@@ -80,6 +83,31 @@ def _(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, norm_q, norm_k, 
     return act_codes.new_empty((act_codes.shape[0], 3 * heads * head_dim), dtype=torch.bfloat16)
 
 
+@torch.library.custom_op("svdq::w4a4_gemm_gelu_quant", mutates_args=())
+def w4a4_gemm_gelu_quant_op(act_codes: Tensor, act_scales: Tensor, w_codes: Tensor, w_scales: Tensor,
+                            xl1: Optional[Tensor], l2t: Optional[Tensor], bias: Optional[Tensor],
+                            smooth_out: Optional[Tensor], l1t_out: Optional[Tensor]) -> Tuple[Tensor, Tensor, Tensor]:
+    """svdq_w4a4_gemm_gelu_quant (int4): the MLP up-projection, GELU and the down
+    projection's activation quantization; returns (codes u8 [M, N/2], scales fp16
+    [M, N/64], xl1 fp32 [M, r_out]), r_out = 0 giving an empty xl1."""
+    if xl1 is not None and xl1.shape[1] == 0:
+        xl1 = None
+    codes, scales, xo = w4a4_gemm_gelu_quant(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias,
+                                             smooth_out, l1t_out)
+    if xo is None:
+        xo = act_codes.new_empty((act_codes.shape[0], 0), dtype=torch.float32)
+    return codes, scales, xo
+
+
+@w4a4_gemm_gelu_quant_op.register_fake
+def _(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, smooth_out, l1t_out):
+    M, N = act_codes.shape[0], w_codes.shape[0]
+    ro = 0 if l1t_out is None else l1t_out.shape[0]
+    return (act_codes.new_empty((M, N // 2), dtype=torch.uint8),
+            act_codes.new_empty((M, N // 64), dtype=torch.float16),
+            act_codes.new_empty((M, ro), dtype=torch.float32))
+
+
 @torch.library.custom_op("svdq::awq_gemv", mutates_args=())
 def awq_gemv_op(x: Tensor, w_codes: Tensor, w_scales: Tensor, w_zeros: Tensor, bias: Optional[Tensor]) -> Tensor:
     """awq_w4a16_gemv: y bf16 [M, N]."""
@@ -128,6 +156,31 @@ class SVDQLinear(torch.nn.Module):
     def forward(self, x: Tensor) -> Tensor:
         return svdq_linear(x, self.smooth, self.l1t, self.w_codes, self.w_scales, self.l2t, self.bias,
                            self.precision, self.act_global_scale, self.w_global_scale)
+
+
+class SVDQMLP(torch.nn.Module):
+    """The DiT MLP dim -> hidden -> dim in SVDQuant W4A4 int4 form, with the
+    up-projection, GELU and the down projection's activation quantization (and
+    its low-rank input XL1) fused in one kernel: quantize_act, then
+    w4a4_gemm_gelu_quant, then w4a4_gemm.  `up` and `down` hold the two layers'
+    tensors as SVDQLinear does; the down layer's smoothing factor and L1^T are
+    consumed by the fused kernel, its codes, scales, L2^T and bias by the GEMM."""
+
+    def __init__(self, dim: int, hidden: int, rank: int = 32, bias: bool = True, device=None):
+        super().__init__()
+        self.up = SVDQLinear(dim, hidden, rank=rank, precision=SVDQ_INT4, bias=bias, device=device)
+        self.down = SVDQLinear(hidden, dim, rank=rank, precision=SVDQ_INT4, bias=bias, device=device)
+
+    def forward(self, x: Tensor) -> Tensor:
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1])
+        up, down = self.up, self.down
+        codes, scales, xl1 = torch.ops.svdq.quantize_act(x2, up.smooth, up.l1t, SVDQ_INT4, 1.0)
+        hc, hs, hx = torch.ops.svdq.w4a4_gemm_gelu_quant(codes, scales, up.w_codes, up.w_scales, xl1, up.l2t,
+                                                         up.bias, down.smooth, down.l1t)
+        y = torch.ops.svdq.w4a4_gemm(hc, hs, down.w_codes, down.w_scales, hx, down.l2t, down.bias, SVDQ_INT4,
+                                     1.0, 1.0)
+        return y.reshape(*lead, down.out_features)
 
 
 class AWQLinear(torch.nn.Module):

@@ -107,3 +107,49 @@ def test_module_against_oracle(prec):
                                 alpha_a=d["alpha_a"], alpha_w=d["alpha_w"])
     got = synth.bf16_bits_to_f64(y.reshape(80, 384).cpu().view(torch.int16).numpy().view(np.uint16))
     assert np.max(np.abs(got - ref)) / np.max(np.abs(ref)) <= 1e-2
+
+
+def _mlp_module(case):
+    up, dn = case["up"], case["down"]
+    m = ops.SVDQMLP(up["K"], up["N"], rank=up["rank"], device="cuda")
+    for lin, d in ((m.up, up), (m.down, dn)):
+        if "lam" in d:
+            lin.smooth.copy_(_t(d["lam"], torch.bfloat16))
+        lin.w_codes.copy_(_t(d["w_codes"], torch.uint8))
+        lin.w_scales.copy_(_t(d["w_scales"], torch.float16))
+        lin.l1t.copy_(_t(d["l1t"], torch.bfloat16))
+        lin.l2t.copy_(_t(d["l2t"], torch.bfloat16))
+        lin.bias.copy_(_t(d["bias"], torch.bfloat16))
+    return m
+
+
+def test_mlp_op_and_module():
+    # 96 tokens, 256 -> 512 -> 256, rank 16: opcheck of the fused operator,
+    # the compiled module bit-equal to eager, and the module's output against the
+    # oracle's down projection of the fused kernel's own codes, scales and XL1
+    # (the fused quantization itself is compared in tests/test_mlp_gpu.py)
+    print("[ops] SVDQMLP", flush=True)
+    case = synth.mlp_layer(61, 96, 512, 256, 16)
+    up, dn = case["up"], case["down"]
+    m = _mlp_module(case)
+    x = _t(up["x"], torch.bfloat16)
+    codes, scales, xl1 = torch.ops.svdq.quantize_act(x, m.up.smooth, m.up.l1t, sq.SVDQ_INT4, 1.0)
+    torch.library.opcheck(torch.ops.svdq.w4a4_gemm_gelu_quant.default,
+                          (codes, scales, m.up.w_codes, m.up.w_scales, xl1, m.up.l2t, m.up.bias, m.down.smooth,
+                           m.down.l1t))
+    y_eager = m(x.reshape(2, 48, 256))
+    torch._dynamo.reset()
+    compiled = torch.compile(m, fullgraph=True, backend="aot_eager")
+    for _ in range(2):
+        y_comp = compiled(x.reshape(2, 48, 256))
+        torch.cuda.synchronize()
+        assert torch.equal(y_comp.view(torch.int16), y_eager.view(torch.int16))
+    hc, hs, hx = torch.ops.svdq.w4a4_gemm_gelu_quant(codes, scales, m.up.w_codes, m.up.w_scales, xl1, m.up.l2t,
+                                                     m.up.bias, m.down.smooth, m.down.l1t)
+    torch.cuda.synchronize()
+    ref, _ = oracle.w4a4_linear(0, hc.cpu().numpy(), hs.cpu().view(torch.int16).numpy().view(np.uint16),
+                                dn["w_codes"], dn["w_scales"], hx.cpu().numpy(), dn["l2t"], dn["bias"])
+    got = synth.bf16_bits_to_f64(y_eager.reshape(96, 256).cpu().view(torch.int16).numpy().view(np.uint16))
+    e = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+    print(f"[ops] SVDQMLP vs oracle on the fused outputs: max-abs-rel {e:.2e}", flush=True)
+    assert e <= 1e-2

@@ -1,4 +1,5 @@
-"""The torch custom-op layer (svdq::quantize_act, svdq::w4a4_gemm, svdq::awq_gemv):
+"""The torch custom-op layer (svdq::quantize_act, svdq::w4a4_gemm,
+svdq::w4a4_gemm_qkv_norm_rope, svdq::w4a4_gemm_gelu_quant, svdq::awq_gemv):
 fake implementations give the shapes and dtypes the C ABI documents, and a
 module built on them traces as one graph (torch.export in strict mode goes
 through the same frontend as torch.compile(fullgraph=True)).  Tracing uses
@@ -80,3 +81,30 @@ def test_fake_qkv():
             None, torch.empty(128, dtype=torch.bfloat16), torch.empty(128, dtype=torch.bfloat16),
             torch.empty(4608, 64, 2), 24, 128, 1e-6, sq.SVDQ_INT4, 1.0, 1.0)
         assert (y.shape, y.dtype) == ((4608, 9216), torch.bfloat16)
+
+
+@pytest.mark.parametrize("ro", [0, 32])
+def test_fake_gelu_quant(ro):
+    M, K, N = 96, 256, 512
+    with FakeTensorMode():
+        codes = torch.empty(M, K // 2, dtype=torch.uint8)
+        scales = torch.empty(M, K // 64, dtype=torch.float16)
+        hc, hs, hx = torch.ops.svdq.w4a4_gemm_gelu_quant(
+            codes, scales, torch.empty(N, K // 2, dtype=torch.uint8), torch.empty(N, K // 64, dtype=torch.float16),
+            torch.empty(M, 16), torch.empty(N, 16, dtype=torch.bfloat16), None,
+            torch.empty(N, dtype=torch.bfloat16), torch.empty(ro, N, dtype=torch.bfloat16) if ro else None)
+        assert (hc.shape, hc.dtype) == ((M, N // 2), torch.uint8)
+        assert (hs.shape, hs.dtype) == ((M, N // 64), torch.float16)
+        assert (hx.shape, hx.dtype) == ((M, ro), torch.float32)
+
+
+def test_export_mlp_full_graph():
+    m = ops.SVDQMLP(256, 1024, rank=16)
+    x = torch.zeros(2, 48, 256, dtype=torch.bfloat16)
+    ep = torch.export.export(m, (x,), strict=True)
+    targets = [n.target for n in ep.graph.nodes if n.op == "call_function"]
+    assert targets.count(torch.ops.svdq.quantize_act.default) == 1
+    assert targets.count(torch.ops.svdq.w4a4_gemm_gelu_quant.default) == 1
+    assert targets.count(torch.ops.svdq.w4a4_gemm.default) == 1
+    out = [n for n in ep.graph.nodes if n.op == "output"][0].args[0][0].meta["val"]
+    assert out.shape == (2, 48, 256) and out.dtype == torch.bfloat16
