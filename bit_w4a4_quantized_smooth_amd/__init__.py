@@ -62,7 +62,7 @@ def lib() -> ctypes.CDLL:
         L.svdq_w4a4_gemm_qkv_norm_rope.argtypes = [i32, i32, i32, i64, i32, i32, i64, vp, vp, f32, vp, vp,
                                                    f32, vp, vp, vp, vp, vp, f32, vp, i64, vp, vp]
         L.svdq_w4a4_gemm_gelu_quant.argtypes = [i32, i32, i32, i64, i64, i64, vp, vp, f32, vp, vp, f32, vp, vp,
-                                                vp, vp, vp, i32, vp, vp, vp, vp]
+                                                vp, vp, vp, i32, f32, vp, vp, vp, vp]
         L.awq_w4a16_gemv.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.svdq_calibrate_smooth.argtypes = [i64, i64, i64, vp, vp, vp, vp]
         L.svdq_lowrank_workspace_bytes.argtypes = [i64, i64, i32, i32]
@@ -227,25 +227,31 @@ def w4a4_gemm_qkv_norm_rope(precision: int, act_codes, act_scales, w_codes, w_sc
 
 
 def w4a4_gemm_gelu_quant(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, smooth_out=None,
-                         l1t_out=None, out=None, stream=None):
-    """svdq_w4a4_gemm_gelu_quant (int4): the MLP up-projection with GELU and the down
-    projection's quantization fused.  Returns (codes u8 [M, N/2], scales fp16 [M, N/64],
-    xl1 fp32 [M, r_out] or None); `out` may supply that triple preallocated."""
+                         l1t_out=None, out=None, stream=None, precision: int = SVDQ_INT4,
+                         act_global_scale: float = 1.0, w_global_scale: float = 1.0,
+                         out_global_scale: float = 1.0):
+    """svdq_w4a4_gemm_gelu_quant: the MLP up-projection with GELU and the down
+    projection's quantization fused (int4, or nvfp4 with the global scales of
+    the up projection and out_global_scale for the quantization of h).
+    Returns (codes u8 [M, N/2], scales [M, N/G] (fp16 for int4, E4M3 u8 for
+    nvfp4), xl1 fp32 [M, r_out] or None); `out` may supply that triple
+    preallocated."""
     fn = "w4a4_gemm_gelu_quant"
-    a, M, N, K, G, r = _gemm_args(fn, SVDQ_INT4, act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias)
+    a, M, N, K, G, r = _gemm_args(fn, precision, act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias)
     ro = 0 if l1t_out is None else _dims(fn, l1t_out, "l1t_out", 2)[0]
+    sdt = _scale_dtype(precision)
     if out is None:
         dev = act_codes.device
-        out = (torch.empty((M, N // 2), dtype=_U8, device=dev), torch.empty((M, N // 64), dtype=_F16, device=dev),
+        out = (torch.empty((M, N // 2), dtype=_U8, device=dev), torch.empty((M, N // G), dtype=sdt, device=dev),
                torch.empty((M, ro), dtype=_F32, device=dev) if ro else None)
     codes, scales, xo = out
     (a.req("smooth_out", smooth_out, _BF16, (N,), True).req("l1t_out", l1t_out, _BF16, (ro, N), True)
-     .req("codes_out", codes, _U8, (M, N // 2)).req("scales_out", scales, _F16, (M, N // 64))
+     .req("codes_out", codes, _U8, (M, N // 2)).req("scales_out", scales, sdt, (M, N // G))
      .req("xl1_out", xo, _F32, (M, ro), ro == 0).done())
     _check(lib().svdq_w4a4_gemm_gelu_quant(
-        SVDQ_INT4, 64, r, M, N, K, _ptr(act_codes), _ptr(act_scales), 1.0, _ptr(w_codes), _ptr(w_scales), 1.0,
-        _ptr(xl1), _ptr(l2t), _ptr(bias), _ptr(smooth_out), _ptr(l1t_out), ro, _ptr(codes), _ptr(scales),
-        _ptr(xo), _stream(stream)))
+        precision, G, r, M, N, K, _ptr(act_codes), _ptr(act_scales), float(act_global_scale), _ptr(w_codes),
+        _ptr(w_scales), float(w_global_scale), _ptr(xl1), _ptr(l2t), _ptr(bias), _ptr(smooth_out),
+        _ptr(l1t_out), ro, float(out_global_scale), _ptr(codes), _ptr(scales), _ptr(xo), _stream(stream)))
     return codes, scales, xo
 
 

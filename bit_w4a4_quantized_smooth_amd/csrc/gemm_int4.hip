@@ -668,7 +668,7 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
           *(uint16_t*)(ct + (16 * j + l16) * CROW + 8 * i + 2 * lg) = (uint16_t)w;
         }
         const int m = m0 + wm + 16 * j + l16;
-        if (lg == 0 && m < M) me.scales[(size_t)m * G2 + gd] = (uint16_t)sbits;
+        if (lg == 0 && m < M) ((uint16_t*)me.scales)[(size_t)m * G2 + gd] = (uint16_t)sbits;
       }
 #pragma unroll
       for (int rr = 0; rr < BJ * 16 * 2 / 64; ++rr) {  // 64 rows x 2 halves, 64 lanes per pass

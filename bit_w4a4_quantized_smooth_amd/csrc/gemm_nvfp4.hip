@@ -37,6 +37,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "mlp_epi.h"
 #include "qkv_epi.h"
 
 namespace svdq {
@@ -75,13 +76,16 @@ __device__ __forceinline__ void scale_pairs(u32 bits, h2& s0, h2& s1) {
 }  // namespace
 
 // MODE 0: Y; 1: fp32 partial products per 16-channel group; 2: Y of the fused
-// attention projection (Q/K RMSNorm and rotary embedding in the epilogue)
+// attention projection (Q/K RMSNorm and rotary embedding in the epilogue);
+// 3: the fused MLP up-projection (no Y: GELU, then the down projection's NVFP4
+// quantization and low-rank input)
 template <int MODE>
 __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
     int M, int N, int K, int rank, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
     float alpha, const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
     const float* __restrict__ xl1, const uint16_t* __restrict__ l2t,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, float* __restrict__ psums, QkvEpi qe) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, float* __restrict__ psums, QkvEpi qe,
+    MlpEpi me) {
   __shared__ __align__(16) uint16_t sW[2][BN * ROW];
   __shared__ __align__(16) uint16_t sX[2][BM * ROW];
 
@@ -375,6 +379,151 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
         }
       }
     }
+    if constexpr (MODE == 3) {
+#pragma clang fp contract(off)
+      // Fused MLP up-projection, NVFP4 (the int4 form is in gemm_int4.hip):
+      // y + bias -> h = bf16(GELU(y)), then svdq_quantize_act's NVFP4 steps on
+      // h: xh = fl32(h * fl32(1/lambda)); per 16-channel group
+      // s = e4m3_sat(fl32(amax / fl32(6 alpha))), c = e2m1(fl32(xh * fl32(1 / fl32(s alpha))))
+      // (code 0 where s is 0); and XL1 += h . L1 (fp32 atomics: every column
+      // tile adds its share).  Y is never written.  This lane holds, for
+      // tokens 32j + lr, the columns 32i + 8q + 4lh + v: a 16-channel group
+      // (i, q pair) is 8 values here and the other 8 in lane ^ 32.
+      const int nw = n0 + wn;
+      const int GS = N >> 4;  // scale bytes per row
+      const float d6 = 6.0f * me.alpha;
+      u32 hp[2][2][4][2];  // [i][j][q]: h as bf16 pairs (v = 0, 1 and 2, 3)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nw + 32 * i + 8 * q + 4 * lh;
+          float b[4] = {0.f, 0.f, 0.f, 0.f};
+          if (bias) {
+            const uint2 bb = *(const uint2*)(bias + n);
+            b[0] = bf16_bits_to_f32(bb.x & 0xFFFFu);
+            b[1] = bf16_bits_to_f32(bb.x >> 16);
+            b[2] = bf16_bits_to_f32(bb.y & 0xFFFFu);
+            b[3] = bf16_bits_to_f32(bb.y >> 16);
+          }
+          const uint2 lw = me.lam ? *(const uint2*)(me.lam + n) : uint2{0x3F803F80u, 0x3F803F80u};
+          const float rl[4] = {1.0f / bf16_bits_to_f32(lw.x & 0xFFFFu), 1.0f / bf16_bits_to_f32(lw.x >> 16),
+                               1.0f / bf16_bits_to_f32(lw.y & 0xFFFFu), 1.0f / bf16_bits_to_f32(lw.y >> 16)};
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float h[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) h[v] = gelu_f32(acc[i][j][4 * q + v] + b[v]);
+            hp[i][j][q][0] = pack_bf16x2(h[0], h[1]);
+            hp[i][j][q][1] = pack_bf16x2(h[2], h[3]);
+            acc[i][j][4 * q] = bf16_bits_to_f32(hp[i][j][q][0] & 0xFFFFu) * rl[0];  // xh
+            acc[i][j][4 * q + 1] = bf16_bits_to_f32(hp[i][j][q][0] >> 16) * rl[1];
+            acc[i][j][4 * q + 2] = bf16_bits_to_f32(hp[i][j][q][1] & 0xFFFFu) * rl[2];
+            acc[i][j][4 * q + 3] = bf16_bits_to_f32(hp[i][j][q][1] >> 16) * rl[3];
+          }
+        }
+      // codes through LDS (free after the main loop): this wave's 64 tokens x
+      // 32 bytes; scales: the wave's four group bytes of a token in one dword
+      constexpr int CROW = 48;  // bytes per LDS row (32 + pad)
+      uint8_t* ct = (uint8_t*)&sW[0][0] + wave * 64 * CROW;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32 sb4 = 0u;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {  // group g: columns 16g .. 16g+15 of the wave's 64
+          const int i = g >> 1, q0 = 2 * (g & 1);
+          float xv[8];
+          float a = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            xv[e] = acc[i][j][4 * q0 + e];
+            a = fmaxf(a, fabsf(xv[e]));
+          }
+          u32 ab = __float_as_uint(a);
+          auto pr = __builtin_amdgcn_permlane32_swap(ab, ab, false, false);  // the partner lane's 8
+          a = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+          const u32 sbits = f32_to_e4m3_sat_pos(a / d6);
+          const float sf = e4m3_to_f32(sbits);
+          float t = 0.0f;
+          if (sf != 0.0f) {
+            const float sa = sf * me.alpha;
+            t = 1.0f / sa;
+          }
+          // a zero scale writes code 0 (t = 0 would give -0 codes for negative xh)
+          const u32 w = sf == 0.0f ? 0u : e2m1_codes8(xv, t);
+          // bytes: columns 16g + 4lh + 0..3 (w's low half), 16g + 8 + 4lh + 0..3 (high half)
+          *(uint16_t*)(ct + (32 * j + lr) * CROW + 8 * g + 2 * lh) = (uint16_t)(w & 0xFFFFu);
+          *(uint16_t*)(ct + (32 * j + lr) * CROW + 8 * g + 4 + 2 * lh) = (uint16_t)(w >> 16);
+          sb4 |= sbits << (8 * g);
+        }
+        const int m = m0 + wm + 32 * j + lr;
+        if (lh == 0 && m < M) *(u32*)((uint8_t*)me.scales + (size_t)m * GS + (nw >> 4)) = sb4;
+      }
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {  // 64 rows x 2 halves, 64 lanes per pass
+        const int row = rr * 32 + (lane >> 1), half = lane & 1;
+        const uint4 v = *(const uint4*)(ct + row * CROW + 16 * half);
+        const int m = m0 + wm + row;
+        if (m < M) *(uint4*)(me.codes + (size_t)m * (N >> 1) + (nw >> 1) + 16 * half) = v;
+      }
+      // XL1 += h . L1 on v_mfma_f32_32x32x16_bf16: A = h [32 tokens x 16
+      // channels], chunk (i, qp) = columns 32i + 16qp + 0..15 with this lane's
+      // own values in its k slots 8lh + 4q' + v (column 32i + 16qp + 8q' + 4lh + v);
+      // B = L1 in the same channel order, 32 ranks per block; D lane (rank lr,
+      // lh) holds tokens 8(v/4) + 4lh + v%4 of the 32.  The two column waves of
+      // a row block (wave and wave ^ 2) cover the same tokens: the second puts
+      // its partial in LDS, the first adds it (a fixed order) and makes the
+      // one atomic add per element.
+      float* const xx = (float*)((uint8_t*)&sW[0][0] + 4 * 64 * CROW);  // [2 row blocks][2 j][16][64]
+      const int cw = wave >> 1, rw = wave & 1;
+      for (int rb = 0; rb < me.rank; rb += 32) {
+        const int r = rb + lr;
+        v8bf bl[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int qp = 0; qp < 2; ++qp) {
+            uint2 lo = {0u, 0u}, hi = {0u, 0u};
+            if (r < me.rank) {
+              lo = *(const uint2*)(me.l1t + (size_t)r * N + nw + 32 * i + 16 * qp + 4 * lh);
+              hi = *(const uint2*)(me.l1t + (size_t)r * N + nw + 32 * i + 16 * qp + 8 + 4 * lh);
+            }
+            bl[i][qp] = __builtin_bit_cast(v8bf, uint4{lo.x, lo.y, hi.x, hi.y});
+          }
+        v16f d[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) d[j][v] = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int qp = 0; qp < 2; ++qp) {
+              const v8bf al = __builtin_bit_cast(v8bf, uint4{hp[i][j][2 * qp][0], hp[i][j][2 * qp][1],
+                                                             hp[i][j][2 * qp + 1][0], hp[i][j][2 * qp + 1][1]});
+              d[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bl[i][qp], d[j], 0, 0, 0);
+            }
+        }
+        __syncthreads();  // the previous block's readers are done with xx
+        if (cw == 1) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) xx[((rw * 2 + j) * 16 + v) * 64 + lane] = d[j][v];
+        }
+        __syncthreads();
+        if (cw == 0 && r < me.rank) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int m = m0 + wm + 32 * j + 8 * (v >> 2) + 4 * lh + (v & 3);
+              if (m < M) unsafeAtomicAdd(me.xl1 + (size_t)m * me.rank + r, d[j][v] + xx[((rw * 2 + j) * 16 + v) * 64 + lane]);
+            }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -405,22 +554,31 @@ hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st) {
   const int m_tiles = (int)((a.M + BM - 1) / BM);
   const int blocks = m_tiles * (int)(a.N / BN);  // N % 128 == 0
   const QkvEpi none{};
+  const MlpEpi mnone{};
   if (a.psums) {
     hipLaunchKernelGGL(gemm_nvfp4_kernel<1>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
                        (int)a.K, 0, (const uint8_t*)a.act_codes, nullptr, 1.0f,
                        (const uint8_t*)a.w_codes, nullptr, nullptr, nullptr, nullptr, nullptr,
-                       (float*)a.psums, none);
+                       (float*)a.psums, none, mnone);
   } else if (a.qkv) {
     hipLaunchKernelGGL(gemm_nvfp4_kernel<2>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
                        (int)a.K, a.rank, (const uint8_t*)a.act_codes, (const uint8_t*)a.act_scales,
                        a.alpha_a * a.alpha_w, (const uint8_t*)a.w_codes, (const uint8_t*)a.w_scales,
                        a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr,
-                       *a.qkv);
+                       *a.qkv, mnone);
+  } else if (a.mlp) {
+    const int nx = (int)(a.M * a.mlp->rank);
+    if (nx > 0) hipLaunchKernelGGL(fill_zero_f32, dim3((nx + 255) / 256), dim3(256), 0, st, a.mlp->xl1, nx);
+    hipLaunchKernelGGL(gemm_nvfp4_kernel<3>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
+                       (int)a.K, a.rank, (const uint8_t*)a.act_codes, (const uint8_t*)a.act_scales,
+                       a.alpha_a * a.alpha_w, (const uint8_t*)a.w_codes, (const uint8_t*)a.w_scales,
+                       a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, nullptr, nullptr, none, *a.mlp);
   } else {
     hipLaunchKernelGGL(gemm_nvfp4_kernel<0>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
                        (int)a.K, a.rank, (const uint8_t*)a.act_codes, (const uint8_t*)a.act_scales,
                        a.alpha_a * a.alpha_w, (const uint8_t*)a.w_codes, (const uint8_t*)a.w_scales,
-                       a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, none);
+                       a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, none,
+                       mnone);
   }
   return hipGetLastError();
 }

@@ -46,16 +46,18 @@ struct QkvEpi {
 };
 
 // Epilogue of the fused MLP up-projection: h = bf16(GELU(y)) is quantized for
-// the down projection (int4, group 64, smoothing lam or NULL) into codes
-// [M, N/2] and fp16 scales [M, N/64], and XL1 = h . L1 [M, rank] is summed
-// into xl1 (zeroed by the launcher) from every column tile.
+// the down projection (smoothing lam or NULL; the GEMM's precision: int4 group
+// 64 with fp16 scales [M, N/64], or nvfp4 group 16 with E4M3 scales [M, N/16]
+// and the global scale alpha) into codes [M, N/2], and XL1 = h . L1 [M, rank]
+// is summed into xl1 (zeroed by the launcher) from every column tile.
 struct MlpEpi {
   const uint16_t* lam;
   const uint16_t* l1t;  // L1^T [rank, N]
   int rank;
   uint8_t* codes;
-  uint16_t* scales;
+  void* scales;
   float* xl1;
+  float alpha;  // nvfp4: the down projection's activation global scale
 };
 
 struct GemmArgs {

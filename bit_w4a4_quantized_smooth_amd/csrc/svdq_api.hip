@@ -268,14 +268,24 @@ svdq_status svdq_w4a4_gemm_gelu_quant(int precision, int group_size, int rank, i
                                      float act_global_scale, const void* w_codes, const void* w_scales,
                                      float w_global_scale, const float* xl1, const void* l2t,
                                      const void* bias, const void* smooth_out, const void* l1t_out,
-                                     int rank_out, void* codes_out, void* scales_out, float* xl1_out,
-                                     void* stream) {
+                                     int rank_out, float out_global_scale, void* codes_out, void* scales_out,
+                                     float* xl1_out, void* stream) {
   svdq_status s;
-  if (precision != SVDQ_INT4)
-    return fail(SVDQ_ERR_UNSUPPORTED, "the fused MLP up-projection supports int4 (group 64) only");
   if ((s = gemm_common(precision, group_size, rank, M, N, K, act_codes, w_codes)) != SVDQ_OK) return s;
   if (!valid_rank(rank_out)) return fail(SVDQ_ERR_UNSUPPORTED, "rank_out %d not in {0, 16, ..., 128}", rank_out);
   if (M * rank_out * 4 >= kMax32) return fail(SVDQ_ERR_UNSUPPORTED, "M*rank_out*4 must stay below 2^31 bytes");
+  const bool fp4 = precision == SVDQ_NVFP4;
+  if (fp4) {
+    if (!(act_global_scale > 0.0f && w_global_scale > 0.0f && act_global_scale < 3.0e38f &&
+          w_global_scale < 3.0e38f && out_global_scale > 0.0f && out_global_scale < 3.0e38f))
+      return fail(SVDQ_ERR_INVALID_ARG, "global scales must be finite and > 0 for nvfp4");
+    const float prod = act_global_scale * w_global_scale, d6 = 6.0f * out_global_scale;
+    if (!(prod >= FLT_MIN && prod <= FLT_MAX))
+      return fail(SVDQ_ERR_INVALID_ARG, "fl32(act_global_scale * w_global_scale) = %g is not a finite normal float",
+                  (double)prod);
+    if (!(d6 >= FLT_MIN && d6 <= FLT_MAX))
+      return fail(SVDQ_ERR_INVALID_ARG, "fl32(6 * out_global_scale) = %g is not a finite normal float", (double)d6);
+  }
   if (M == 0) return ok();
   if (!act_scales || !w_scales || !codes_out || !scales_out)
     return fail(SVDQ_ERR_INVALID_ARG, "act_scales, w_scales, codes_out and scales_out are required");
@@ -287,9 +297,12 @@ svdq_status svdq_w4a4_gemm_gelu_quant(int precision, int group_size, int rank, i
       !aligned16(xl1) || !aligned16(l2t) || !aligned16(bias) || !aligned16(smooth_out) ||
       !aligned16(l1t_out) || !aligned16(codes_out) || !aligned16(scales_out) || !aligned16(xl1_out))
     return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
-  const size_t nc = (size_t)M * N / 2, ns = (size_t)M * (N / 64) * 2, nx = (size_t)M * rank_out * 4;
+  const size_t nc = (size_t)M * N / 2, nx = (size_t)M * rank_out * 4;
+  const size_t ns = fp4 ? (size_t)M * (N / 16) : (size_t)M * (N / 64) * 2;
+  const size_t ns_a = fp4 ? (size_t)M * (K / 16) : (size_t)M * (K / 64) * 2;
+  const size_t ns_w = fp4 ? (size_t)N * (K / 16) : (size_t)N * (K / 64) * 2;
   const void* ins[] = {act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, smooth_out, l1t_out};
-  const size_t nin[] = {(size_t)M * K / 2, (size_t)M * (K / 64) * 2, (size_t)N * K / 2, (size_t)N * (K / 64) * 2,
+  const size_t nin[] = {(size_t)M * K / 2, ns_a, (size_t)N * K / 2, ns_w,
                         (size_t)M * rank * 4, (size_t)N * rank * 2, (size_t)N * 2, (size_t)N * 2,
                         (size_t)rank_out * N * 2};
   for (int i = 0; i < 9; ++i)
@@ -301,13 +314,11 @@ svdq_status svdq_w4a4_gemm_gelu_quant(int precision, int group_size, int rank, i
     return fail(SVDQ_ERR_INVALID_ARG, "outputs must not overlap each other");
   if ((s = check_arch()) != SVDQ_OK) return s;
   if ((s = check_sticky()) != SVDQ_OK) return s;
-  (void)act_global_scale;
-  (void)w_global_scale;
   const svdq::MlpEpi me{(const uint16_t*)smooth_out, (const uint16_t*)l1t_out, rank_out, (uint8_t*)codes_out,
-                        (uint16_t*)scales_out, xl1_out};
-  svdq::GemmArgs a{precision, rank, M, N, K, act_codes, act_scales, 1.0f, w_codes, w_scales, 1.0f,
-                   xl1, l2t, bias, nullptr, nullptr, nullptr, &me};
-  return launched(svdq::launch_gemm_int4(a, (hipStream_t)stream));
+                        scales_out, xl1_out, fp4 ? out_global_scale : 1.0f};
+  svdq::GemmArgs a{precision, rank, M, N, K, act_codes, act_scales, fp4 ? act_global_scale : 1.0f, w_codes,
+                   w_scales, fp4 ? w_global_scale : 1.0f, xl1, l2t, bias, nullptr, nullptr, nullptr, &me};
+  return launched(fp4 ? svdq::launch_gemm_nvfp4(a, (hipStream_t)stream) : svdq::launch_gemm_int4(a, (hipStream_t)stream));
 }
 
 svdq_status svdq_w4a4_group_psums(int precision, int group_size, int64_t M, int64_t N, int64_t K,

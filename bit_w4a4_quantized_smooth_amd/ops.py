@@ -86,25 +86,30 @@ def _(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, norm_q, norm_k, 
 @torch.library.custom_op("svdq::w4a4_gemm_gelu_quant", mutates_args=())
 def w4a4_gemm_gelu_quant_op(act_codes: Tensor, act_scales: Tensor, w_codes: Tensor, w_scales: Tensor,
                             xl1: Optional[Tensor], l2t: Optional[Tensor], bias: Optional[Tensor],
-                            smooth_out: Optional[Tensor], l1t_out: Optional[Tensor]) -> Tuple[Tensor, Tensor, Tensor]:
-    """svdq_w4a4_gemm_gelu_quant (int4): the MLP up-projection, GELU and the down
-    projection's activation quantization; returns (codes u8 [M, N/2], scales fp16
-    [M, N/64], xl1 fp32 [M, r_out]), r_out = 0 giving an empty xl1."""
+                            smooth_out: Optional[Tensor], l1t_out: Optional[Tensor], precision: int,
+                            act_global_scale: float, w_global_scale: float,
+                            out_global_scale: float) -> Tuple[Tensor, Tensor, Tensor]:
+    """svdq_w4a4_gemm_gelu_quant: the MLP up-projection, GELU and the down
+    projection's activation quantization; returns (codes u8 [M, N/2], scales
+    [M, N/G], xl1 fp32 [M, r_out]), r_out = 0 giving an empty xl1."""
     if xl1 is not None and xl1.shape[1] == 0:
         xl1 = None
     codes, scales, xo = w4a4_gemm_gelu_quant(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias,
-                                             smooth_out, l1t_out)
+                                             smooth_out, l1t_out, precision=precision,
+                                             act_global_scale=act_global_scale, w_global_scale=w_global_scale,
+                                             out_global_scale=out_global_scale)
     if xo is None:
         xo = act_codes.new_empty((act_codes.shape[0], 0), dtype=torch.float32)
     return codes, scales, xo
 
 
 @w4a4_gemm_gelu_quant_op.register_fake
-def _(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, smooth_out, l1t_out):
+def _(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, smooth_out, l1t_out, precision,
+      act_global_scale, w_global_scale, out_global_scale):
     M, N = act_codes.shape[0], w_codes.shape[0]
     ro = 0 if l1t_out is None else l1t_out.shape[0]
     return (act_codes.new_empty((M, N // 2), dtype=torch.uint8),
-            act_codes.new_empty((M, N // 64), dtype=torch.float16),
+            act_codes.new_empty((M, N // GROUP[precision]), dtype=_SCALE_DTYPE[precision]),
             act_codes.new_empty((M, ro), dtype=torch.float32))
 
 
@@ -159,27 +164,31 @@ class SVDQLinear(torch.nn.Module):
 
 
 class SVDQMLP(torch.nn.Module):
-    """The DiT MLP dim -> hidden -> dim in SVDQuant W4A4 int4 form, with the
-    up-projection, GELU and the down projection's activation quantization (and
-    its low-rank input XL1) fused in one kernel: quantize_act, then
-    w4a4_gemm_gelu_quant, then w4a4_gemm.  `up` and `down` hold the two layers'
-    tensors as SVDQLinear does; the down layer's smoothing factor and L1^T are
-    consumed by the fused kernel, its codes, scales, L2^T and bias by the GEMM."""
+    """The DiT MLP dim -> hidden -> dim in SVDQuant W4A4 form (int4 or nvfp4),
+    with the up-projection, GELU and the down projection's activation
+    quantization (and its low-rank input XL1) fused in one kernel:
+    quantize_act, then w4a4_gemm_gelu_quant, then w4a4_gemm.  `up` and `down`
+    hold the two layers' tensors as SVDQLinear does; the down layer's smoothing
+    factor, L1^T and activation global scale are consumed by the fused kernel,
+    its codes, scales, L2^T and bias by the GEMM."""
 
-    def __init__(self, dim: int, hidden: int, rank: int = 32, bias: bool = True, device=None):
+    def __init__(self, dim: int, hidden: int, rank: int = 32, precision: int = SVDQ_INT4, bias: bool = True,
+                 device=None):
         super().__init__()
-        self.up = SVDQLinear(dim, hidden, rank=rank, precision=SVDQ_INT4, bias=bias, device=device)
-        self.down = SVDQLinear(hidden, dim, rank=rank, precision=SVDQ_INT4, bias=bias, device=device)
+        self.precision = precision
+        self.up = SVDQLinear(dim, hidden, rank=rank, precision=precision, bias=bias, device=device)
+        self.down = SVDQLinear(hidden, dim, rank=rank, precision=precision, bias=bias, device=device)
 
     def forward(self, x: Tensor) -> Tensor:
         lead = x.shape[:-1]
         x2 = x.reshape(-1, x.shape[-1])
-        up, down = self.up, self.down
-        codes, scales, xl1 = torch.ops.svdq.quantize_act(x2, up.smooth, up.l1t, SVDQ_INT4, 1.0)
+        up, down, p = self.up, self.down, self.precision
+        codes, scales, xl1 = torch.ops.svdq.quantize_act(x2, up.smooth, up.l1t, p, up.act_global_scale)
         hc, hs, hx = torch.ops.svdq.w4a4_gemm_gelu_quant(codes, scales, up.w_codes, up.w_scales, xl1, up.l2t,
-                                                         up.bias, down.smooth, down.l1t)
-        y = torch.ops.svdq.w4a4_gemm(hc, hs, down.w_codes, down.w_scales, hx, down.l2t, down.bias, SVDQ_INT4,
-                                     1.0, 1.0)
+                                                         up.bias, down.smooth, down.l1t, p, up.act_global_scale,
+                                                         up.w_global_scale, down.act_global_scale)
+        y = torch.ops.svdq.w4a4_gemm(hc, hs, down.w_codes, down.w_scales, hx, down.l2t, down.bias, p,
+                                     down.act_global_scale, down.w_global_scale)
         return y.reshape(*lead, down.out_features)
 
 

@@ -154,18 +154,31 @@ def qkv_layer(seed: int, M: int, heads: int, head_dim: int, K: int, rank: int, p
 
 def mlp_layer(seed: int, M: int, hidden: int, dim: int, rank: int, prec: int = INT4) -> dict:
     """The two linears of a DiT MLP (dim -> hidden -> dim) for the fused up-projection:
-    `up` = svdq_layer(seed, M, hidden, dim, rank) (its X, outliers and weights); the down
-    projection's smoothing factor lam_down bf16 ~ U(0.5, 2) [hidden] (a stand-in for a
+    `up` = svdq_layer(seed, M, hidden, dim, rank, prec) (its X, outliers and weights); the
+    down projection's smoothing factor lam_down bf16 ~ U(0.5, 2) [hidden] (a stand-in for a
     calibrated one: calibration would need the hidden activations, which only the method
     computes), its L1^T bf16 ~ N(0, 0.02^2) [rank, hidden] and its weights as in
-    svdq_layer (int4 codes uniform in [-8, 7], fp16 scales ~ U(0.005, 0.02), L2^T, bias)."""
+    svdq_layer (int4: codes uniform in [-8, 7], fp16 scales ~ U(0.005, 0.02); nvfp4: codes
+    uniform over the 16 E2M1 nibbles, scales e4m3(U(0.005, 0.02) / alpha_w), alpha_w = 2^-6),
+    L2^T and bias.  nvfp4: the down projection's activation global scale alpha_a = 2^-6, a
+    stand-in for a calibrated one for the same reason as lam_down (it keeps amax / (6 alpha)
+    of these hidden activations inside the E4M3 range)."""
     up = svdq_layer(seed, M, hidden, dim, rank, prec, 0.005, 30.0)
-    g = 64
+    g = 64 if prec == INT4 else 16
+    if prec == INT4:
+        w_codes = pack_nibbles(_rng(seed, 23).integers(-8, 8, size=(dim, hidden)) & 0xF)
+        w_scales = to_f16_bits(_rng(seed, 24).uniform(0.005, 0.02, size=(dim, hidden // g)))
+        alpha_a, alpha_w = 1.0, 1.0
+    else:
+        aw = 2.0 ** -6
+        w_codes = pack_nibbles(_rng(seed, 23).integers(0, 16, size=(dim, hidden)))
+        w_scales = to_e4m3_bits(_rng(seed, 24).uniform(0.005, 0.02, size=(dim, hidden // g)) / aw)
+        alpha_a, alpha_w = 2.0 ** -6, aw
     down = dict(
+        prec=prec,
         lam=to_bf16_bits(_rng(seed, 21).uniform(0.5, 2.0, hidden)),
         l1t=to_bf16_bits(_rng(seed, 22).normal(0.0, 0.02, size=(rank, hidden))) if rank else np.zeros((0, hidden), np.uint16),
-        w_codes=pack_nibbles(_rng(seed, 23).integers(-8, 8, size=(dim, hidden)) & 0xF),
-        w_scales=to_f16_bits(_rng(seed, 24).uniform(0.005, 0.02, size=(dim, hidden // g))),
+        w_codes=w_codes, w_scales=w_scales, alpha_a=alpha_a, alpha_w=alpha_w,
         l2t=to_bf16_bits(_rng(seed, 25).normal(0.0, 0.02, size=(dim, rank))) if rank else np.zeros((dim, 0), np.uint16),
         bias=to_bf16_bits(_rng(seed, 26).normal(0.0, 0.01, size=dim)),
         rank=rank, N=dim, K=hidden)

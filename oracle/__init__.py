@@ -244,19 +244,20 @@ def smooth(x, lam=None):
 
 
 def mlp_up_gelu_quant(a_codes, a_scales, w_codes, w_scales, xl1, l2t, bias, lam_down, l1t_down,
-                      rows=None, nthreads=0):
-    """The fused MLP up-projection (int4): the up linear y over whole rows (all of them, or
-    the token rows `rows`), h = bf16(GELU(y)), then the down-projection's activation
-    quantization of h (smoothing lam_down, int4 group 64) and its low-rank input
-    XL1 = h . L1_down.  Returns dict(y, h_bf16, codes, scales, xl1, xh)."""
+                      rows=None, nthreads=0, prec=INT4, alpha_a=1.0, alpha_w=1.0, alpha_out=1.0):
+    """The fused MLP up-projection: the up linear y (precision prec, global scales
+    alpha_a, alpha_w for nvfp4) over whole rows (all of them, or the token rows
+    `rows`), h = bf16(GELU(y)), then the down-projection's activation quantization of h
+    in the same precision (smoothing lam_down; nvfp4 global scale alpha_out) and its
+    low-rank input XL1 = h . L1_down.  Returns dict(y, h_bf16, codes, scales, xl1, xh)."""
     M, N = a_codes.shape[0], w_codes.shape[0]
     rid = np.arange(M, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
-    y, _ = w4a4_linear(INT4, a_codes, a_scales, w_codes, w_scales, xl1, l2t, bias,
-                       rows=np.repeat(rid, N), cols=np.tile(np.arange(N, dtype=np.int64), rid.size),
+    y, _ = w4a4_linear(prec, a_codes, a_scales, w_codes, w_scales, xl1, l2t, bias, alpha_a=alpha_a,
+                       alpha_w=alpha_w, rows=np.repeat(rid, N), cols=np.tile(np.arange(N, dtype=np.int64), rid.size),
                        nthreads=nthreads)
     y = y.reshape(rid.size, N)
     _, hb = gelu(y)
-    codes, scales = quantize_act(INT4, hb, lam_down, nthreads=nthreads)
+    codes, scales = quantize_act(prec, hb, lam_down, alpha=alpha_out, nthreads=nthreads)
     xl1_down = lowrank_down(hb, l1t_down, nthreads=nthreads)
     return dict(y=y, h_bf16=hb, codes=codes, scales=scales, xl1=xl1_down, xh=smooth(hb, lam_down))
 

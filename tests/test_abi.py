@@ -170,16 +170,22 @@ def test_qkv_entry_point_validation(L):
 
 
 def mlp(L, prec=0, G=64, r=16, M=256, N=512, K=512, ac=A, as_=2 * A, wc=3 * A, ws=4 * A, xl1=5 * A, l2t=6 * A,
-        bias=7 * A, lam=9 * A, l1t=10 * A, ro=32, co=11 * A, so=12 * A, xo=13 * A):
-    return L.svdq_w4a4_gemm_gelu_quant(prec, G, r, M, N, K, ac, as_, 1.0, wc, ws, 1.0, xl1, l2t, bias, lam, l1t,
-                                       ro, co, so, xo, None)
+        bias=7 * A, lam=9 * A, l1t=10 * A, ro=32, co=11 * A, so=12 * A, xo=13 * A, aa=1.0, aw=1.0, ao=1.0):
+    return L.svdq_w4a4_gemm_gelu_quant(prec, G, r, M, N, K, ac, as_, aa, wc, ws, aw, xl1, l2t, bias, lam, l1t,
+                                       ro, ao, co, so, xo, None)
 
 
 def test_mlp_entry_point_validation(L):
     assert mlp(L) == UNSUPPORTED                       # valid: reaches the arch check
     assert mlp(L, lam=None) == UNSUPPORTED             # smoothing is optional
     assert mlp(L, ro=0, l1t=None, xo=None) == UNSUPPORTED
-    assert mlp(L, prec=1, G=16) == UNSUPPORTED         # int4 only
+    assert mlp(L, prec=1, G=16) == UNSUPPORTED         # nvfp4: valid, reaches the arch check
+    assert mlp(L, prec=1, G=64) == UNSUPPORTED         # nvfp4 takes group 16
+    assert mlp(L, prec=1, G=16, ao=0.0) == INVALID     # nvfp4: out_global_scale must be > 0
+    assert mlp(L, prec=1, G=16, ao=float("inf")) == INVALID
+    assert mlp(L, prec=1, G=16, ao=1e-39) == INVALID   # 6 * it would not be a normal float
+    assert mlp(L, prec=1, G=16, aa=1e20, aw=1e20) == INVALID  # product of the up projection's scales overflows
+    assert mlp(L, ao=0.0) == UNSUPPORTED               # int4 ignores the global scales
     assert mlp(L, ro=24) == UNSUPPORTED
     assert mlp(L, N=500) == UNSUPPORTED
     assert mlp(L, ro=32, l1t=None) == INVALID

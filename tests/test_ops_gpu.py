@@ -136,7 +136,7 @@ def test_mlp_op_and_module():
     codes, scales, xl1 = torch.ops.svdq.quantize_act(x, m.up.smooth, m.up.l1t, sq.SVDQ_INT4, 1.0)
     torch.library.opcheck(torch.ops.svdq.w4a4_gemm_gelu_quant.default,
                           (codes, scales, m.up.w_codes, m.up.w_scales, xl1, m.up.l2t, m.up.bias, m.down.smooth,
-                           m.down.l1t))
+                           m.down.l1t, sq.SVDQ_INT4, 1.0, 1.0, 1.0))
     y_eager = m(x.reshape(2, 48, 256))
     torch._dynamo.reset()
     compiled = torch.compile(m, fullgraph=True, backend="aot_eager")
@@ -145,7 +145,8 @@ def test_mlp_op_and_module():
         torch.cuda.synchronize()
         assert torch.equal(y_comp.view(torch.int16), y_eager.view(torch.int16))
     hc, hs, hx = torch.ops.svdq.w4a4_gemm_gelu_quant(codes, scales, m.up.w_codes, m.up.w_scales, xl1, m.up.l2t,
-                                                     m.up.bias, m.down.smooth, m.down.l1t)
+                                                     m.up.bias, m.down.smooth, m.down.l1t, sq.SVDQ_INT4, 1.0, 1.0,
+                                                     1.0)
     torch.cuda.synchronize()
     ref, _ = oracle.w4a4_linear(0, hc.cpu().numpy(), hs.cpu().view(torch.int16).numpy().view(np.uint16),
                                 dn["w_codes"], dn["w_scales"], hx.cpu().numpy(), dn["l2t"], dn["bias"])

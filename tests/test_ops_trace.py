@@ -92,14 +92,16 @@ def test_fake_gelu_quant(ro):
         hc, hs, hx = torch.ops.svdq.w4a4_gemm_gelu_quant(
             codes, scales, torch.empty(N, K // 2, dtype=torch.uint8), torch.empty(N, K // 64, dtype=torch.float16),
             torch.empty(M, 16), torch.empty(N, 16, dtype=torch.bfloat16), None,
-            torch.empty(N, dtype=torch.bfloat16), torch.empty(ro, N, dtype=torch.bfloat16) if ro else None)
+            torch.empty(N, dtype=torch.bfloat16), torch.empty(ro, N, dtype=torch.bfloat16) if ro else None,
+            sq.SVDQ_INT4, 1.0, 1.0, 1.0)
         assert (hc.shape, hc.dtype) == ((M, N // 2), torch.uint8)
         assert (hs.shape, hs.dtype) == ((M, N // 64), torch.float16)
         assert (hx.shape, hx.dtype) == ((M, ro), torch.float32)
 
 
-def test_export_mlp_full_graph():
-    m = ops.SVDQMLP(256, 1024, rank=16)
+@pytest.mark.parametrize("prec", [sq.SVDQ_INT4, sq.SVDQ_NVFP4])
+def test_export_mlp_full_graph(prec):
+    m = ops.SVDQMLP(256, 1024, rank=16, precision=prec)
     x = torch.zeros(2, 48, 256, dtype=torch.bfloat16)
     ep = torch.export.export(m, (x,), strict=True)
     targets = [n.target for n in ep.graph.nodes if n.op == "call_function"]
