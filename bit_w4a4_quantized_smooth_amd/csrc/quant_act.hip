@@ -24,6 +24,8 @@
 //          c = e2m1_sat(fl32(xh * fl32(1 / fl32(s*alpha))))
 #pragma clang fp contract(off)
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -236,17 +238,24 @@ __global__ __launch_bounds__(QuantCfg<RB>::NT) void quant_act_kernel(
 // partial products in another fixed order.
 //
 // Workgroup = 32 rows of X (two 16-row blocks) x 8 waves: wave w takes row
-// block w/4 and the steps w%4, w%4 + 4, ... of each chunk, so the two waves
-// of a step lane work on the same steps and share one L1^T slice.  A ring of
-// three LDS slots per wave (X) and per step lane (L1^T) keeps two steps in
-// flight; one barrier per step publishes a slot and frees the oldest.  In LDS
-// the 16-byte pieces of a 128-byte row segment are stored XOR-swizzled by the
-// row (piece p of row i at slot p ^ (i & 7)), so the fragment reads of 16
-// rows spread over the banks.
+// block w/4 and the steps w%4, w%4 + 4, ... of the whole K, so the two waves
+// of a step lane work on the same steps and share one L1^T slice.  Round j
+// computes steps 4j .. 4j+3 (one per step lane).  The workgroup is bound by
+// how many bytes it keeps in flight (a copy takes a few us under a full-chip
+// load), so the ring has four LDS slots per wave (X) and per step lane
+// (L1^T), three steps in flight, and runs unbroken over all of K: codes and
+// scales leave from registers as each step is computed (no staging tile),
+// and the reciprocals of lambda live in a double-buffered table of 2048
+// channels whose next chunk is loaded during the current one.  One barrier
+// per round publishes a slot and frees the oldest.  In LDS the 16-byte
+// pieces of a 128-byte row segment are stored XOR-swizzled by the row (piece
+// p of row i at slot p ^ (i & 7)), so the fragment reads of 16 rows spread
+// over the banks.
 namespace dma {
-constexpr int KC = 2048;  // channels per chunk: 32 steps, 8 per step lane
+constexpr int KC = 2048;  // channels per reciprocal-table chunk: 32 steps = 8 rounds
 constexpr int NT = 512;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
 
 // s_waitcnt with vmcnt = n (0..63), lgkmcnt = 0, expcnt untouched
 #define SVDQ_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0070)
@@ -259,141 +268,102 @@ __device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t res, uint8_t* dst,
 }
 }  // namespace dma
 
-template <int PREC, int RB>
+template <int PREC, int RB, bool CH>
 __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
     int M, int K, const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
     const uint16_t* __restrict__ l1t, float alpha, uint8_t* __restrict__ codes,
     void* __restrict__ scales, float* __restrict__ xl1) {
   using namespace dma;
-  static_assert(RB <= 2, "LDS holds L1^T slices of at most 32 ranks");
-  constexpr int RBX = RB > 0 ? RB : 1;
-  constexpr int LSL = RBX * 2048;   // bytes of one step's L1^T slice (16*RB rows x 128 B)
-  constexpr int NDMA = 2 + RB;      // copies per wave per step: 2 for X, RB for L1^T (8 rows each)
-  constexpr int kOut = 0x7FFFFFF0;  // offset past num_records: zeros, no memory access
-  constexpr int CROW = KC / 2 + 16; // bytes per codes row in LDS
-  __shared__ __align__(16) float rl[KC];                    // lambda reciprocals of the chunk
-  __shared__ __align__(16) uint8_t ctile[32][CROW];         // codes of the chunk (XL1 partials at the end)
-  __shared__ __align__(16) uint8_t stile[32][KC / 16];      // scales of the chunk
-  __shared__ __align__(16) uint8_t xs0[8][2048], xs1[8][2048], xs2[8][2048];  // X slices per wave
-  __shared__ __align__(16) uint8_t ls0[4][LSL], ls1[4][LSL], ls2[4][LSL];     // L1^T slices per step lane
+  static_assert(RB == 1 || RB == 2, "LDS holds L1^T slices of 16 or 32 ranks");
+  constexpr int LSL = RB * 2048;    // bytes of one step's L1^T slice (16*RB rows x 128 B)
+  constexpr int NDMA = 2 + RB;      // copies per wave per round: 2 for X, RB for L1^T (8 rows each)
+  constexpr int NSTO = 2;           // stores per wave per round: codes, scales
+  // Memory instructions retire in order and a round issues, after its
+  // barrier, [the next chunk's lambda load (first round of a chunk)], the
+  // copies of round j+3, then the stores of round j.  Round j needs the
+  // copies of round j itself (issued three rounds earlier): what may still be
+  // in flight is everything issued after them.
+  constexpr int kAfter = 2 * NDMA + 3 * NSTO;
+  constexpr int kOut = 0x7FFFFFF0;  // offset past num_records: zeros / dropped, no memory access
+  __shared__ __align__(16) float rl[2][KC];                 // lambda reciprocals, two chunks
+  __shared__ __align__(16) uint8_t lst[8][1024];            // the next chunk's lambda (bf16), waves 0-3
+  __shared__ __align__(16) uint8_t xs0[8][2048], xs1[8][2048], xs2[8][2048], xs3[8][2048];  // X slices per wave
+  __shared__ __align__(16) uint8_t ls0[4][LSL], ls1[4][LSL], ls2[4][LSL], ls3[4][LSL];     // L1^T slices per step lane
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rbk = wave >> 2, sl = wave & 3;  // row block, step lane
   const int row0 = blockIdx.x * 32;
   const int r = lane & 15, c = lane >> 4;
+  const int nsteps = K >> 6;
+  const int rounds = (nsteps + 3) >> 2;
 
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t lres = __builtin_amdgcn_make_buffer_rsrc((void*)l1t, (short)0, RB * 16 * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t lamres = __builtin_amdgcn_make_buffer_rsrc((void*)lam, (short)0, lam ? K * 2 : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t cres = __builtin_amdgcn_make_buffer_rsrc((void*)codes, (short)0, M * (K >> 1), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      scales, (short)0, PREC == 0 ? M * (K >> 6) * 2 : M * (K >> 4), 0x00020000);
   // copy lanes: lane l moves piece (l%8) ^ swizzle of row l/8 of an 8-row group
   const int cr = lane >> 3;
-  u32 xdo[2], ldo[RBX];
+  u32 xdo[2], ldo[RB];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int ri = 8 * i + cr;  // row within the 16-row X slice
     xdo[i] = (u32)(row0 + 16 * rbk + ri) * (u32)K * 2u + (u32)(((lane & 7) ^ (ri & 7)) << 4);
   }
 #pragma unroll
-  for (int i = 0; i < RBX; ++i) {
+  for (int i = 0; i < RB; ++i) {
     const int ri = 8 * (RB * rbk + i) + cr;  // L1^T row: this wave copies rows 8*RB*rbk .. +8*RB
     ldo[i] = (u32)ri * (u32)K * 2u + (u32)(((lane & 7) ^ (ri & 7)) << 4);
   }
+  // this lane's output row and its store offsets (rows past M: dropped)
+  const int orow = row0 + 16 * rbk + r;
+  const bool rlive = orow < M;
+  const int cbase = rlive ? orow * (K >> 1) + 8 * c : kOut;
+  const int sbase = PREC == 0 ? (rlive && c == 0 ? orow * (K >> 6) * 2 : kOut) : (rlive ? orow * (K >> 4) + c : kOut);
 
-  v4f acc[RBX];
+  v4f acc[RB];
 #pragma unroll
-  for (int i = 0; i < RBX; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < RB; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   const float d6 = 6.0f * alpha;
 
-  for (int c0 = 0; c0 < K; c0 += KC) {
-    const int kc = K - c0 < KC ? K - c0 : KC;
-    const int nsteps = kc >> 6;
-    const int nst = nsteps > sl ? (nsteps - sl + 3) >> 2 : 0;  // this step lane's steps
-    const int J = (nsteps + 3) >> 2;                           // rounds (the step lane 0 count)
-
-    // copy local step j of this wave into slot buffers (xb, lb); past the end:
-    // out-of-range offsets (zeros, no memory access), so every wave issues the
-    // same number of copies in every round and the waits count exactly
-    auto issue = [&](int j, uint8_t(*xb)[2048], uint8_t(*lb)[LSL]) __attribute__((always_inline)) {
-      const bool live = j < nst;
-      const u32 sb = 128u * (u32)((c0 >> 6) + sl + 4 * j);
+  // copy the step of round j for this wave into slot buffers (xb, lb); steps
+  // past the end use out-of-range offsets (zeros, no memory access), so every
+  // wave issues the same copies in every round and the waits count exactly
+  auto issue = [&](int j, uint8_t(*xb)[2048], uint8_t(*lb)[LSL]) __attribute__((always_inline)) {
+    const int st = 4 * j + sl;
+    const bool live = st < nsteps;
+    const u32 sb = 128u * (u32)st;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        copy16(xres, xb[wave] + 1024 * i, live ? (int)(xdo[i] + sb) : kOut);
-      if constexpr (RB > 0) {
+    for (int i = 0; i < 2; ++i) copy16(xres, xb[wave] + 1024 * i, live ? (int)(xdo[i] + sb) : kOut);
 #pragma unroll
-        for (int i = 0; i < RB; ++i)
-          copy16(lres, lb[sl] + 1024 * (RB * rbk + i), live ? (int)(ldo[i] + sb) : kOut);
-      }
-    };
-
-    // quantize local step j from slot buffers (xb, lb) and add its X.L1 share
-    auto compute = [&](int j, uint8_t(*xb)[2048], uint8_t(*lb)[LSL]) __attribute__((always_inline)) {
-      const int ls = sl + 4 * j;             // step within the chunk
-      const int k0 = (ls << 6) + (c << 4);   // this lane's first channel within the chunk
-      const uint8_t* xrow = xb[wave] + r * 128;
-      const uint4 va = *(const uint4*)(xrow + swz(r, 2 * c));
-      const uint4 vb = *(const uint4*)(xrow + swz(r, 2 * c + 1));
-      const u32 xw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-      float rk[16];
-      *(float4*)&rk[0] = *(const float4*)&rl[k0];
-      *(float4*)&rk[4] = *(const float4*)&rl[k0 + 4];
-      *(float4*)&rk[8] = *(const float4*)&rl[k0 + 8];
-      *(float4*)&rk[12] = *(const float4*)&rl[k0 + 12];
-      float xh[16];
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        xh[2 * i] = bf16_bits_to_f32(xw[i] & 0xFFFFu) * rk[2 * i];
-        xh[2 * i + 1] = bf16_bits_to_f32(xw[i] >> 16) * rk[2 * i + 1];
-        amax = fmaxf(amax, fmaxf(fabsf(xh[2 * i]), fabsf(xh[2 * i + 1])));
-      }
-      u32 pk0 = 0u, pk1 = 0u;
-      const int trow = 16 * rbk + r;  // row within the workgroup's 32
-      if constexpr (PREC == 0) {
-        amax = max_over_rows(amax);  // one 64-channel group = lanes l, l^16, l^32, l^48
-        const u32 sbits = f32_to_f16_sat_bits(div7_rn(amax));
-        const float sf = f16_bits_to_f32(sbits);
-        const float t = sf == 0.0f ? 0.0f : 1.0f / sf;
-        pk0 = int4_codes8(xh, t);
-        pk1 = int4_codes8(xh + 8, t);
-        if (c == 0) *(uint16_t*)(&stile[trow][2 * ls]) = (uint16_t)sbits;
-      } else {
-        // one 16-channel group = this lane's 16 channels
-        const u32 sbits = f32_to_e4m3_sat_pos(amax / d6);
-        const float sf = e4m3_to_f32(sbits);
-        float t = 0.0f;
-        if (sf != 0.0f) {
-          const float sa = sf * alpha;
-          t = 1.0f / sa;
-        }
-        // a zero scale writes code 0 (t = 0 would give -0 codes for negative xh)
-        pk0 = sf == 0.0f ? 0u : e2m1_codes8(xh, t);
-        pk1 = sf == 0.0f ? 0u : e2m1_codes8(xh + 8, t);
-        stile[trow][4 * ls + c] = (uint8_t)sbits;
-      }
-      *(uint2*)(&ctile[trow][k0 >> 1]) = uint2{pk0, pk1};
-      if constexpr (RB > 0) {
-        // XL1 += X[16 rows, these 64 channels] . L1[these channels, 16*RB]
-        const v8bf a0 = __builtin_bit_cast(v8bf, va);
-        const v8bf a1 = __builtin_bit_cast(v8bf, vb);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int lr = rb * 16 + r;  // L1^T row = rank
-          const uint8_t* lrow = lb[sl] + lr * 128;
-          const uint4 b0 = *(const uint4*)(lrow + swz(lr, 2 * c));
-          const uint4 b1 = *(const uint4*)(lrow + swz(lr, 2 * c + 1));
-          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, b0), acc[rb], 0, 0, 0);
-          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, b1), acc[rb], 0, 0, 0);
-        }
-      }
-    };
-
-    // the first two steps in flight while the reciprocal table is built
-    issue(0, xs0, ls0);
-    issue(1, xs1, ls1);
-    if (tid * 8 < kc) {
-      const uint4 lv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lamres, (c0 + tid * 8) * 2, 0, 0));
+    for (int i = 0; i < RB; ++i) copy16(lres, lb[sl] + 1024 * (RB * rbk + i), live ? (int)(ldo[i] + sb) : kOut);
+  };
+  // the NSTO stores of a round, issued also for steps past the end (dropped)
+  auto store = [&](int st, u32 pk0, u32 pk1, u32 sbits) __attribute__((always_inline)) {
+    const bool live = st < nsteps;
+    __builtin_amdgcn_raw_buffer_store_b64(u2v{pk0, pk1}, cres, live ? cbase + 32 * st : kOut, 0, 0);
+    if constexpr (PREC == 0)
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)sbits, sres, live ? sbase + 2 * st : kOut, 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sbits, sres, live ? sbase + 4 * st : kOut, 0, 0);
+  };
+  // lambda of a chunk: thread t < 256 loads channels 8t .. 8t+7 (16 bytes);
+  // for the first chunk straight into registers, for the next ones by a copy
+  // into lst (a register load issued rounds before its use would be sunk by
+  // the compiler to its use, stalling the ring there), one per wave
+  auto lam_load = [&](int q) __attribute__((always_inline)) -> uint4 {
+    const int ch = q * KC + 8 * tid;
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         lamres, tid < KC / 8 && ch < K ? 2 * ch : kOut, 0, 0));
+  };
+  auto lam_copy = [&](int q) __attribute__((always_inline)) {
+    const int ch = q * KC + 8 * tid;
+    copy16(lamres, lst[wave], wave < 4 && ch < K ? 2 * ch : kOut);
+  };
+  auto lam_store = [&](int buf, uint4 lv) __attribute__((always_inline)) {
+    if (tid < KC / 8) {
       const u32 w4[4] = {lv.x, lv.y, lv.z, lv.w};
       float o[8];
 #pragma unroll
@@ -401,98 +371,182 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
         o[2 * e] = lam ? 1.0f / bf16_bits_to_f32(w4[e] & 0xFFFFu) : 1.0f;
         o[2 * e + 1] = lam ? 1.0f / bf16_bits_to_f32(w4[e] >> 16) : 1.0f;
       }
-      *(float4*)&rl[tid * 8] = float4{o[0], o[1], o[2], o[3]};
-      *(float4*)&rl[tid * 8 + 4] = float4{o[4], o[5], o[6], o[7]};
+      *(float4*)&rl[buf][8 * tid] = float4{o[0], o[1], o[2], o[3]};
+      *(float4*)&rl[buf][8 * tid + 4] = float4{o[4], o[5], o[6], o[7]};
     }
+  };
 
-    // Round j: wait for this wave's copies of step j (the NDMA copies of
-    // step j+1 may stay in flight) and its LDS reads, barrier (every wave's
-    // copies of step j have landed; every wave is done with the slot of step
-    // j-1), refill that slot with step j+2, compute step j.
-    auto round = [&](int j, uint8_t(*xa)[2048], uint8_t(*la)[LSL], uint8_t(*xc)[2048], uint8_t(*lc)[LSL])
-        __attribute__((always_inline)) {
-      SVDQ_WAIT_VM_LGKM0(NDMA);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      issue(j + 2, xc, lc);
-      if (j < nst) compute(j, xa, la);  // wave-uniform
-    };
-    int j = 0;
-    for (; j + 3 <= J; j += 3) {
-      round(j, xs0, ls0, xs2, ls2);
-      round(j + 1, xs1, ls1, xs0, ls0);
-      round(j + 2, xs2, ls2, xs1, ls1);
+  // quantize the step of round j from slot buffers (xb, lb), store its codes
+  // and scale, and add its X.L1 share
+  auto compute = [&](int j, uint8_t(*xb)[2048], uint8_t(*lb)[LSL]) __attribute__((always_inline)) {
+    const int st = 4 * j + sl;  // step within K
+    const float* rlc = CH ? &rl[(st >> 5) & 1][((st & 31) << 6) + (c << 4)] : &rl[0][0] + (st << 6) + (c << 4);
+    const uint8_t* xrow = xb[wave] + r * 128;
+    const uint4 va = *(const uint4*)(xrow + swz(r, 2 * c));
+    const uint4 vb = *(const uint4*)(xrow + swz(r, 2 * c + 1));
+    const u32 xw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+    float rk[16];
+    *(float4*)&rk[0] = *(const float4*)&rlc[0];
+    *(float4*)&rk[4] = *(const float4*)&rlc[4];
+    *(float4*)&rk[8] = *(const float4*)&rlc[8];
+    *(float4*)&rk[12] = *(const float4*)&rlc[12];
+    float xh[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      xh[2 * i] = bf16_bits_to_f32(xw[i] & 0xFFFFu) * rk[2 * i];
+      xh[2 * i + 1] = bf16_bits_to_f32(xw[i] >> 16) * rk[2 * i + 1];
+      amax = fmaxf(amax, fmaxf(fabsf(xh[2 * i]), fabsf(xh[2 * i + 1])));
     }
-    if (j < J) round(j, xs0, ls0, xs2, ls2);
-    if (j + 1 < J) round(j + 1, xs1, ls1, xs0, ls0);
-    __syncthreads();  // every copy and every code and scale of the chunk in LDS
+    u32 pk0, pk1, sbits;
+    if constexpr (PREC == 0) {
+      amax = max_over_rows(amax);  // one 64-channel group = lanes l, l^16, l^32, l^48
+      sbits = f32_to_f16_sat_bits(div7_rn(amax));
+      const float sf = f16_bits_to_f32(sbits);
+      const float t = sf == 0.0f ? 0.0f : 1.0f / sf;
+      pk0 = int4_codes8(xh, t);
+      pk1 = int4_codes8(xh + 8, t);
+    } else {
+      // one 16-channel group = this lane's 16 channels
+      sbits = f32_to_e4m3_sat_pos(amax / d6);
+      const float sf = e4m3_to_f32(sbits);
+      float t = 0.0f;
+      if (sf != 0.0f) {
+        const float sa = sf * alpha;
+        t = 1.0f / sa;
+      }
+      // a zero scale writes code 0 (t = 0 would give -0 codes for negative xh)
+      pk0 = sf == 0.0f ? 0u : e2m1_codes8(xh, t);
+      pk1 = sf == 0.0f ? 0u : e2m1_codes8(xh + 8, t);
+    }
+    store(st, pk0, pk1, sbits);
+    // XL1 += X[16 rows, these 64 channels] . L1[these channels, 16*RB]
+    const v8bf a0 = __builtin_bit_cast(v8bf, va);
+    const v8bf a1 = __builtin_bit_cast(v8bf, vb);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int lr = rb * 16 + r;  // L1^T row = rank
+      const uint8_t* lrow = lb[sl] + lr * 128;
+      const uint4 b0 = *(const uint4*)(lrow + swz(lr, 2 * c));
+      const uint4 b1 = *(const uint4*)(lrow + swz(lr, 2 * c + 1));
+      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, b0), acc[rb], 0, 0, 0);
+      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, b1), acc[rb], 0, 0, 0);
+    }
+  };
 
-    // the chunk's codes and scales out: LDS reads first, then the stores
-    {
-      const int cpr = kc >> 5;  // 16-byte code pieces per row
-      constexpr int CIT = 32 * (KC / 32) / NT;
-      uint4 cv[CIT];
-      int cdst[CIT];
+  // Prologue: the reciprocals of lambda (K <= 2 KC: the whole table; else the
+  // first chunk), then rounds 0 .. 2 in flight, each followed by NSTO dropped
+  // stores so that every later round finds the same instruction pattern
+  // behind its copies (the waits below count it).
+  if constexpr (CH) {
+    lam_store(0, lam_load(0));
+  } else {
+    const int ch = 8 * tid;
+    const uint4 lv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lamres, ch < K ? 2 * ch : kOut, 0, 0));
+    const u32 w4[4] = {lv.x, lv.y, lv.z, lv.w};
+    float o[8];
 #pragma unroll
-      for (int i = 0; i < CIT; ++i) {
-        const int idx = tid + NT * i;
-        const int rr = idx / cpr, off = (idx - rr * cpr) << 4;
-        const bool ok = idx < 32 * cpr && row0 + rr < M;
-        cv[i] = ok ? *(const uint4*)(&ctile[rr][off]) : uint4{0u, 0u, 0u, 0u};
-        cdst[i] = ok ? (row0 + rr) * (K >> 1) + (c0 >> 1) + off : -1;
-      }
-      const int sb = PREC == 0 ? 2 * (kc >> 6) : (kc >> 4);   // scale bytes of the chunk per row (even)
-      const int sbr = PREC == 0 ? 2 * (K >> 6) : (K >> 4);    // scale bytes per row
-      const int s0b = PREC == 0 ? 2 * (c0 >> 6) : (c0 >> 4);  // first scale byte of the chunk
-      constexpr int SIT = 32 * ((PREC == 0 ? 2 * (KC >> 6) : (KC >> 4)) / 2) / NT;
-      uint16_t sv[SIT];
-      int sdst[SIT];
-#pragma unroll
-      for (int i = 0; i < SIT; ++i) {
-        const int idx = tid + NT * i;
-        const int rr = idx / (sb >> 1), off = (idx - rr * (sb >> 1)) << 1;
-        const bool ok = idx < 32 * (sb >> 1) && row0 + rr < M;
-        sv[i] = ok ? *(const uint16_t*)(&stile[rr][off]) : (uint16_t)0;
-        sdst[i] = ok ? (row0 + rr) * sbr + s0b + off : -1;
-      }
-#pragma unroll
-      for (int i = 0; i < CIT; ++i)
-        if (cdst[i] >= 0) *(uint4*)(codes + cdst[i]) = cv[i];
-#pragma unroll
-      for (int i = 0; i < SIT; ++i)
-        if (sdst[i] >= 0) *(uint16_t*)((uint8_t*)scales + sdst[i]) = sv[i];
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = lam ? 1.0f / bf16_bits_to_f32(w4[e] & 0xFFFFu) : 1.0f;
+      o[2 * e + 1] = lam ? 1.0f / bf16_bits_to_f32(w4[e] >> 16) : 1.0f;
     }
-    __syncthreads();  // rl, ctile, stile and the slots are rewritten by the next chunk
+    *(float4*)(&rl[0][0] + ch) = float4{o[0], o[1], o[2], o[3]};
+    *(float4*)(&rl[0][0] + ch + 4) = float4{o[4], o[5], o[6], o[7]};
+  }
+  issue(0, xs0, ls0);
+  store(nsteps, 0u, 0u, 0u);
+  issue(1, xs1, ls1);
+  store(nsteps, 0u, 0u, 0u);
+  issue(2, xs2, ls2);
+  store(nsteps, 0u, 0u, 0u);
+
+  // Round j = 8t + P: wait for this wave's copies of round j and its LDS
+  // traffic, barrier (every wave's copies of round j have landed; every wave
+  // is done with the slot of round j-1 and, at P = 0, with the reciprocal
+  // buffer of the chunk before), then, with a chunked table, at P = 0 copy
+  // the next chunk's lambda (landed by the wait of round j+3, where the table
+  // is filled; lst is rewritten only by the next chunk's P = 0, after that
+  // round's barrier), refill the freed slot with round j+3, compute round j.
+  // Steps past the end (a partial last round, the rounds that pad the loop to
+  // whole unrolled blocks) are computed on the zeros their copies brought and
+  // their stores dropped: no branch, so the compiler keeps track of which copy
+  // fills which slot and adds no waits of its own.
+  auto round = [&](int j, auto pc, uint8_t(*xa)[2048], uint8_t(*la)[LSL], uint8_t(*xc)[2048], uint8_t(*lc)[LSL])
+      __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+    SVDQ_WAIT_VM_LGKM0(kAfter + (CH && (P == 1 || P == 2) ? 1 : 0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if constexpr (CH && P == 0) lam_copy((j >> 3) + 1);
+    issue(j + 3, xc, lc);
+    if constexpr (CH && P == 3) {
+      if (tid < KC / 8) lam_store(((j >> 3) + 1) & 1, *(const uint4*)&lst[tid >> 6][16 * (tid & 63)]);
+    }
+    compute(j, xa, la);
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  using P4 = std::integral_constant<int, 4>;
+  using P5 = std::integral_constant<int, 5>;
+  using P6 = std::integral_constant<int, 6>;
+  using P7 = std::integral_constant<int, 7>;
+  if constexpr (CH) {
+    for (int j = 0; j < rounds; j += 8) {
+      round(j, P0{}, xs0, ls0, xs3, ls3);
+      round(j + 1, P1{}, xs1, ls1, xs0, ls0);
+      round(j + 2, P2{}, xs2, ls2, xs1, ls1);
+      round(j + 3, P3{}, xs3, ls3, xs2, ls2);
+      round(j + 4, P4{}, xs0, ls0, xs3, ls3);
+      round(j + 5, P5{}, xs1, ls1, xs0, ls0);
+      round(j + 6, P6{}, xs2, ls2, xs1, ls1);
+      round(j + 7, P7{}, xs3, ls3, xs2, ls2);
+    }
+  } else {
+    for (int j = 0; j < rounds; j += 4) {
+      round(j, P4{}, xs0, ls0, xs3, ls3);
+      round(j + 1, P5{}, xs1, ls1, xs0, ls0);
+      round(j + 2, P6{}, xs2, ls2, xs1, ls1);
+      round(j + 3, P7{}, xs3, ls3, xs2, ls2);
+    }
   }
 
-  if constexpr (RB > 0) {
-    constexpr int R = RB * 16;
-    // per-wave partial XL1 tiles [16 rows][R] in the codes tile (free now),
-    // summed over the four step lanes of each row block in a fixed order;
-    // lane holds D[row 4*(lane/16) + v][col lane%16] of each 16x16 block
-    float* red = (float*)&ctile[0][0];
-    static_assert(8 * 16 * R * 4 <= 32 * CROW, "partial XL1 tiles fit in the codes tile");
+  // per-wave partial XL1 tiles [16 rows][R] in slot xs0 (every copy has
+  // landed and every wave is past its last read), summed over the four step
+  // lanes of each row block in a fixed order; lane holds
+  // D[row 4*(lane/16) + v][col lane%16] of each 16x16 block
+  constexpr int R = RB * 16;
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+  __syncthreads();
+  float* red = (float*)&xs0[0][0];
+  static_assert(8 * 16 * R * 4 <= 8 * 2048, "partial XL1 tiles fit in one X slot");
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * c + v) * R + rb * 16 + r] = acc[rb][v];
-    __syncthreads();
-    for (int idx = tid; idx < 32 * R; idx += NT) {
-      const int rr = idx / R, col = idx - rr * R;  // row within the 32
-      const int b = rr >> 4, ri = rr & 15;
-      float sum = red[((4 * b) * 16 + ri) * R + col];
+    for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * c + v) * R + rb * 16 + r] = acc[rb][v];
+  __syncthreads();
+  for (int idx = tid; idx < 32 * R; idx += NT) {
+    const int rr = idx / R, col = idx - rr * R;  // row within the 32
+    const int b = rr >> 4, ri = rr & 15;
+    float sum = red[((4 * b) * 16 + ri) * R + col];
 #pragma unroll
-      for (int s2 = 1; s2 < 4; ++s2) sum += red[((4 * b + s2) * 16 + ri) * R + col];  // fixed order
-      if (row0 + rr < M) xl1[(size_t)(row0 + rr) * R + col] = sum;
-    }
+    for (int s2 = 1; s2 < 4; ++s2) sum += red[((4 * b + s2) * 16 + ri) * R + col];  // fixed order
+    if (row0 + rr < M) xl1[(size_t)(row0 + rr) * R + col] = sum;
   }
 }
 
 template <int PREC, int RB>
 static hipError_t launch_quant_dma(const QuantArgs& a, hipStream_t st) {
   const int blocks = (int)((a.M + 31) / 32);
-  hipLaunchKernelGGL((quant_act_dma_kernel<PREC, RB>), dim3(blocks), dim3(dma::NT), 0, st, (int)a.M, (int)a.K,
+  if (a.K <= 2 * dma::KC) {  // the whole reciprocal table in LDS
+    hipLaunchKernelGGL((quant_act_dma_kernel<PREC, RB, false>), dim3(blocks), dim3(dma::NT), 0, st, (int)a.M,
+                       (int)a.K, (const uint16_t*)a.x, (const uint16_t*)a.smooth, (const uint16_t*)a.l1t, a.alpha,
+                       (uint8_t*)a.codes, a.scales, a.xl1);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((quant_act_dma_kernel<PREC, RB, true>), dim3(blocks), dim3(dma::NT), 0, st, (int)a.M, (int)a.K,
                      (const uint16_t*)a.x, (const uint16_t*)a.smooth, (const uint16_t*)a.l1t,
                      a.alpha, (uint8_t*)a.codes, a.scales, a.xl1);
   return hipGetLastError();

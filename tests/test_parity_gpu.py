@@ -212,15 +212,20 @@ def test_gemm_split_boundary(M):
 
 # --------------------------------------------------------------------------- quantizer, many rows
 # int4 with ranks 16 / 32 on more 16-row blocks than the device has CUs goes to
-# the LDS-staged quantizer (32 rows per workgroup, 2048-channel chunks): the
-# DiT attention input, ragged rows and channels (a partial last workgroup, a
-# partial last chunk, a one-step chunk) and a single 64-channel step.
+# the LDS-staged quantizer (32 rows per workgroup, one ring over all of K with
+# lambda reciprocals in 2048-channel chunks): the DiT attention input, ragged
+# rows and channels (a partial last workgroup, a partial last chunk, a
+# one-step chunk), a single 64-channel step, and no smoothing factor.
 MANY_ROWS = {
     "int4_4608x3072_r32": lambda: synth.svdq_layer(1002, 4608, 128, 3072, 32, synth.INT4, 0.005, 30.0),
     "int4_ragged_4100x4160_r16": lambda: synth.svdq_layer(31, 4100, 128, 4160, 16, synth.INT4, 0.02, 30.0),
     "int4_ragged_4130x2112_r32": lambda: synth.svdq_layer(32, 4130, 128, 2112, 32, synth.INT4, 0.02, 30.0),
     "int4_4200x64_r32": lambda: synth.svdq_layer(33, 4200, 128, 64, 32, synth.INT4, 0.02, 30.0),
     "nvfp4_4608x3072_r32": lambda: synth.svdq_layer(1004, 4608, 128, 3072, 32, synth.NVFP4, 0.005, 30.0),
+    # no smoothing factor (lambda = 1), and nvfp4 on ragged rows with a one-step last chunk
+    "int4_nosmooth_4112x2176_r16": lambda: synth.svdq_layer(34, 4112, 128, 2176, 16, synth.INT4, 0.02, 30.0,
+                                                             smooth=False),
+    "nvfp4_ragged_4100x4160_r16": lambda: synth.svdq_layer(35, 4100, 128, 4160, 16, synth.NVFP4, 0.02, 30.0),
 }
 
 
