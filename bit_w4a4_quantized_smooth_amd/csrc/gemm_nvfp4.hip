@@ -86,8 +86,12 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
     const float* __restrict__ xl1, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, float* __restrict__ psums, QkvEpi qe,
     MlpEpi me) {
-  __shared__ __align__(16) uint16_t sW[2][BN * ROW];
-  __shared__ __align__(16) uint16_t sX[2][BM * ROW];
+  // One array: the activation tiles start 32 bytes past a multiple of 128
+  // bytes from the weight tiles, so that a staging store whose lanes write
+  // both (the same rows and halves of each) spreads over all the banks.
+  __shared__ __align__(16) uint16_t sWX[2 * BN * ROW + 16 + 2 * BM * ROW];
+  uint16_t(*const sW)[BN * ROW] = (uint16_t(*)[BN * ROW])sWX;
+  uint16_t(*const sX)[BM * ROW] = (uint16_t(*)[BM * ROW])(sWX + 2 * BN * ROW + 16);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // XCD-contiguous ranges of a banded tile order (see gemm_int4.hip)
