@@ -249,8 +249,8 @@ __global__ __launch_bounds__(QuantCfg<RB>::NT) void quant_act_kernel(
 // channels whose next chunk is loaded during the current one.  One barrier
 // per round publishes a slot and frees the oldest.  In LDS the 16-byte
 // pieces of a 128-byte row segment are stored XOR-swizzled by the row (piece
-// p of row i at slot p ^ (i & 7)), so the fragment reads of 16 rows spread
-// over the banks.
+// p of row i at slot p ^ ((i ^ (i >> 3)) & 7)), so the fragment reads of 16
+// rows spread over the banks.
 namespace dma {
 constexpr int KC = 2048;  // channels per reciprocal-table chunk: 32 steps = 8 rounds
 constexpr int NT = 512;
@@ -260,7 +260,11 @@ typedef unsigned int u2v __attribute__((ext_vector_type(2)));
 // s_waitcnt with vmcnt = n (0..63), lgkmcnt = 0, expcnt untouched
 #define SVDQ_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0070)
 
-__device__ __forceinline__ int swz(int row, int piece) { return (piece ^ (row & 7)) << 4; }
+// the 16-byte piece p of a 128-byte row segment sits at slot p ^ rsw(row):
+// rows r and r + 8 get different slots too, so a fragment read of 16 rows
+// (two rows per 256 bytes of banks) touches every bank once
+__device__ __forceinline__ int rsw(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz(int row, int piece) { return (piece ^ rsw(row)) << 4; }
 
 // 16 bytes per lane, global (buffer offset off) -> LDS at dst + 16 * lane
 __device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t res, uint8_t* dst, int off) {
@@ -310,12 +314,12 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int ri = 8 * i + cr;  // row within the 16-row X slice
-    xdo[i] = (u32)(row0 + 16 * rbk + ri) * (u32)K * 2u + (u32)(((lane & 7) ^ (ri & 7)) << 4);
+    xdo[i] = (u32)(row0 + 16 * rbk + ri) * (u32)K * 2u + (u32)(((lane & 7) ^ rsw(ri)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
     const int ri = 8 * (RB * rbk + i) + cr;  // L1^T row: this wave copies rows 8*RB*rbk .. +8*RB
-    ldo[i] = (u32)ri * (u32)K * 2u + (u32)(((lane & 7) ^ (ri & 7)) << 4);
+    ldo[i] = (u32)ri * (u32)K * 2u + (u32)(((lane & 7) ^ rsw(ri)) << 4);
   }
   // this lane's output row and its store offsets (rows past M: dropped)
   const int orow = row0 + 16 * rbk + r;
