@@ -111,32 +111,37 @@ def test_module_against_oracle(prec):
 
 def _mlp_module(case):
     up, dn = case["up"], case["down"]
-    m = ops.SVDQMLP(up["K"], up["N"], rank=up["rank"], device="cuda")
+    prec = up["prec"]
+    m = ops.SVDQMLP(up["K"], up["N"], rank=up["rank"], precision=prec, device="cuda")
+    sdt = torch.float16 if prec == sq.SVDQ_INT4 else torch.uint8
     for lin, d in ((m.up, up), (m.down, dn)):
         if "lam" in d:
             lin.smooth.copy_(_t(d["lam"], torch.bfloat16))
         lin.w_codes.copy_(_t(d["w_codes"], torch.uint8))
-        lin.w_scales.copy_(_t(d["w_scales"], torch.float16))
+        lin.w_scales.copy_(_t(d["w_scales"], sdt))
         lin.l1t.copy_(_t(d["l1t"], torch.bfloat16))
         lin.l2t.copy_(_t(d["l2t"], torch.bfloat16))
         lin.bias.copy_(_t(d["bias"], torch.bfloat16))
+        lin.act_global_scale, lin.w_global_scale = float(d["alpha_a"]), float(d["alpha_w"])
     return m
 
 
-def test_mlp_op_and_module():
+@pytest.mark.parametrize("prec", [sq.SVDQ_INT4, sq.SVDQ_NVFP4])
+def test_mlp_op_and_module(prec):
     # 96 tokens, 256 -> 512 -> 256, rank 16: opcheck of the fused operator,
     # the compiled module bit-equal to eager, and the module's output against the
     # oracle's down projection of the fused kernel's own codes, scales and XL1
     # (the fused quantization itself is compared in tests/test_mlp_gpu.py)
-    print("[ops] SVDQMLP", flush=True)
-    case = synth.mlp_layer(61, 96, 512, 256, 16)
+    print(f"[ops] SVDQMLP precision {prec}", flush=True)
+    case = synth.mlp_layer(61, 96, 512, 256, 16, prec)
     up, dn = case["up"], case["down"]
     m = _mlp_module(case)
     x = _t(up["x"], torch.bfloat16)
-    codes, scales, xl1 = torch.ops.svdq.quantize_act(x, m.up.smooth, m.up.l1t, sq.SVDQ_INT4, 1.0)
+    ga = (m.up.act_global_scale, m.up.w_global_scale, m.down.act_global_scale)
+    codes, scales, xl1 = torch.ops.svdq.quantize_act(x, m.up.smooth, m.up.l1t, prec, ga[0])
     torch.library.opcheck(torch.ops.svdq.w4a4_gemm_gelu_quant.default,
                           (codes, scales, m.up.w_codes, m.up.w_scales, xl1, m.up.l2t, m.up.bias, m.down.smooth,
-                           m.down.l1t, sq.SVDQ_INT4, 1.0, 1.0, 1.0))
+                           m.down.l1t, prec, *ga))
     y_eager = m(x.reshape(2, 48, 256))
     torch._dynamo.reset()
     compiled = torch.compile(m, fullgraph=True, backend="aot_eager")
@@ -145,11 +150,11 @@ def test_mlp_op_and_module():
         torch.cuda.synchronize()
         assert torch.equal(y_comp.view(torch.int16), y_eager.view(torch.int16))
     hc, hs, hx = torch.ops.svdq.w4a4_gemm_gelu_quant(codes, scales, m.up.w_codes, m.up.w_scales, xl1, m.up.l2t,
-                                                     m.up.bias, m.down.smooth, m.down.l1t, sq.SVDQ_INT4, 1.0, 1.0,
-                                                     1.0)
+                                                     m.up.bias, m.down.smooth, m.down.l1t, prec, *ga)
     torch.cuda.synchronize()
-    ref, _ = oracle.w4a4_linear(0, hc.cpu().numpy(), hs.cpu().view(torch.int16).numpy().view(np.uint16),
-                                dn["w_codes"], dn["w_scales"], hx.cpu().numpy(), dn["l2t"], dn["bias"])
+    hs_np = hs.cpu().view(torch.int16).numpy().view(np.uint16) if prec == sq.SVDQ_INT4 else hs.cpu().numpy()
+    ref, _ = oracle.w4a4_linear(prec, hc.cpu().numpy(), hs_np, dn["w_codes"], dn["w_scales"], hx.cpu().numpy(),
+                                dn["l2t"], dn["bias"], alpha_a=dn["alpha_a"], alpha_w=dn["alpha_w"])
     got = synth.bf16_bits_to_f64(y_eager.reshape(96, 256).cpu().view(torch.int16).numpy().view(np.uint16))
     e = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
     print(f"[ops] SVDQMLP vs oracle on the fused outputs: max-abs-rel {e:.2e}", flush=True)
