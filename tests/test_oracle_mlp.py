@@ -74,3 +74,60 @@ def test_mlp_up_composition():
                                     lam_down, l1t_down, rows=[5, 2])
     np.testing.assert_array_equal(some["codes"], out["codes"][[5, 2]])
     np.testing.assert_array_equal(some["xl1"], out["xl1"][[5, 2]])
+
+
+def test_mlp_up_composition_nvfp4():
+    # the nvfp4 form: the up projection with its global scales, then the down
+    # projection's nvfp4 quantization of h with its own global scale
+    d = synth.svdq_layer(12, 8, 256, 128, 16, synth.NVFP4, 0.01, 20.0)
+    codes, scales = oracle.quantize_act(1, d["x"], d["lam"], alpha=d["alpha_a"])
+    xl1 = oracle.lowrank_down(d["x"], d["l1t"])
+    rng = np.random.default_rng(3)
+    lam_down = synth.to_bf16_bits(rng.uniform(0.5, 2.0, 256))
+    l1t_down = synth.to_bf16_bits(rng.normal(0, 0.02, (16, 256)))
+    ao = 2.0 ** -6
+    kw = dict(prec=1, alpha_a=d["alpha_a"], alpha_w=d["alpha_w"], alpha_out=ao)
+    out = oracle.mlp_up_gelu_quant(codes, scales, d["w_codes"], d["w_scales"], xl1, d["l2t"], d["bias"],
+                                   lam_down, l1t_down, **kw)
+    y, _ = oracle.w4a4_linear(1, codes, scales, d["w_codes"], d["w_scales"], xl1, d["l2t"], d["bias"],
+                              alpha_a=d["alpha_a"], alpha_w=d["alpha_w"])
+    np.testing.assert_array_equal(out["y"], y)
+    _, hb = oracle.gelu(y)
+    np.testing.assert_array_equal(out["h_bf16"], hb)
+    c2, s2 = oracle.quantize_act(1, hb, lam_down, alpha=ao)
+    assert out["scales"].dtype == np.uint8 and out["scales"].shape == (8, 256 // 16)
+    np.testing.assert_array_equal(out["codes"], c2)
+    np.testing.assert_array_equal(out["scales"], s2)
+    np.testing.assert_array_equal(out["xl1"], oracle.lowrank_down(hb, l1t_down))
+    # every code decodes to within half an E2M1 step of xh / (s alpha) (E2M1
+    # steps 0.5 / 1 / 2 above 0 / 2 / 4), or saturates at 6
+    s = oracle.e4m3_to_f32(out["scales"]).astype(np.float64)
+    lo, hi = out["codes"] & 0xF, out["codes"] >> 4
+    q = np.stack([lo, hi], -1).reshape(8, 256)
+    v = oracle.e2m1_to_f32(q).astype(np.float64)
+    t = out["xh"].astype(np.float64) / (np.repeat(s, 16, axis=1) * ao)
+    half = np.where(np.abs(v) < 2, 0.25, np.where(np.abs(v) < 4, 0.5, 1.0))
+    assert np.all((np.abs(v - t) <= half * (1 + 1e-6)) | ((np.abs(v) == 6) & (np.abs(t) >= 5)))
+    some = oracle.mlp_up_gelu_quant(codes, scales, d["w_codes"], d["w_scales"], xl1, d["l2t"], d["bias"],
+                                    lam_down, l1t_down, rows=[6, 1], **kw)
+    np.testing.assert_array_equal(some["codes"], out["codes"][[6, 1]])
+    np.testing.assert_array_equal(some["scales"], out["scales"][[6, 1]])
+
+
+@pytest.mark.parametrize("prec", [synth.INT4, synth.NVFP4])
+def test_mlp_layer_generator(prec):
+    # shapes, dtypes and format of the synthetic MLP pair in both precisions
+    case = synth.mlp_layer(5, 20, 256, 128, 16, prec)
+    up, dn = case["up"], case["down"]
+    G = 64 if prec == synth.INT4 else 16
+    assert up["N"] == 256 and up["K"] == 128 and dn["N"] == 128 and dn["K"] == 256
+    assert dn["w_codes"].shape == (128, 128) and dn["w_codes"].dtype == np.uint8
+    assert dn["w_scales"].shape == (128, 256 // G)
+    assert dn["w_scales"].dtype == (np.uint16 if prec == synth.INT4 else np.uint8)
+    assert dn["l1t"].shape == (16, 256) and dn["l2t"].shape == (128, 16) and dn["lam"].shape == (256,)
+    if prec == synth.NVFP4:
+        assert dn["alpha_a"] == 2.0 ** -6 and dn["alpha_w"] == 2.0 ** -6
+        sw = oracle.e4m3_to_f32(dn["w_scales"]).astype(np.float64) * dn["alpha_w"]
+        assert np.all((sw >= 0.005 * (1 - 2 ** -4)) & (sw <= 0.02 * (1 + 2 ** -4)))  # one E4M3 rounding
+    else:
+        assert dn["alpha_a"] == 1.0 and dn["alpha_w"] == 1.0
