@@ -3,8 +3,9 @@
 One step = one pass of the whole hot path over one batch of synthetic input:
   1. svdq_quantize_act  on the DiT fused-QKV projection input X [4608, 3072]
      (smoothing, int4 group-64 codes and scales, fused X.L1 with rank 32),
-  2. svdq_w4a4_gemm     against W [9216, 3072] (int4 group 64) with the fused
-     low-rank up-projection and bias, Y bf16 [4608, 9216],
+  2. svdq_w4a4_gemm_ws  against W [9216, 3072] (int4 group 64) with the fused
+     low-rank up-projection and bias, Y bf16 [4608, 9216] (with its workspace:
+     the grid's last partial round of tiles runs as K slices),
   3. awq_w4a16_gemv     on the modulation projection x [2, 3072] x W [18432, 3072].
 Inputs are resident in HBM before timing starts; several copies of every input
 are cycled so that the 256 MB Infinity Cache cannot serve a step from the
@@ -156,6 +157,7 @@ def main():
     SCALES = [torch.empty((M, K // 64), dtype=torch.float16, device=dev) for _ in range(C)]
     XL1 = [torch.empty((M, R), dtype=torch.float32, device=dev) for _ in range(C)]
     Y = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    WORK = sq.gemm_workspace(dev)  # the GEMM's split last round of tiles (svdq_w4a4_gemm_ws)
 
     A = max(1, args.awq_copies)
     AX = bf(awq["x"])
@@ -179,7 +181,7 @@ def main():
         if gemm_ev is not None:
             gemm_ev[0].record(stream)
         sq.w4a4_gemm(sq.SVDQ_INT4, CODES[c], SCALES[c], WC[c], WS[c], XL1[c], L2T, BIAS, out=Y[i % 2],
-                     stream=stream)
+                     stream=stream, workspace=WORK)
         if ev is not None:
             ev[2].record(stream)
         if gemm_ev is not None:
@@ -468,6 +470,22 @@ def extras(args, torch, sq, synth, t, bf, f16, stream):
     dst = torch.empty_like(src)
     ms = median_ms(lambda i: dst.copy_(src), 5, stream, torch)
     res["copy_attainable_GBps"] = round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+
+    # context, not this library: the vendor's dense GEMMs (hipBLASLt under torch) at the
+    # QKV projection's shape, int8 x int8 -> int32 with the weight as [N, K] (no group
+    # scales, no low-rank branch, no bias) and bf16 x bf16 -> bf16
+    M, N, K = 4608, 9216, 3072
+    a8 = torch.randint(-8, 8, (M, K), dtype=torch.int8, device=dev)
+    w8 = torch.randint(-8, 8, (N, K), dtype=torch.int8, device=dev)
+    ab = torch.randn(M, K, dtype=torch.bfloat16, device=dev)
+    wb = torch.randn(N, K, dtype=torch.bfloat16, device=dev)
+    ops = 2 * M * N * K
+    ms8 = median_ms(lambda i: torch._int_mm(a8, w8.t()), n, stream, torch)
+    msb = median_ms(lambda i: torch.mm(ab, wb.t()), n, stream, torch)
+    res["library_gemm_4608x9216x3072"] = {
+        "int8_int_mm_ms": round(ms8, 5), "int8_TOPS": round(ops / (ms8 * 1e-3) / 1e12, 1),
+        "bf16_mm_ms": round(msb, 5), "bf16_TFLOPS": round(ops / (msb * 1e-3) / 1e12, 1)}
     return res
 
 

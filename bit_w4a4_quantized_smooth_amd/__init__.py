@@ -30,7 +30,10 @@ GROUP = {SVDQ_INT4: 64, SVDQ_NVFP4: 16}
 _STATUS = {0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARG", 2: "SVDQ_ERR_UNSUPPORTED",
            3: "SVDQ_ERR_ALIGNMENT", 4: "SVDQ_ERR_DEVICE"}
 
-EXPORTS = ["svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_qkv_norm_rope", "svdq_w4a4_gemm_gelu_quant",
+# SVDQ_GEMM_WORK_BYTES: size of svdq_w4a4_gemm_ws's workspace
+GEMM_WORK_BYTES = 16 * 1024 * 1024 + 4096
+
+EXPORTS = ["svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_ws", "svdq_w4a4_gemm_qkv_norm_rope", "svdq_w4a4_gemm_gelu_quant",
            "awq_w4a16_gemv", "svdq_calibrate_smooth", "svdq_lowrank_workspace_bytes", "svdq_lowrank_decompose",
            "svdq_lowrank_decompose_noalloc",
            "svdq_quantize_weight", "awq_quantize_weight",
@@ -59,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.svdq_quantize_act.argtypes = [i32, i32, i32, i64, i64, vp, vp, vp, f32, vp, vp, vp, vp]
         L.svdq_w4a4_gemm.argtypes = [i32, i32, i32, i64, i64, i64, vp, vp, f32, vp, vp, f32, vp, vp,
                                      vp, vp, vp]
+        L.svdq_w4a4_gemm_ws.argtypes = [i32, i32, i32, i64, i64, i64, vp, vp, f32, vp, vp, f32, vp, vp,
+                                        vp, vp, vp, i64, vp]
         L.svdq_w4a4_gemm_qkv_norm_rope.argtypes = [i32, i32, i32, i64, i32, i32, i64, vp, vp, f32, vp, vp,
                                                    f32, vp, vp, vp, vp, vp, f32, vp, i64, vp, vp]
         L.svdq_w4a4_gemm_gelu_quant.argtypes = [i32, i32, i32, i64, i64, i64, vp, vp, f32, vp, vp, f32, vp, vp,
@@ -72,7 +77,7 @@ def lib() -> ctypes.CDLL:
         L.svdq_quantize_weight.argtypes = [i32, i32, i64, i64, vp, f32, vp, vp, vp]
         L.awq_quantize_weight.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
         L.svdq_w4a4_group_psums.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp]
-        for f in ("svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_qkv_norm_rope",
+        for f in ("svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_ws", "svdq_w4a4_gemm_qkv_norm_rope",
                   "svdq_w4a4_gemm_gelu_quant", "awq_w4a16_gemv", "svdq_w4a4_group_psums", "svdq_calibrate_smooth",
                   "svdq_lowrank_decompose", "svdq_lowrank_decompose_noalloc", "svdq_quantize_weight",
                   "awq_quantize_weight"):
@@ -191,17 +196,26 @@ def _gemm_args(fn, precision, act_codes, act_scales, w_codes, w_scales, xl1, l2t
     return a, M, N, K, G, r
 
 
+def gemm_workspace(device=None):
+    """A zero-filled workspace for w4a4_gemm(..., workspace=): u8 [GEMM_WORK_BYTES] on
+    `device`.  One per stream that may run GEMMs at the same time as another."""
+    return torch.zeros((GEMM_WORK_BYTES,), dtype=_U8, device=device if device is not None else "cuda")
+
+
 def w4a4_gemm(precision: int, act_codes, act_scales, w_codes, w_scales, xl1=None, l2t=None,
               bias=None, act_global_scale: float = 1.0, w_global_scale: float = 1.0, out=None,
-              stream=None):
-    """svdq_w4a4_gemm.  Returns Y bf16 [M, N]."""
+              stream=None, workspace=None):
+    """svdq_w4a4_gemm, or svdq_w4a4_gemm_ws when `workspace` (see gemm_workspace) is
+    given.  Returns Y bf16 [M, N]."""
     a, M, N, K, G, r = _gemm_args("w4a4_gemm", precision, act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias)
     y = out if out is not None else torch.empty((M, N), dtype=_BF16, device=act_codes.device)
-    a.req("y", y, _BF16, (M, N)).done()
-    _check(lib().svdq_w4a4_gemm(precision, G, r, M, N, K, _ptr(act_codes), _ptr(act_scales),
-                                float(act_global_scale), _ptr(w_codes), _ptr(w_scales),
-                                float(w_global_scale), _ptr(xl1), _ptr(l2t), _ptr(bias), _ptr(y),
-                                _stream(stream)))
+    a.req("y", y, _BF16, (M, N)).req("workspace", workspace, _U8, (GEMM_WORK_BYTES,), True).done()
+    args = (precision, G, r, M, N, K, _ptr(act_codes), _ptr(act_scales), float(act_global_scale), _ptr(w_codes),
+            _ptr(w_scales), float(w_global_scale), _ptr(xl1), _ptr(l2t), _ptr(bias), _ptr(y))
+    if workspace is None:
+        _check(lib().svdq_w4a4_gemm(*args, _stream(stream)))
+    else:
+        _check(lib().svdq_w4a4_gemm_ws(*args, _ptr(workspace), GEMM_WORK_BYTES, _stream(stream)))
     return y
 
 

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
     int M, int N, int K, int rank, const uint8_t* __restrict__ ac, const uint16_t* __restrict__ as,
     const uint8_t* __restrict__ wc, const uint16_t* __restrict__ ws, const float* __restrict__ xl1,
     const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-    int32_t* __restrict__ psums, QkvEpi qe, MlpEpi me) {
+    int32_t* __restrict__ psums, QkvEpi qe, MlpEpi me, TailSplit ts) {
   static_assert(SPLIT == 1 || (SPLIT == 2 && MODE == 0), "K split only for the plain GEMM");
   extern __shared__ __align__(16) uint8_t smem[];
   const int half = SPLIT == 2 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x / NT) : 0;
@@ -133,7 +133,25 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
   const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;  // N % 128 == 0
   const int tiles = m_tiles * n_tiles;
   int t = blockIdx.x;
-  if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
+  // A K slice of a tile of the last partial round (plain GEMM, grid split by
+  // the launcher): its tile is one of the last tail/8 of its XCD's range, so
+  // every slice of a tile runs on the same XCD as the tile's neighbours.
+  int slice = -1, tail_idx = 0;
+  constexpr bool kTailSplit = MODE == 0 && SPLIT == 1;
+  if ((tiles & 7) == 0) {
+    const int tpx = tiles >> 3;
+    if (kTailSplit && ts.parts > 0 && t >= ts.full) {
+      const int sb = t - ts.full, tail_px = ts.tail >> 3, j = sb >> 3;
+      const int tt = j % tail_px;
+      slice = j / tail_px;
+      tail_idx = (sb & 7) * tail_px + tt;
+      t = (sb & 7) * tpx + (tpx - tail_px) + tt;
+    } else if (kTailSplit && ts.parts > 0) {
+      t = (t & 7) * tpx + (t >> 3);  // whole tiles: the first tpx - tail/8 of each XCD's range
+    } else {
+      t = (t & 7) * tpx + (t >> 3);
+    }
+  }
   constexpr int kBandM = 12;
   const int band = t / (kBandM * n_tiles), in_band = t - band * (kBandM * n_tiles);
   const int band_m0 = band * kBandM;
@@ -142,8 +160,12 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
   const int wn = (wave / WAVES_M) * (BI * 16), wm = (wave % WAVES_M) * (BJ * 16);
   const int G = K >> 6;
   const int stages = (G + KG - 1) / KG;
-  const int lstages = stages / SPLIT;  // stages of this copy (SPLIT divides stages)
-  const int s_off = half * lstages;    // its first stage
+  int lstages = stages / SPLIT;  // stages of this copy (SPLIT divides stages)
+  int s_off = half * lstages;    // its first stage
+  if (kTailSplit && slice >= 0) {  // slice p: stages [p*stages/parts, (p+1)*stages/parts)
+    s_off = slice * stages / ts.parts;
+    lstages = (slice + 1) * stages / ts.parts - s_off;
+  }
   const int rowb = K >> 1;
 
   // Buffer resources: reads past the last row return zeros (the M and N tails).
@@ -405,6 +427,63 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
           acc[2 * pi + (q >> 1)][2 * pj + (q & 1)][v] =
               fmaf(sbuf[Qp & 1][4 * q + v], __int_as_float(dbuf[Qp & 1][q][v]),
                    acc[2 * pi + (q >> 1)][2 * pj + (q & 1)][v]);
+    }
+    if constexpr (kTailSplit) {
+      if (slice >= 0) {
+        // A K slice: store the partial accumulators with agent-coherent stores,
+        // wait until they are performed, then count this slice in; the last
+        // slice of the tile to arrive sums all partials in slice order (the
+        // same sums whichever slice it is) and runs the epilogue.  No
+        // workgroup waits for another.
+        constexpr int PER = (NT / 64) * BI * BJ * 64 * 4;  // floats of one partial tile
+        static_assert(PER * 4 == kTailTileBytes, "partial tile size");
+        float* const base = ts.part + (size_t)tail_idx * ts.parts * PER;
+        uint64_t* const mine = (uint64_t*)(base + (size_t)slice * PER) + ((size_t)wave * BI * BJ * 64 + lane) * 2;
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+#pragma unroll
+          for (int j = 0; j < BJ; ++j) {
+            const uint4 v = __builtin_bit_cast(uint4, acc[i][j]);
+            uint64_t* const d = mine + (size_t)(i * BJ + j) * 64 * 2;
+            __hip_atomic_store(d, (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(d + 1, (uint64_t)v.z | ((uint64_t)v.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);  // every store of this wave performed
+        __syncthreads();
+        unsigned* const flag = (unsigned*)sm;  // staging LDS is free: the loop's last barrier is behind
+        if (tid == 0)
+          *flag = __hip_atomic_fetch_add(ts.cnt + tail_idx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const unsigned arrived = __builtin_amdgcn_readfirstlane(*(volatile unsigned*)flag);
+        if (arrived != (unsigned)ts.parts - 1) return;
+        if (tid == 0) __hip_atomic_store(ts.cnt + tail_idx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v4f sum[BI][BJ];
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+#pragma unroll
+          for (int j = 0; j < BJ; ++j) sum[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < ts.parts; ++q) {
+          const uint64_t* const src = (const uint64_t*)(base + (size_t)q * PER) + ((size_t)wave * BI * BJ * 64 + lane) * 2;
+#pragma unroll
+          for (int i = 0; i < BI; ++i)
+#pragma unroll
+            for (int j = 0; j < BJ; ++j) {
+              v4f p = acc[i][j];
+              if (q != slice) {
+                const uint64_t* const s2 = src + (size_t)(i * BJ + j) * 64 * 2;
+                const uint64_t lo = __hip_atomic_load(s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t hi = __hip_atomic_load(s2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                p = __builtin_bit_cast(v4f, uint4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)});
+              }
+              sum[i][j] += p;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+#pragma unroll
+          for (int j = 0; j < BJ; ++j) acc[i][j] = sum[i][j];
+      }
     }
     if constexpr (SPLIT == 2) {
       // the second copy's accumulators, through its own staging LDS (every
@@ -772,6 +851,26 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
   }
 }
 
+// The plain grid's last partial round, split along K when a workspace is
+// given: grids of more than one round of two tiles per CU whose last round
+// holds at most an eighth of a round (2592 tiles of the 4608 x 9216 QKV shape:
+// 32 left on 512 slots), with at least eight two-group stages.  Measured on
+// that shape: 2, 3, 4 and 6 slices per tile all take ~200 us against 206.5 us
+// unsplit; 8 slices 205.7 us.
+static TailSplit tail_split(int blocks, int groups, void* work) {
+  TailSplit ts{};
+  const int slots = 2 * device_cu_count(), stages = (groups + KG - 1) / KG;
+  if (!work || (blocks & 7) || (slots & 7) || blocks <= slots || stages < 8) return ts;
+  const int tail = blocks % slots;  // a multiple of 8 (blocks and slots are)
+  if (tail == 0 || tail > slots / 8 || tail > kTailMaxTiles) return ts;
+  ts.full = blocks - tail;
+  ts.tail = tail;
+  ts.parts = kTailParts;
+  ts.part = (float*)work;
+  ts.cnt = (unsigned*)((uint8_t*)work + kTailPartBytes);
+  return ts;
+}
+
 // Test hook: when set, the plain GEMM never takes the K-split instance.
 static std::atomic<int> g_no_ksplit{0};
 void set_no_ksplit(int v) { g_no_ksplit.store(v ? 1 : 0); }
@@ -791,22 +890,23 @@ hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   const QkvEpi qnone{};
   const MlpEpi mnone{};
+  const TailSplit tnone{};
   if (a.psums) {
     hipLaunchKernelGGL(k1, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, 0,
                        (const uint8_t*)a.act_codes, nullptr, (const uint8_t*)a.w_codes, nullptr, nullptr,
-                       nullptr, nullptr, nullptr, (int32_t*)a.psums, qnone, mnone);
+                       nullptr, nullptr, nullptr, (int32_t*)a.psums, qnone, mnone, tnone);
   } else if (a.qkv) {
     hipLaunchKernelGGL(k2, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
                        (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
                        (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
-                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, *a.qkv, mnone);
+                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, *a.qkv, mnone, tnone);
   } else if (a.mlp) {
     const int nx = (int)(a.M * a.mlp->rank);
     if (nx > 0) hipLaunchKernelGGL(fill_zero_f32, dim3((nx + 255) / 256), dim3(256), 0, st, a.mlp->xl1, nx);
     hipLaunchKernelGGL(k3, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
                        (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
                        (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
-                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, nullptr, nullptr, qnone, *a.mlp);
+                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, nullptr, nullptr, qnone, *a.mlp, tnone);
   } else {
     // A grid of at most one tile per CU runs on the K-split kernel (needs an
     // even number of two-group stages: K % 256 == 0).  Sending only the last
@@ -818,12 +918,14 @@ hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(ks, dim3(blocks), dim3(2 * NT), 2 * LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
                          (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
                          (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
-                         (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, qnone, mnone);
+                         (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, qnone, mnone, tnone);
     } else {
-      hipLaunchKernelGGL(k0, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
+      const TailSplit ts = tail_split(blocks, (int)(a.K / 64), a.work);
+      const int grid = ts.parts > 0 ? ts.full + ts.tail * ts.parts : blocks;
+      hipLaunchKernelGGL(k0, dim3(grid), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
                          (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
                          (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
-                         (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, qnone, mnone);
+                         (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, qnone, mnone, ts);
     }
   }
   return hipGetLastError();

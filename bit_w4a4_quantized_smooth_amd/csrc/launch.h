@@ -60,6 +60,26 @@ struct MlpEpi {
   float alpha;  // nvfp4: the down projection's activation global scale
 };
 
+// The last partial round of the plain int4 GEMM's tile grid, split along K.
+// Blocks [0, full) run whole tiles; the tiles left over (tail of them, the
+// last tail/8 of each XCD's range of the tile order) run as `parts` K slices
+// each, in blocks [full, full + tail * parts) of the same launch.  A slice
+// stores its fp32 accumulators in part, counts itself in cnt[tile], and the
+// last of a tile's slices to arrive sums all of them in slice order and runs
+// the epilogue.  cnt holds zeros between calls (the last slice resets it).
+struct TailSplit {
+  int full, tail, parts;  // parts == 0: no split
+  float* part;            // [tail][parts][NT/64 waves][BI*BJ blocks][64 lanes][4]
+  unsigned* cnt;          // [tail]
+};
+
+// Workspace of the split tail (svdq_w4a4_gemm_ws): partial tiles of up to
+// kTailMaxTiles tiles x kTailParts slices, then one counter per tile.
+constexpr int kTailMaxTiles = 64, kTailParts = 4;
+constexpr size_t kTailTileBytes = (size_t)128 * 128 * 4;  // fp32 accumulators of one 128 x 128 tile
+constexpr size_t kTailPartBytes = (size_t)kTailMaxTiles * kTailParts * kTailTileBytes;
+constexpr size_t kGemmWorkBytes = kTailPartBytes + 4096;
+
 struct GemmArgs {
   int precision, rank;
   int64_t M, N, K;
@@ -76,6 +96,7 @@ struct GemmArgs {
   void* psums;   // ... or [M, N, K/G] partial products (test support)
   const QkvEpi* qkv;  // non-null: Y with the Q/K norm and rotary epilogue
   const MlpEpi* mlp;  // non-null: no Y; GELU + the next layer's quantization
+  void* work;         // plain int4 GEMM: kGemmWorkBytes, counters zero, or null
 };
 
 struct AwqArgs {

@@ -183,7 +183,7 @@ static svdq_status gemm_y(int precision, int group_size, int rank, int64_t M, in
                           float act_global_scale, const void* w_codes, const void* w_scales,
                           float w_global_scale, const float* xl1, const void* l2t,
                           const void* bias, void* y, void* stream, const svdq::QkvEpi* qkv,
-                          size_t rope_bytes) {
+                          size_t rope_bytes, void* work = nullptr) {
   svdq_status s;
   if ((s = gemm_common(precision, group_size, rank, M, N, K, act_codes, w_codes)) != SVDQ_OK) return s;
   if (M == 0) return ok();  // empty call: nothing to read or write
@@ -224,7 +224,7 @@ static svdq_status gemm_y(int precision, int group_size, int rank, int64_t M, in
   if (M == 0) return ok();
   if ((s = check_sticky()) != SVDQ_OK) return s;
   svdq::GemmArgs a{precision, rank, M, N, K, act_codes, act_scales, act_global_scale, w_codes,
-                   w_scales, w_global_scale, xl1, l2t, bias, y, nullptr, qkv, nullptr};
+                   w_scales, w_global_scale, xl1, l2t, bias, y, nullptr, qkv, nullptr, work};
   return launched(precision == SVDQ_INT4 ? svdq::launch_gemm_int4(a, (hipStream_t)stream)
                                          : svdq::launch_gemm_nvfp4(a, (hipStream_t)stream));
 }
@@ -236,6 +236,34 @@ svdq_status svdq_w4a4_gemm(int precision, int group_size, int rank, int64_t M, i
                            const void* bias, void* y, void* stream) {
   return gemm_y(precision, group_size, rank, M, N, K, act_codes, act_scales, act_global_scale, w_codes,
                 w_scales, w_global_scale, xl1, l2t, bias, y, stream, nullptr, 0);
+}
+
+static_assert(SVDQ_GEMM_WORK_BYTES == svdq::kGemmWorkBytes, "workspace size of the header and the kernels");
+
+svdq_status svdq_w4a4_gemm_ws(int precision, int group_size, int rank, int64_t M, int64_t N,
+                              int64_t K, const void* act_codes, const void* act_scales,
+                              float act_global_scale, const void* w_codes, const void* w_scales,
+                              float w_global_scale, const float* xl1, const void* l2t,
+                              const void* bias, void* y, void* work, int64_t work_bytes, void* stream) {
+  if (work) {
+    if (work_bytes < (int64_t)SVDQ_GEMM_WORK_BYTES)
+      return fail(SVDQ_ERR_INVALID_ARG, "work_bytes=%lld below SVDQ_GEMM_WORK_BYTES=%lld", (long long)work_bytes,
+                  (long long)SVDQ_GEMM_WORK_BYTES);
+    if (!aligned16(work)) return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
+    const size_t nw = SVDQ_GEMM_WORK_BYTES;
+    const size_t ns_a = precision == SVDQ_INT4 ? (size_t)M * (K / 64) * 2 : (size_t)M * (K / 16);
+    const size_t ns_w = precision == SVDQ_INT4 ? (size_t)N * (K / 64) * 2 : (size_t)N * (K / 16);
+    if (M >= 0 && N > 0 && K > 0 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim && rank >= 0 && rank <= 128 &&
+        (overlaps(work, nw, y, (size_t)M * N * 2) || overlaps(work, nw, act_codes, (size_t)M * K / 2) ||
+         overlaps(work, nw, w_codes, (size_t)N * K / 2) || overlaps(work, nw, act_scales, ns_a) ||
+         overlaps(work, nw, w_scales, ns_w) || overlaps(work, nw, xl1, (size_t)M * rank * 4) ||
+         overlaps(work, nw, l2t, (size_t)N * rank * 2) || overlaps(work, nw, bias, (size_t)N * 2)))
+      return fail(SVDQ_ERR_INVALID_ARG, "work must not overlap y or an input");
+  } else if (work_bytes != 0) {
+    return fail(SVDQ_ERR_INVALID_ARG, "work_bytes=%lld given without work", (long long)work_bytes);
+  }
+  return gemm_y(precision, group_size, rank, M, N, K, act_codes, act_scales, act_global_scale, w_codes,
+                w_scales, w_global_scale, xl1, l2t, bias, y, stream, nullptr, 0, precision == SVDQ_INT4 ? work : nullptr);
 }
 
 svdq_status svdq_w4a4_gemm_qkv_norm_rope(int precision, int group_size, int rank, int64_t M,

@@ -122,6 +122,34 @@ svdq_status svdq_w4a4_gemm(int precision, int group_size, int rank, int64_t M, i
                            const void* bias, void* y, void* stream);
 
 /*
+ * svdq_w4a4_gemm_ws -- svdq_w4a4_gemm with a caller-owned workspace: the same
+ * product (blog, "Background: SVDQuant and Nunchaku"), where the int4 kernel
+ * may run the tiles of its grid's last partial round as K slices spread over
+ * the CUs.  The slices' fp32 partial accumulators meet in `work`, and the last
+ * slice of a tile to finish adds them up in slice order and writes the tile.
+ * Those tiles' fp32 sums are then formed in another order than
+ * svdq_w4a4_gemm's, so their Y can differ from it in the last bit (the same
+ * bits from call to call).
+ *
+ *   work        NULL (then exactly svdq_w4a4_gemm; work_bytes must be 0), or
+ *               device memory of at least SVDQ_GEMM_WORK_BYTES bytes, 16-byte
+ *               aligned, not overlapping y or an input, zero-filled before
+ *               its first use.  A call leaves its counter words zero again (the
+ *               rest is scratch), so the same workspace serves every later
+ *               call on the same stream; calls that may run at the same time
+ *               (other streams) need workspaces of their own.  Ignored for
+ *               nvfp4.
+ *   work_bytes  its size in bytes
+ *   the other arguments, limits and errors as for svdq_w4a4_gemm
+ */
+#define SVDQ_GEMM_WORK_BYTES ((int64_t)16 * 1024 * 1024 + 4096)
+svdq_status svdq_w4a4_gemm_ws(int precision, int group_size, int rank, int64_t M, int64_t N,
+                              int64_t K, const void* act_codes, const void* act_scales,
+                              float act_global_scale, const void* w_codes, const void* w_scales,
+                              float w_global_scale, const float* xl1, const void* l2t,
+                              const void* bias, void* y, void* work, int64_t work_bytes, void* stream);
+
+/*
  * svdq_w4a4_gemm_qkv_norm_rope -- the fused attention projection: the 4-bit
  * GEMM of the grouped Q/K/V weights with the per-head RMSNorm of Q and K and
  * the rotary embedding applied to its fp32 result inside the epilogue, so Y

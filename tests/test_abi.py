@@ -261,3 +261,29 @@ def test_noalloc_decompose_limits(L):
     assert na(1536, 768, r=24) == UNSUPPORTED                                   # the same rank rules
     assert L.svdq_lowrank_decompose_noalloc(1536, 768, 32, 16, 4, None, 2 * B, 3 * B, 4 * B, 5 * B, 6 * B,
                                             None) == INVALID
+
+
+def gemm_ws(L, work=64 * A, work_bytes=sq.GEMM_WORK_BYTES, prec=0, G=64, M=256, y=8 * A, ac=A):
+    return L.svdq_w4a4_gemm_ws(prec, G, 16, M, 512, 512, ac, 2 * A, 1.0, 3 * A, 4 * A, 1.0, 5 * A, 6 * A, 7 * A, y,
+                               work, work_bytes, None)
+
+
+def test_gemm_workspace_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+SVDQ_GEMM_WORK_BYTES\s+\(\(int64_t\)\s*16\s*\*\s*1024\s*\*\s*1024\s*\+\s*4096\)", text)
+    assert m, "SVDQ_GEMM_WORK_BYTES definition changed"
+    assert sq.GEMM_WORK_BYTES == 16 * 1024 * 1024 + 4096
+
+
+def test_gemm_workspace_validation(L):
+    assert gemm_ws(L) == UNSUPPORTED                              # valid: reaches the arch check
+    assert gemm_ws(L, work=None, work_bytes=0) == UNSUPPORTED     # no workspace: the plain GEMM
+    assert gemm_ws(L, prec=1, G=16) == UNSUPPORTED                # nvfp4: the workspace is ignored
+    assert gemm_ws(L, work=None, work_bytes=4096) == INVALID      # a size without a buffer
+    assert gemm_ws(L, work_bytes=sq.GEMM_WORK_BYTES - 1) == INVALID and b"SVDQ_GEMM_WORK_BYTES" in L.svdq_last_error()
+    assert gemm_ws(L, work=64 * A + 8) == ALIGN
+    assert gemm_ws(L, work=8 * A - 4096) == INVALID               # overlaps y
+    assert gemm_ws(L, work=A - 4096) == INVALID                   # overlaps act_codes
+    assert gemm_ws(L, y=None) == INVALID                          # the plain GEMM's own checks still apply
+    L.svdq_test_set_arch_override(b"gfx950")
+    assert gemm_ws(L, M=0) == OK

@@ -105,3 +105,14 @@ def test_layout_and_types():
         sq.quantize_act(sq.SVDQ_INT4, z(64, dtype=bf16))
     with pytest.raises(ValueError, match="must be a torch.Tensor"):
         call_gemm(bias=[0.0] * 128)
+
+
+def test_gemm_workspace_is_checked():
+    a = gemm_inputs()
+    args = (sq.SVDQ_INT4, a["act_codes"], a["act_scales"], a["w_codes"], a["w_scales"], a["xl1"], a["l2t"], a["bias"])
+    with pytest.raises(ValueError, match="workspace must have shape"):
+        sq.w4a4_gemm(*args, workspace=z(1024))
+    with pytest.raises(ValueError, match="workspace must be torch.uint8"):
+        sq.w4a4_gemm(*args, workspace=z(sq.GEMM_WORK_BYTES // 4, dtype=f32))
+    with pytest.raises(ValueError, match="not on a GPU"):
+        sq.w4a4_gemm(*args, workspace=z(sq.GEMM_WORK_BYTES))
