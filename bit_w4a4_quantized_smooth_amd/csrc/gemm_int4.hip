@@ -438,15 +438,17 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
         constexpr int PER = (NT / 64) * BI * BJ * 64 * 4;  // floats of one partial tile
         static_assert(PER * 4 == kTailTileBytes, "partial tile size");
         float* const base = ts.part + (size_t)tail_idx * ts.parts * PER;
-        uint64_t* const mine = (uint64_t*)(base + (size_t)slice * PER) + ((size_t)wave * BI * BJ * 64 + lane) * 2;
+        // layout [wave][block][half][lane] of 8-byte words: each store
+        // instruction writes 512 contiguous bytes (whole lines)
+        uint64_t* const mine = (uint64_t*)(base + (size_t)slice * PER) + (size_t)wave * BI * BJ * 128 + lane;
 #pragma unroll
         for (int i = 0; i < BI; ++i)
 #pragma unroll
           for (int j = 0; j < BJ; ++j) {
             const uint4 v = __builtin_bit_cast(uint4, acc[i][j]);
-            uint64_t* const d = mine + (size_t)(i * BJ + j) * 64 * 2;
+            uint64_t* const d = mine + (size_t)(i * BJ + j) * 128;
             __hip_atomic_store(d, (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(d + 1, (uint64_t)v.z | ((uint64_t)v.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(d + 64, (uint64_t)v.z | ((uint64_t)v.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0);  // every store of this wave performed
@@ -464,16 +466,16 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
 #pragma unroll
           for (int j = 0; j < BJ; ++j) sum[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
         for (int q = 0; q < ts.parts; ++q) {
-          const uint64_t* const src = (const uint64_t*)(base + (size_t)q * PER) + ((size_t)wave * BI * BJ * 64 + lane) * 2;
+          const uint64_t* const src = (const uint64_t*)(base + (size_t)q * PER) + (size_t)wave * BI * BJ * 128 + lane;
 #pragma unroll
           for (int i = 0; i < BI; ++i)
 #pragma unroll
             for (int j = 0; j < BJ; ++j) {
               v4f p = acc[i][j];
               if (q != slice) {
-                const uint64_t* const s2 = src + (size_t)(i * BJ + j) * 64 * 2;
+                const uint64_t* const s2 = src + (size_t)(i * BJ + j) * 128;
                 const uint64_t lo = __hip_atomic_load(s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint64_t hi = __hip_atomic_load(s2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t hi = __hip_atomic_load(s2 + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 p = __builtin_bit_cast(v4f, uint4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)});
               }
               sum[i][j] += p;

@@ -69,7 +69,7 @@ struct MlpEpi {
 // the epilogue.  cnt holds zeros between calls (the last slice resets it).
 struct TailSplit {
   int full, tail, parts;  // parts == 0: no split
-  float* part;            // [tail][parts][NT/64 waves][BI*BJ blocks][64 lanes][4]
+  float* part;            // [tail][parts][NT/64 waves][BI*BJ blocks][2 halves][64 lanes][2]
   unsigned* cnt;          // [tail]
 };
 
