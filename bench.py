@@ -41,7 +41,7 @@ PEAK_FP8_TFLOPS = 5000.0  # dense fp8
 PEAK_FP4_TFLOPS = 10100.0 # dense fp4 / fp6
 PEAK_BF16_TFLOPS = 2500.0 # dense bf16
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
-GEMM_SOURCES = ["gemm_int4.hip", "common.h", "launch.h"]
+GEMM_SOURCES = ["gemm_int4.hip", "tail_split.h", "common.h", "launch.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_int4_dit_qkv_4608x9216x3072.txt")
 
 
@@ -301,6 +301,7 @@ def extras(args, torch, sq, synth, t, bf, f16, stream):
     res = {}
     dev = torch.device("cuda:0")
     n = args.calls
+    work = sq.gemm_workspace(dev)
 
     def linear(name, seed, M, N, K, prec, outlier_frac, outlier_scale, kind="normal"):
         d = synth.svdq_layer(seed, M, N, K, 32, prec, outlier_frac, outlier_scale, kind)
@@ -318,7 +319,7 @@ def extras(args, torch, sq, synth, t, bf, f16, stream):
         q_ms = median_ms(lambda i: sq.quantize_act(prec, x, lam, l1t, aa, out=(codes, scales, xl1), stream=stream),
                          n, stream, torch)
         g_ms = median_ms(lambda i: sq.w4a4_gemm(prec, codes, scales, wc, ws, xl1, l2t, bias, aa, aw, out=y,
-                                                stream=stream), n, stream, torch)
+                                                stream=stream, workspace=work), n, stream, torch)
         ops = 2.0 * M * N * K
         tops = ops / (g_ms * 1e-3) / 1e12
         qb = M * K * 2 + K * 2 + 32 * K * 2 + M * K // 2 + M * (K // G) * (2 if prec == sq.SVDQ_INT4 else 1) + M * 32 * 4

@@ -51,6 +51,7 @@
 #include "launch.h"
 #include "mlp_epi.h"
 #include "qkv_epi.h"
+#include "tail_split.h"
 
 namespace svdq {
 
@@ -138,20 +139,7 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
   // every slice of a tile runs on the same XCD as the tile's neighbours.
   int slice = -1, tail_idx = 0;
   constexpr bool kTailSplit = MODE == 0 && SPLIT == 1;
-  if ((tiles & 7) == 0) {
-    const int tpx = tiles >> 3;
-    if (kTailSplit && ts.parts > 0 && t >= ts.full) {
-      const int sb = t - ts.full, tail_px = ts.tail >> 3, j = sb >> 3;
-      const int tt = j % tail_px;
-      slice = j / tail_px;
-      tail_idx = (sb & 7) * tail_px + tt;
-      t = (sb & 7) * tpx + (tpx - tail_px) + tt;
-    } else if (kTailSplit && ts.parts > 0) {
-      t = (t & 7) * tpx + (t >> 3);  // whole tiles: the first tpx - tail/8 of each XCD's range
-    } else {
-      t = (t & 7) * tpx + (t >> 3);
-    }
-  }
+  if ((tiles & 7) == 0) t = split_tile_of(t, tiles, kTailSplit ? ts : TailSplit{}, slice, tail_idx);
   constexpr int kBandM = 12;
   const int band = t / (kBandM * n_tiles), in_band = t - band * (kBandM * n_tiles);
   const int band_m0 = band * kBandM;
@@ -429,63 +417,13 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
                    acc[2 * pi + (q >> 1)][2 * pj + (q & 1)][v]);
     }
     if constexpr (kTailSplit) {
-      if (slice >= 0) {
-        // A K slice: store the partial accumulators with agent-coherent stores,
-        // wait until they are performed, then count this slice in; the last
-        // slice of the tile to arrive sums all partials in slice order (the
-        // same sums whichever slice it is) and runs the epilogue.  No
-        // workgroup waits for another.
-        constexpr int PER = (NT / 64) * BI * BJ * 64 * 4;  // floats of one partial tile
-        static_assert(PER * 4 == kTailTileBytes, "partial tile size");
-        float* const base = ts.part + (size_t)tail_idx * ts.parts * PER;
-        // layout [wave][block][half][lane] of 8-byte words: each store
-        // instruction writes 512 contiguous bytes (whole lines)
-        uint64_t* const mine = (uint64_t*)(base + (size_t)slice * PER) + (size_t)wave * BI * BJ * 128 + lane;
-#pragma unroll
-        for (int i = 0; i < BI; ++i)
-#pragma unroll
-          for (int j = 0; j < BJ; ++j) {
-            const uint4 v = __builtin_bit_cast(uint4, acc[i][j]);
-            uint64_t* const d = mine + (size_t)(i * BJ + j) * 128;
-            __hip_atomic_store(d, (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(d + 64, (uint64_t)v.z | ((uint64_t)v.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);  // every store of this wave performed
-        __syncthreads();
-        unsigned* const flag = (unsigned*)sm;  // staging LDS is free: the loop's last barrier is behind
-        if (tid == 0)
-          *flag = __hip_atomic_fetch_add(ts.cnt + tail_idx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        const unsigned arrived = __builtin_amdgcn_readfirstlane(*(volatile unsigned*)flag);
-        if (arrived != (unsigned)ts.parts - 1) return;
-        if (tid == 0) __hip_atomic_store(ts.cnt + tail_idx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v4f sum[BI][BJ];
-#pragma unroll
-        for (int i = 0; i < BI; ++i)
-#pragma unroll
-          for (int j = 0; j < BJ; ++j) sum[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-        for (int q = 0; q < ts.parts; ++q) {
-          const uint64_t* const src = (const uint64_t*)(base + (size_t)q * PER) + (size_t)wave * BI * BJ * 128 + lane;
-#pragma unroll
-          for (int i = 0; i < BI; ++i)
-#pragma unroll
-            for (int j = 0; j < BJ; ++j) {
-              v4f p = acc[i][j];
-              if (q != slice) {
-                const uint64_t* const s2 = src + (size_t)(i * BJ + j) * 128;
-                const uint64_t lo = __hip_atomic_load(s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint64_t hi = __hip_atomic_load(s2 + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                p = __builtin_bit_cast(v4f, uint4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)});
-              }
-              sum[i][j] += p;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < BI; ++i)
-#pragma unroll
-          for (int j = 0; j < BJ; ++j) acc[i][j] = sum[i][j];
-      }
+      // a K slice: partials through the workspace; the tile's last slice
+      // continues with the sum of all of them
+      if (slice >= 0 &&
+          !split_exchange<BI * BJ>(ts, tail_idx, slice, wave, lane, tid, (unsigned*)sm,
+                                   [&](int k) { return acc[k / BJ][k % BJ]; },
+                                   [&](int k, v4f v) { acc[k / BJ][k % BJ] = v; }))
+        return;
     }
     if constexpr (SPLIT == 2) {
       // the second copy's accumulators, through its own staging LDS (every

@@ -39,6 +39,7 @@
 #include "launch.h"
 #include "mlp_epi.h"
 #include "qkv_epi.h"
+#include "tail_split.h"
 
 namespace svdq {
 
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
     float alpha, const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
     const float* __restrict__ xl1, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, float* __restrict__ psums, QkvEpi qe,
-    MlpEpi me) {
+    MlpEpi me, TailSplit ts) {
   // One array: the activation tiles start 32 bytes past a multiple of 128
   // bytes from the weight tiles, so that a staging store whose lanes write
   // both (the same rows and halves of each) spreads over all the banks.
@@ -97,16 +98,24 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   // XCD-contiguous ranges of a banded tile order (see gemm_int4.hip)
   const int m_tiles = (M + BM - 1) / BM, n_tiles = N / BN;
   const int tiles = m_tiles * n_tiles;
-  int t = blockIdx.x;
-  if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
+  // the plain GEMM may run its grid's last partial round as K slices
+  // (tail_split.h): slices are whole 16-step scale blocks of K
+  int t = blockIdx.x, slice = -1, tail_idx = 0;
+  if ((tiles & 7) == 0) t = split_tile_of(t, tiles, MODE == 0 ? ts : TailSplit{}, slice, tail_idx);
   constexpr int kBandM = 12;
   const int band = t / (kBandM * n_tiles), in_band = t - band * (kBandM * n_tiles);
   const int band_m0 = band * kBandM;
   const int band_h = m_tiles - band_m0 < kBandM ? m_tiles - band_m0 : kBandM;
   const int m0 = (band_m0 + in_band % band_h) * BM, n0 = (in_band / band_h) * BN;
   const int wn = (wave >> 1) * 64, wm = (wave & 1) * 64;
-  const int steps = K >> 6, G = K >> 4;
+  int steps = K >> 6, st0 = 0;  // this workgroup's steps: [st0, st0 + steps)
+  const int G = K >> 4;
   const int rowb = K >> 1;
+  if (MODE == 0 && slice >= 0) {
+    const int nb = steps >> 4;
+    st0 = 16 * (slice * nb / ts.parts);
+    steps = 16 * ((slice + 1) * nb / ts.parts) - st0;
+  }
 
   // Staging.  Two K steps (128 channels) are 64 contiguous bytes of codes per
   // row; a load gives each lane 16 of them, four lanes per row, so one load
@@ -124,8 +133,8 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   const __amdgpu_buffer_rsrc_t wsres = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, MODE != 1 ? N * G : 0, kBufDword3);
   const __amdgpu_buffer_rsrc_t asres = __builtin_amdgcn_make_buffer_rsrc((void*)as, (short)0, MODE != 1 ? M * G : 0, kBufDword3);
   // rows past M read as zero (codes and scales)
-  const int wco = (n0 + r0) * rowb + 16 * p, xco = (m0 + r0) * rowb + 16 * (p ^ 2);
-  const int wso = (n0 + r0) * G, xso = (m0 + r0) * G;
+  const int wco = (n0 + r0) * rowb + 16 * p + 32 * st0, xco = (m0 + r0) * rowb + 16 * (p ^ 2) + 32 * st0;
+  const int wso = (n0 + r0) * G + 4 * st0, xso = (m0 + r0) * G + 4 * st0;
 
   v16f acc[2][2];
 #pragma unroll
@@ -262,6 +271,28 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
     }
     static_for([&](auto ic) { if (st + decltype(ic)::value < steps) stage(st + decltype(ic)::value, ic); },
                std::make_integer_sequence<int, 15>{});
+  }
+
+  if constexpr (MODE == 0) {
+    // a K slice: partials through the workspace; the tile's last slice
+    // continues with the sum of all of them (4-float vector k of this lane:
+    // acc[k / 8][(k / 4) % 2], elements 4 (k % 4) .. +3)
+    if (slice >= 0 &&
+        !split_exchange<16>(ts, tail_idx, slice, wave, lane, tid, (unsigned*)sWX,
+                            [&](int k) {
+                              const v16f& a = acc[k >> 3][(k >> 2) & 1];
+                              const int q = 4 * (k & 3);
+                              return v4f{a[q], a[q + 1], a[q + 2], a[q + 3]};
+                            },
+                            [&](int k, v4f v) {
+                              v16f& a = acc[k >> 3][(k >> 2) & 1];
+                              const int q = 4 * (k & 3);
+                              a[q] = v[0];
+                              a[q + 1] = v[1];
+                              a[q + 2] = v[2];
+                              a[q + 3] = v[3];
+                            }))
+      return;
   }
 
   if constexpr (MODE != 1) {
@@ -554,35 +585,58 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   }
 }
 
+// The plain grid's last partial round as K slices of whole 16-step scale
+// blocks, with a workspace: the same grids as the int4 GEMM's split (more
+// than one round of two tiles per CU, a last round of at most an eighth of a
+// round), K of at least two blocks; as many slices as blocks, at most
+// kTailParts (the 3072-channel QKV projection: three).
+static TailSplit nvfp4_tail_split(int blocks, int steps, void* work) {
+  TailSplit ts{};
+  const int slots = 2 * device_cu_count(), nb = steps / 16;
+  if (!work || (blocks & 7) || (slots & 7) || blocks <= slots || (steps % 16) || nb < 2) return ts;
+  const int tail = blocks % slots;
+  if (tail == 0 || tail > slots / 8 || tail > kTailMaxTiles) return ts;
+  ts.full = blocks - tail;
+  ts.tail = tail;
+  ts.parts = nb < kTailParts ? nb : kTailParts;
+  ts.part = (float*)work;
+  ts.cnt = (unsigned*)((uint8_t*)work + kTailPartBytes);
+  return ts;
+}
+
 hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st) {
   const int m_tiles = (int)((a.M + BM - 1) / BM);
   const int blocks = m_tiles * (int)(a.N / BN);  // N % 128 == 0
   const QkvEpi none{};
   const MlpEpi mnone{};
+  const TailSplit tnone{};
   if (a.psums) {
     hipLaunchKernelGGL(gemm_nvfp4_kernel<1>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
                        (int)a.K, 0, (const uint8_t*)a.act_codes, nullptr, 1.0f,
                        (const uint8_t*)a.w_codes, nullptr, nullptr, nullptr, nullptr, nullptr,
-                       (float*)a.psums, none, mnone);
+                       (float*)a.psums, none, mnone, tnone);
   } else if (a.qkv) {
     hipLaunchKernelGGL(gemm_nvfp4_kernel<2>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
                        (int)a.K, a.rank, (const uint8_t*)a.act_codes, (const uint8_t*)a.act_scales,
                        a.alpha_a * a.alpha_w, (const uint8_t*)a.w_codes, (const uint8_t*)a.w_scales,
                        a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr,
-                       *a.qkv, mnone);
+                       *a.qkv, mnone, tnone);
   } else if (a.mlp) {
     const int nx = (int)(a.M * a.mlp->rank);
     if (nx > 0) hipLaunchKernelGGL(fill_zero_f32, dim3((nx + 255) / 256), dim3(256), 0, st, a.mlp->xl1, nx);
     hipLaunchKernelGGL(gemm_nvfp4_kernel<3>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
                        (int)a.K, a.rank, (const uint8_t*)a.act_codes, (const uint8_t*)a.act_scales,
                        a.alpha_a * a.alpha_w, (const uint8_t*)a.w_codes, (const uint8_t*)a.w_scales,
-                       a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, nullptr, nullptr, none, *a.mlp);
+                       a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, nullptr, nullptr, none, *a.mlp,
+                       tnone);
   } else {
-    hipLaunchKernelGGL(gemm_nvfp4_kernel<0>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
+    const TailSplit ts = nvfp4_tail_split(blocks, (int)(a.K / 64), a.work);
+    const int grid = ts.parts > 0 ? ts.full + ts.tail * ts.parts : blocks;
+    hipLaunchKernelGGL(gemm_nvfp4_kernel<0>, dim3(grid), dim3(256), 0, st, (int)a.M, (int)a.N,
                        (int)a.K, a.rank, (const uint8_t*)a.act_codes, (const uint8_t*)a.act_scales,
                        a.alpha_a * a.alpha_w, (const uint8_t*)a.w_codes, (const uint8_t*)a.w_scales,
                        a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, none,
-                       mnone);
+                       mnone, ts);
   }
   return hipGetLastError();
 }

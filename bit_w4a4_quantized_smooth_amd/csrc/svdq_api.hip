@@ -263,7 +263,7 @@ svdq_status svdq_w4a4_gemm_ws(int precision, int group_size, int rank, int64_t M
     return fail(SVDQ_ERR_INVALID_ARG, "work_bytes=%lld given without work", (long long)work_bytes);
   }
   return gemm_y(precision, group_size, rank, M, N, K, act_codes, act_scales, act_global_scale, w_codes,
-                w_scales, w_global_scale, xl1, l2t, bias, y, stream, nullptr, 0, precision == SVDQ_INT4 ? work : nullptr);
+                w_scales, w_global_scale, xl1, l2t, bias, y, stream, nullptr, 0, work);
 }
 
 svdq_status svdq_w4a4_gemm_qkv_norm_rope(int precision, int group_size, int rank, int64_t M,

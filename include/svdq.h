@@ -123,10 +123,11 @@ svdq_status svdq_w4a4_gemm(int precision, int group_size, int rank, int64_t M, i
 
 /*
  * svdq_w4a4_gemm_ws -- svdq_w4a4_gemm with a caller-owned workspace: the same
- * product (blog, "Background: SVDQuant and Nunchaku"), where the int4 kernel
- * may run the tiles of its grid's last partial round as K slices spread over
- * the CUs.  The slices' fp32 partial accumulators meet in `work`, and the last
- * slice of a tile to finish adds them up in slice order and writes the tile.
+ * product (blog, "Background: SVDQuant and Nunchaku"), where the kernel may
+ * run the tiles of its grid's last partial round as K slices spread over the
+ * CUs (int4 and nvfp4; nvfp4 slices are whole 1024-channel blocks of K).
+ * The slices' fp32 partial accumulators meet in `work`, and the last slice of
+ * a tile to finish adds them up in slice order and writes the tile.
  * Those tiles' fp32 sums are then formed in another order than
  * svdq_w4a4_gemm's, so their Y can differ from it in the last bit (the same
  * bits from call to call).
@@ -137,8 +138,7 @@ svdq_status svdq_w4a4_gemm(int precision, int group_size, int rank, int64_t M, i
  *               its first use.  A call leaves its counter words zero again (the
  *               rest is scratch), so the same workspace serves every later
  *               call on the same stream; calls that may run at the same time
- *               (other streams) need workspaces of their own.  Ignored for
- *               nvfp4.
+ *               (other streams) need workspaces of their own.
  *   work_bytes  its size in bytes
  *   the other arguments, limits and errors as for svdq_w4a4_gemm
  */

@@ -1,18 +1,23 @@
-"""svdq_w4a4_gemm_ws: the int4 GEMM with its grid's last partial round of tiles
-run as K slices that meet in a caller-owned workspace.
+"""svdq_w4a4_gemm_ws: the 4-bit GEMM with its grid's last partial round of
+tiles run as K slices that meet in a caller-owned workspace.
 
-On the QKV projection (4608 x 9216 x 3072, rank 32; 2592 tiles, so 32 tiles
-are left for the last round on a 256-CU device), through the C ABI:
+On the QKV projection in int4 and in nvfp4 (4608 x 9216 x 3072, rank 32;
+2592 tiles, so 32 tiles are left for the last round on a 256-CU device),
+through the C ABI:
   * every output outside the split tiles is bit-identical to svdq_w4a4_gemm's;
+  * the split ran: the partial tiles were written into the (zero-filled)
+    workspace;
   * the split tiles match the oracle's double y (max-abs-rel <= 1e-2): two of
-    them in full, 256 seeded outputs of each of the others; and they do
-    differ from svdq_w4a4_gemm's somewhere (the split ran);
+    them in full, 256 seeded outputs of each of the others (in nvfp4 the
+    fp32 sums of these inputs are exact, multiples of 1/4 far below 2^24
+    quanta, so there they equal svdq_w4a4_gemm's bit for bit; in int4 the
+    constant offset of the integer-to-float step rounds, and some differ);
   * a second call gives the same bits, and every call leaves the counter
     words of the workspace zero;
   * a different activation through the same workspace is again right (no
     partial of the previous call is read);
-  * where no split applies (a grid without a small last round, nvfp4), the
-    result is svdq_w4a4_gemm's, bit for bit.
+  * where no split applies (a grid without a small last round), the result
+    is svdq_w4a4_gemm's, bit for bit, and the workspace is not written.
 The product is the blog's "Background: SVDQuant and Nunchaku" per-group
 scaled 4-bit GEMM with the low-rank branch and bias in the epilogue.
 """
@@ -45,13 +50,16 @@ def host(t):
     return t.view(torch.int16).numpy().view(np.uint16) if t.dtype in (torch.bfloat16, torch.float16) else t.numpy()
 
 
-def split_tiles(M, N, K, cus):
+def split_tiles(prec, M, N, K, cus):
     """(row0, col0) of the tiles the launcher runs as K slices: the grid's tiles
     left after whole rounds of two per CU, when they are at most an eighth of a
-    round, taken as the last tail/8 of each XCD's eighth of the banded tile order."""
+    round, taken as the last tail/8 of each XCD's eighth of the banded tile order
+    (int4: K of at least eight 128-channel stages; nvfp4: K a multiple of 1024
+    channels, at least two such blocks)."""
     mt, nt = (M + TILE - 1) // TILE, N // TILE
-    tiles, slots, stages = mt * nt, 2 * cus, (K // 64 + 1) // 2
-    if tiles % 8 or slots % 8 or tiles <= slots or stages < 8:
+    tiles, slots = mt * nt, 2 * cus
+    k_ok = (K // 64 + 1) // 2 >= 8 if prec == sq.SVDQ_INT4 else (K // 64) % 16 == 0 and K // 1024 >= 2
+    if tiles % 8 or slots % 8 or tiles <= slots or not k_ok:
         return []
     tail = tiles % slots
     if tail == 0 or tail > slots // 8 or tail > 64:
@@ -73,8 +81,9 @@ def max_abs_rel(y_bits, ref):
     return float(np.max(np.abs(y - ref)) / max(np.max(np.abs(ref)), 1e-30))
 
 
-def gemm(prec, g, codes, scales, ws=None):
-    return sq.w4a4_gemm(prec, codes, scales, g["wc"], g["ws"], g["xl1"], g["l2t"], g["bias"], workspace=ws)
+def gemm(d, g, codes, scales, ws=None):
+    return sq.w4a4_gemm(d["prec"], codes, scales, g["wc"], g["ws"], g["xl1"], g["l2t"], g["bias"], d["alpha_a"],
+                        d["alpha_w"], workspace=ws)
 
 
 def check_tiles(d, oc, os_, ox, y, tiles, full, seed):
@@ -86,18 +95,19 @@ def check_tiles(d, oc, os_, ox, y, tiles, full, seed):
             pick = rng.choice(rr.size, 256, replace=False)
             rr, cc = rr[pick], cc[pick]
         ref, _ = oracle.w4a4_linear(d["prec"], oc, os_, d["w_codes"], d["w_scales"], ox, d["l2t"], d["bias"],
-                                    rows=rr, cols=cc)
+                                    alpha_a=d["alpha_a"], alpha_w=d["alpha_w"], rows=rr, cols=cc)
         e = max_abs_rel(y[rr, cc], ref)
         assert e <= Y_TOL, f"tile ({m0}, {n0}): max-abs-rel {e:.2e}"
 
 
-@pytest.fixture(scope="module")
-def qkv():
-    name = "dit_qkv_int4_4608x9216x3072_r32"
+@pytest.fixture(scope="module", params=["dit_qkv_int4_4608x9216x3072_r32", "dit_qkv_nvfp4_4608x9216x3072_r32"])
+def qkv(request):
+    name = request.param
     print(f"[tail split] {name}: inputs", flush=True)
     d = synth.WORKLOADS[name]()
-    g = dict(x=b16(d["x"]), lam=b16(d["lam"]), l1t=b16(d["l1t"]), wc=dev(d["w_codes"]),
-             ws=b16(d["w_scales"], torch.float16), l2t=b16(d["l2t"]), bias=b16(d["bias"]))
+    ws = b16(d["w_scales"], torch.float16) if d["prec"] == sq.SVDQ_INT4 else dev(d["w_scales"])
+    g = dict(x=b16(d["x"]), lam=b16(d["lam"]), l1t=b16(d["l1t"]), wc=dev(d["w_codes"]), ws=ws,
+             l2t=b16(d["l2t"]), bias=b16(d["bias"]))
     yield d, g
     del g
     torch.cuda.empty_cache()
@@ -107,17 +117,19 @@ def test_split_tail_on_the_qkv_projection(qkv):
     d, g = qkv
     M, N, K = d["M"], d["N"], d["K"]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tiles = split_tiles(M, N, K, cus)
+    tiles = split_tiles(d["prec"], M, N, K, cus)
     print(f"[tail split] {cus} CUs: {len(tiles)} tiles split", flush=True)
     if not tiles:
         pytest.skip(f"no split on a {cus}-CU device for this grid")
-    codes, scales, xl1 = sq.quantize_act(d["prec"], g["x"], g["lam"], g["l1t"])
+    codes, scales, xl1 = sq.quantize_act(d["prec"], g["x"], g["lam"], g["l1t"], d["alpha_a"])
     g["xl1"] = xl1
     work = sq.gemm_workspace()
     print("[tail split] plain GEMM, then twice with the workspace", flush=True)
-    y_plain = gemm(d["prec"], g, codes, scales)
-    y_ws = gemm(d["prec"], g, codes, scales, work)
-    y_ws2 = gemm(d["prec"], g, codes, scales, work)
+    y_plain = gemm(d, g, codes, scales)
+    y_ws = gemm(d, g, codes, scales, work)
+    torch.cuda.synchronize()
+    assert int(work[:PART_BYTES].count_nonzero()) > 0, "no partial tile written: no split ran"
+    y_ws2 = gemm(d, g, codes, scales, work)
     torch.cuda.synchronize()
     assert torch.equal(y_ws.view(torch.int16), y_ws2.view(torch.int16)), "second call differs"
     assert int(work[PART_BYTES:].count_nonzero()) == 0, "counter words not left zero"
@@ -127,7 +139,6 @@ def test_split_tail_on_the_qkv_projection(qkv):
         in_split[m0:m0 + TILE, n0:n0 + TILE] = True
     differ = y_ws.view(torch.int16) != y_plain.view(torch.int16)
     assert not bool((differ & ~in_split).any()), "outputs outside the split tiles differ"
-    assert bool(differ.any()), "the split tiles equal the plain ones bit for bit: no split ran"
     print(f"[tail split] {int(differ.sum())} outputs of the split tiles differ from the plain GEMM's", flush=True)
 
     oc, os_ = host(codes), host(scales)
@@ -137,9 +148,9 @@ def test_split_tail_on_the_qkv_projection(qkv):
 
     # a different activation (rows rotated) through the same workspace
     x2 = np.ascontiguousarray(np.roll(d["x"], 37, axis=0))
-    codes2, scales2, xl12 = sq.quantize_act(d["prec"], b16(x2), g["lam"], g["l1t"])
+    codes2, scales2, xl12 = sq.quantize_act(d["prec"], b16(x2), g["lam"], g["l1t"], d["alpha_a"])
     g["xl1"] = xl12
-    y2 = gemm(d["prec"], g, codes2, scales2, work)
+    y2 = gemm(d, g, codes2, scales2, work)
     torch.cuda.synchronize()
     assert int(work[PART_BYTES:].count_nonzero()) == 0
     ox2 = oracle.lowrank_down(x2, d["l1t"])
@@ -147,8 +158,7 @@ def test_split_tail_on_the_qkv_projection(qkv):
     print("[tail split] second activation through the same workspace matches the oracle", flush=True)
 
 
-@pytest.mark.parametrize("name", ["svdq_int4_256x512x512_r16", "dit_mlp_up_int4_4608x12288x3072_r32",
-                                  "dit_qkv_nvfp4_4608x9216x3072_r32"])
+@pytest.mark.parametrize("name", ["svdq_int4_256x512x512_r16", "dit_mlp_up_int4_4608x12288x3072_r32"])
 def test_no_split_is_the_plain_gemm(name):
     d = synth.WORKLOADS[name]()
     print(f"[tail split] {name}: with and without the workspace", flush=True)
@@ -157,7 +167,9 @@ def test_no_split_is_the_plain_gemm(name):
     g = dict(wc=dev(d["w_codes"]), ws=sc(d["w_scales"]), l2t=b16(d["l2t"]), bias=b16(d["bias"]))
     codes, scales, g["xl1"] = sq.quantize_act(prec, b16(d["x"]), b16(d["lam"]), b16(d["l1t"]), d["alpha_a"])
     y0 = sq.w4a4_gemm(prec, codes, scales, g["wc"], g["ws"], g["xl1"], g["l2t"], g["bias"], d["alpha_a"], d["alpha_w"])
+    work = sq.gemm_workspace()
     y1 = sq.w4a4_gemm(prec, codes, scales, g["wc"], g["ws"], g["xl1"], g["l2t"], g["bias"], d["alpha_a"], d["alpha_w"],
-                      workspace=sq.gemm_workspace())
+                      workspace=work)
     torch.cuda.synchronize()
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert int(work.count_nonzero()) == 0
