@@ -4,8 +4,8 @@ AWQ W4A16 linears can be traced whole by torch.compile (fullgraph=True).
 The pages say the quantized linear layers work under torch.compile ("Nunchaku
 Lite", section "torch.compile"; blog "Nunchaku 4-bit inference in Diffusers",
 "Benchmarks").  Here each library entry point becomes one opaque operator
-(`svdq::quantize_act`, `svdq::w4a4_gemm`, `svdq::w4a4_gemm_qkv_norm_rope`,
-`svdq::w4a4_gemm_gelu_quant`, `svdq::awq_gemv`) with a fake
+(`svdq::quantize_act`, `svdq::w4a4_gemm`, `svdq::w4a4_gemm_ws`,
+`svdq::w4a4_gemm_qkv_norm_rope`, `svdq::w4a4_gemm_gelu_quant`, `svdq::awq_gemv`) with a fake
 (meta) implementation that only computes output shapes and dtypes, so the
 tracer never runs a kernel; the real implementation is the ctypes call into
 libsvdq.so on the tensors' current stream.  Nothing here computes: every
@@ -14,7 +14,10 @@ arithmetic step stays in the library's kernels.
 `SVDQLinear`, `SVDQMLP` and `AWQLinear` are nn.Modules holding the packed
 layer tensors (as buffers) whose forward uses these operators; `SVDQMLP` is
 the DiT MLP with the fused up-projection ("Nunchaku Lite", "Fused kernels":
-the GELU-MLP fusion), three operators per call.
+the GELU-MLP fusion), three operators per call.  An SVDQLinear whose
+`workspace` attribute holds a workspace from `gemm_workspace()` (one may serve
+every layer that runs on the same stream) calls `svdq::w4a4_gemm_ws`, which
+runs the GEMM grid's last partial round of tiles as K slices.
 """
 from __future__ import annotations
 
@@ -25,6 +28,7 @@ from torch import Tensor
 
 from . import (SVDQ_INT4, SVDQ_NVFP4, GROUP, awq_gemv, quantize_act, w4a4_gemm, w4a4_gemm_gelu_quant,
                w4a4_gemm_qkv_norm_rope)
+from . import gemm_workspace  # noqa: F401  (re-exported for module users)
 
 _SCALE_DTYPE = {SVDQ_INT4: torch.float16, SVDQ_NVFP4: torch.uint8}
 
@@ -63,6 +67,31 @@ def w4a4_gemm_op(act_codes: Tensor, act_scales: Tensor, w_codes: Tensor, w_scale
 @w4a4_gemm_op.register_fake
 def _(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, precision, act_global_scale, w_global_scale):
     return act_codes.new_empty((act_codes.shape[0], w_codes.shape[0]), dtype=torch.bfloat16)
+
+
+@torch.library.custom_op("svdq::w4a4_gemm_ws", mutates_args=("workspace",))
+def w4a4_gemm_ws_op(act_codes: Tensor, act_scales: Tensor, w_codes: Tensor, w_scales: Tensor,
+                    xl1: Optional[Tensor], l2t: Optional[Tensor], bias: Optional[Tensor], workspace: Tensor,
+                    precision: int, act_global_scale: float, w_global_scale: float) -> Tensor:
+    """svdq_w4a4_gemm_ws: Y bf16 [M, N]; `workspace` (u8 [GEMM_WORK_BYTES], zero-filled once)
+    receives the partial tiles of the split last round."""
+    if xl1 is not None and xl1.shape[1] == 0:
+        xl1 = None
+    return w4a4_gemm(precision, act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias,
+                     act_global_scale, w_global_scale, workspace=workspace)
+
+
+@w4a4_gemm_ws_op.register_fake
+def _(act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias, workspace, precision, act_global_scale,
+      w_global_scale):
+    return act_codes.new_empty((act_codes.shape[0], w_codes.shape[0]), dtype=torch.bfloat16)
+
+
+def _gemm(codes, scales, w_codes, w_scales, xl1, l2t, bias, precision, ags, wgs, workspace=None):
+    if workspace is None:
+        return torch.ops.svdq.w4a4_gemm(codes, scales, w_codes, w_scales, xl1, l2t, bias, precision, ags, wgs)
+    return torch.ops.svdq.w4a4_gemm_ws(codes, scales, w_codes, w_scales, xl1, l2t, bias, workspace, precision,
+                                       ags, wgs)
 
 
 @torch.library.custom_op("svdq::w4a4_gemm_qkv_norm_rope", mutates_args=())
@@ -126,13 +155,15 @@ def _(x, w_codes, w_scales, w_zeros, bias):
 
 def svdq_linear(x: Tensor, smooth: Optional[Tensor], l1t: Optional[Tensor], w_codes: Tensor, w_scales: Tensor,
                 l2t: Optional[Tensor], bias: Optional[Tensor], precision: int = SVDQ_INT4,
-                act_global_scale: float = 1.0, w_global_scale: float = 1.0) -> Tensor:
-    """The SVDQuant linear as two traceable operators; x may have any leading shape."""
+                act_global_scale: float = 1.0, w_global_scale: float = 1.0,
+                workspace: Optional[Tensor] = None) -> Tensor:
+    """The SVDQuant linear as two traceable operators; x may have any leading shape.  With a
+    `workspace` (gemm_workspace()) the GEMM is svdq::w4a4_gemm_ws."""
     lead = x.shape[:-1]
     x2 = x.reshape(-1, x.shape[-1])
     codes, scales, xl1 = torch.ops.svdq.quantize_act(x2, smooth, l1t, precision, act_global_scale)
-    y = torch.ops.svdq.w4a4_gemm(codes, scales, w_codes, w_scales, xl1, l2t, bias, precision,
-                                 act_global_scale, w_global_scale)
+    y = _gemm(codes, scales, w_codes, w_scales, xl1, l2t, bias, precision, act_global_scale, w_global_scale,
+              workspace)
     return y.reshape(*lead, w_codes.shape[0])
 
 
@@ -157,10 +188,13 @@ class SVDQLinear(torch.nn.Module):
         self.register_buffer("bias", torch.zeros(out_features, dtype=torch.bfloat16, **kw) if bias else None)
         self.act_global_scale = 1.0  # NVFP4: static, calibrated offline
         self.w_global_scale = 1.0
+        # optional GEMM workspace (gemm_workspace()), shared by the layers of one stream:
+        # an attribute, not a buffer, so that one 16 MiB workspace serves them all
+        self.workspace: Optional[Tensor] = None
 
     def forward(self, x: Tensor) -> Tensor:
         return svdq_linear(x, self.smooth, self.l1t, self.w_codes, self.w_scales, self.l2t, self.bias,
-                           self.precision, self.act_global_scale, self.w_global_scale)
+                           self.precision, self.act_global_scale, self.w_global_scale, self.workspace)
 
 
 class SVDQMLP(torch.nn.Module):
@@ -187,8 +221,8 @@ class SVDQMLP(torch.nn.Module):
         hc, hs, hx = torch.ops.svdq.w4a4_gemm_gelu_quant(codes, scales, up.w_codes, up.w_scales, xl1, up.l2t,
                                                          up.bias, down.smooth, down.l1t, p, up.act_global_scale,
                                                          up.w_global_scale, down.act_global_scale)
-        y = torch.ops.svdq.w4a4_gemm(hc, hs, down.w_codes, down.w_scales, hx, down.l2t, down.bias, p,
-                                     down.act_global_scale, down.w_global_scale)
+        y = _gemm(hc, hs, down.w_codes, down.w_scales, hx, down.l2t, down.bias, p, down.act_global_scale,
+                  down.w_global_scale, down.workspace)
         return y.reshape(*lead, down.out_features)
 
 

@@ -57,6 +57,9 @@ def test_opcheck(prec):
     m = _svdq_module(d)
     torch.library.opcheck(torch.ops.svdq.w4a4_gemm.default,
                           (codes, scales, m.w_codes, m.w_scales, xl1, m.l2t, m.bias, prec, d["alpha_a"], d["alpha_w"]))
+    torch.library.opcheck(torch.ops.svdq.w4a4_gemm_ws.default,
+                          (codes, scales, m.w_codes, m.w_scales, xl1, m.l2t, m.bias, sq.gemm_workspace(), prec,
+                           d["alpha_a"], d["alpha_w"]))
     qd = synth.qkv_layer(33, 96, 2, 128, 256, 16, prec)
     qc, qs, qx = torch.ops.svdq.quantize_act(_t(qd["x"], torch.bfloat16), _t(qd["lam"], torch.bfloat16),
                                              _t(qd["l1t"], torch.bfloat16), prec, qd["alpha_a"])
@@ -159,3 +162,34 @@ def test_mlp_op_and_module(prec):
     e = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
     print(f"[ops] SVDQMLP vs oracle on the fused outputs: max-abs-rel {e:.2e}", flush=True)
     assert e <= 1e-2
+
+
+@pytest.mark.parametrize("prec", [sq.SVDQ_INT4, sq.SVDQ_NVFP4])
+def test_module_with_workspace(prec):
+    # the QKV projection's size (4608 tokens, 3072 -> 9216, rank 32), where the
+    # GEMM grid's last round is split: the layer with a workspace against the
+    # same layer without (every output outside the 32 split tiles equal, the
+    # rest within the int4 conversion noise), and compiled against eager bit
+    # for bit, the workspace's counter words left zero
+    print(f"[ops] SVDQLinear with a workspace, prec {prec}", flush=True)
+    d = synth.svdq_layer(71, 4608, 9216, 3072, 32, prec, 0.005, 30.0)
+    m = _svdq_module(d)
+    x = _t(d["x"], torch.bfloat16).reshape(2, 2304, 3072)
+    y_plain = m(x)
+    m.workspace = ops.gemm_workspace()
+    y_ws = m(x)
+    torch.cuda.synchronize()
+    assert int(m.workspace[:16 << 20].count_nonzero()) > 0, "no partial tile written: no split ran"
+    assert int(m.workspace[16 << 20:].count_nonzero()) == 0
+    n_diff = int((y_ws.view(torch.int16) != y_plain.view(torch.int16)).sum())
+    assert n_diff <= 32 * 128 * 128
+    rel = float((y_ws.float() - y_plain.float()).abs().max() / y_plain.float().abs().max())
+    print(f"[ops] {n_diff} outputs differ from the layer without a workspace, max-abs-rel {rel:.1e}", flush=True)
+    assert rel <= 1e-2
+    torch._dynamo.reset()
+    compiled = torch.compile(m, fullgraph=True, backend="aot_eager")
+    for _ in range(2):
+        y_comp = compiled(x)
+        torch.cuda.synchronize()
+        assert torch.equal(y_comp.view(torch.int16), y_ws.view(torch.int16))
+    assert int(m.workspace[16 << 20:].count_nonzero()) == 0

@@ -110,3 +110,24 @@ def test_export_mlp_full_graph(prec):
     assert targets.count(torch.ops.svdq.w4a4_gemm.default) == 1
     out = [n for n in ep.graph.nodes if n.op == "output"][0].args[0][0].meta["val"]
     assert out.shape == (2, 48, 256) and out.dtype == torch.bfloat16
+
+
+def test_fake_gemm_ws():
+    with FakeTensorMode():
+        codes = torch.empty(96, 256, dtype=torch.uint8)
+        scales = torch.empty(96, 8, dtype=torch.float16)
+        work = torch.empty(sq.GEMM_WORK_BYTES, dtype=torch.uint8)
+        y = torch.ops.svdq.w4a4_gemm_ws(codes, scales, torch.empty(384, 256, dtype=torch.uint8),
+                                        torch.empty(384, 8, dtype=torch.float16), None, None, None, work,
+                                        sq.SVDQ_INT4, 1.0, 1.0)
+        assert (y.shape, y.dtype) == ((96, 384), torch.bfloat16)
+
+
+def test_export_with_workspace():
+    # a layer given a workspace traces to quantize_act + w4a4_gemm_ws, the
+    # workspace a constant tensor of the graph
+    m = ops.SVDQLinear(256, 384, rank=16)
+    m.workspace = torch.zeros(sq.GEMM_WORK_BYTES, dtype=torch.uint8)
+    ep = torch.export.export(m, (torch.zeros(2, 48, 256, dtype=torch.bfloat16),), strict=True)
+    svdq_ops = [str(n.target) for n in ep.graph.nodes if n.op == "call_function" and "svdq" in str(n.target)]
+    assert svdq_ops == ["svdq.quantize_act.default", "svdq.w4a4_gemm_ws.default"]
