@@ -173,3 +173,40 @@ def test_no_split_is_the_plain_gemm(name):
     torch.cuda.synchronize()
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
     assert int(work.count_nonzero()) == 0
+
+
+# Grids at the edges of the split: the smallest last round (8 tiles: 65 x 8
+# tiles of 128 x 128) and the largest (64 tiles: 72 x 8), and the shortest K
+# that is split (int4: eight 128-channel stages; nvfp4: two 1024-channel
+# blocks).  Seeded synthetic layers of the same recipe as the workloads.
+EDGES = [(sq.SVDQ_INT4, 8320, 1024, 1024), (sq.SVDQ_INT4, 9216, 1024, 2048),
+         (sq.SVDQ_NVFP4, 8320, 1024, 2048), (sq.SVDQ_NVFP4, 9216, 1024, 2048)]
+
+
+@pytest.mark.parametrize("prec,M,N,K", EDGES)
+def test_split_tail_edges(prec, M, N, K):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = split_tiles(prec, M, N, K, cus)
+    print(f"[tail split] edge prec {prec} {M}x{N}x{K}: {len(tiles)} tiles split", flush=True)
+    if not tiles:
+        pytest.skip(f"no split on a {cus}-CU device for this grid")
+    d = synth.svdq_layer(81 + M % 7 + K % 5, M, N, K, 16, prec, 0.005, 30.0)
+    sc = (lambda s: b16(s, torch.float16)) if prec == sq.SVDQ_INT4 else dev
+    g = dict(wc=dev(d["w_codes"]), ws=sc(d["w_scales"]), l2t=b16(d["l2t"]), bias=b16(d["bias"]))
+    codes, scales, g["xl1"] = sq.quantize_act(prec, b16(d["x"]), b16(d["lam"]), b16(d["l1t"]), d["alpha_a"])
+    work = sq.gemm_workspace()
+    y_plain = gemm(d, g, codes, scales)
+    y_ws = gemm(d, g, codes, scales, work)
+    torch.cuda.synchronize()
+    assert int(work[:PART_BYTES].count_nonzero()) > 0, "no partial tile written: no split ran"
+    assert int(work[PART_BYTES:].count_nonzero()) == 0
+    y_ws2 = gemm(d, g, codes, scales, work)
+    torch.cuda.synchronize()
+    assert torch.equal(y_ws.view(torch.int16), y_ws2.view(torch.int16))
+    in_split = torch.zeros((M, N), dtype=torch.bool, device="cuda")
+    for m0, n0 in tiles:
+        in_split[m0:m0 + TILE, n0:n0 + TILE] = True
+    differ = y_ws.view(torch.int16) != y_plain.view(torch.int16)
+    assert not bool((differ & ~in_split).any()), "outputs outside the split tiles differ"
+    xl1 = oracle.lowrank_down(d["x"], d["l1t"])
+    check_tiles(d, host(codes), host(scales), xl1, host(y_ws), tiles, 1, 9)
