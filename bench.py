@@ -340,7 +340,7 @@ def extras(args, torch, sq, synth, t, bf, f16, stream):
 
     # fused attention projection (QKV GEMM + per-head RMSNorm + rotary epilogue)
     # against the same GEMM followed by the norm and rotary steps as separate
-    # torch kernels on the bf16 output
+    # torch kernels on the bf16 output (both GEMMs with the workspace)
     for name, seed, prec in (("qkv_fused_int4_4608x9216x3072_h24d128", 1002, sq.SVDQ_INT4),
                              ("qkv_fused_nvfp4_4608x9216x3072_h24d128", 1004, sq.SVDQ_NVFP4)):
         M, H, D, K = 4608, 24, 128, 3072
@@ -356,10 +356,10 @@ def extras(args, torch, sq, synth, t, bf, f16, stream):
         codes, scales, xl1 = sq.quantize_act(prec, x, lam, l1t, aa, stream=stream)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         fused_ms = median_ms(lambda i: sq.w4a4_gemm_qkv_norm_rope(
-            prec, codes, scales, wc, ws, xl1, l2t, bias, H, D, nq, nk, eps, rope, aa, aw, out=y, stream=stream),
-            n, stream, torch)
+            prec, codes, scales, wc, ws, xl1, l2t, bias, H, D, nq, nk, eps, rope, aa, aw, out=y, stream=stream,
+            workspace=work), n, stream, torch)
         plain_ms = median_ms(lambda i: sq.w4a4_gemm(prec, codes, scales, wc, ws, xl1, l2t, bias, aa, aw, out=y,
-                                                    stream=stream), n, stream, torch)
+                                                    stream=stream, workspace=work), n, stream, torch)
         cos, sin = rope[:, :, 0].unsqueeze(1), rope[:, :, 1].unsqueeze(1)
 
         def norm_rope(part, w):
@@ -370,7 +370,7 @@ def extras(args, torch, sq, synth, t, bf, f16, stream):
                 torch.bfloat16)
 
         def unfused(i):
-            sq.w4a4_gemm(prec, codes, scales, wc, ws, xl1, l2t, bias, aa, aw, out=y, stream=stream)
+            sq.w4a4_gemm(prec, codes, scales, wc, ws, xl1, l2t, bias, aa, aw, out=y, stream=stream, workspace=work)
             norm_rope(0, nq)
             norm_rope(1, nk)
 

@@ -33,7 +33,8 @@ _STATUS = {0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARG", 2: "SVDQ_ERR_UNSUPPORTED",
 # SVDQ_GEMM_WORK_BYTES: size of svdq_w4a4_gemm_ws's workspace
 GEMM_WORK_BYTES = 16 * 1024 * 1024 + 4096
 
-EXPORTS = ["svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_ws", "svdq_w4a4_gemm_qkv_norm_rope", "svdq_w4a4_gemm_gelu_quant",
+EXPORTS = ["svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_ws", "svdq_w4a4_gemm_qkv_norm_rope",
+           "svdq_w4a4_gemm_qkv_norm_rope_ws", "svdq_w4a4_gemm_gelu_quant",
            "awq_w4a16_gemv", "svdq_calibrate_smooth", "svdq_lowrank_workspace_bytes", "svdq_lowrank_decompose",
            "svdq_lowrank_decompose_noalloc",
            "svdq_quantize_weight", "awq_quantize_weight",
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
                                         vp, vp, vp, i64, vp]
         L.svdq_w4a4_gemm_qkv_norm_rope.argtypes = [i32, i32, i32, i64, i32, i32, i64, vp, vp, f32, vp, vp,
                                                    f32, vp, vp, vp, vp, vp, f32, vp, i64, vp, vp]
+        L.svdq_w4a4_gemm_qkv_norm_rope_ws.argtypes = [i32, i32, i32, i64, i32, i32, i64, vp, vp, f32, vp, vp,
+                                                      f32, vp, vp, vp, vp, vp, f32, vp, i64, vp, vp, i64, vp]
         L.svdq_w4a4_gemm_gelu_quant.argtypes = [i32, i32, i32, i64, i64, i64, vp, vp, f32, vp, vp, f32, vp, vp,
                                                 vp, vp, vp, i32, f32, vp, vp, vp, vp]
         L.awq_w4a16_gemv.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
@@ -78,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.awq_quantize_weight.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
         L.svdq_w4a4_group_psums.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp]
         for f in ("svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_ws", "svdq_w4a4_gemm_qkv_norm_rope",
+                  "svdq_w4a4_gemm_qkv_norm_rope_ws",
                   "svdq_w4a4_gemm_gelu_quant", "awq_w4a16_gemv", "svdq_w4a4_group_psums", "svdq_calibrate_smooth",
                   "svdq_lowrank_decompose", "svdq_lowrank_decompose_noalloc", "svdq_quantize_weight",
                   "awq_quantize_weight"):
@@ -222,8 +226,9 @@ def w4a4_gemm(precision: int, act_codes, act_scales, w_codes, w_scales, xl1=None
 def w4a4_gemm_qkv_norm_rope(precision: int, act_codes, act_scales, w_codes, w_scales, xl1, l2t, bias,
                             heads: int, head_dim: int, norm_q, norm_k, eps: float, rope=None,
                             act_global_scale: float = 1.0, w_global_scale: float = 1.0, out=None,
-                            stream=None):
-    """svdq_w4a4_gemm_qkv_norm_rope: the fused attention projection.  w_codes holds the Q, K
+                            stream=None, workspace=None):
+    """svdq_w4a4_gemm_qkv_norm_rope (svdq_w4a4_gemm_qkv_norm_rope_ws when `workspace`, see
+    gemm_workspace, is given): the fused attention projection.  w_codes holds the Q, K
     and V weights concatenated along N (= 3 * heads * head_dim); rope is fp32
     [S, head_dim/2, 2] (cos, sin) or None.  Returns Y bf16 [M, N]."""
     fn = "w4a4_gemm_qkv_norm_rope"
@@ -232,11 +237,15 @@ def w4a4_gemm_qkv_norm_rope(precision: int, act_codes, act_scales, w_codes, w_sc
     rope_rows = 0 if rope is None else _dims(fn, rope, "rope", 3)[0]
     y = out if out is not None else torch.empty((M, N), dtype=_BF16, device=act_codes.device)
     (a.req("norm_q", norm_q, _BF16, (head_dim,)).req("norm_k", norm_k, _BF16, (head_dim,))
-     .req("rope", rope, _F32, (rope_rows, head_dim // 2, 2), True).req("y", y, _BF16, (M, N)).done())
-    _check(lib().svdq_w4a4_gemm_qkv_norm_rope(
-        precision, G, r, M, heads, head_dim, K, _ptr(act_codes), _ptr(act_scales), float(act_global_scale),
-        _ptr(w_codes), _ptr(w_scales), float(w_global_scale), _ptr(xl1), _ptr(l2t), _ptr(bias), _ptr(norm_q),
-        _ptr(norm_k), float(eps), _ptr(rope), rope_rows, _ptr(y), _stream(stream)))
+     .req("rope", rope, _F32, (rope_rows, head_dim // 2, 2), True).req("y", y, _BF16, (M, N))
+     .req("workspace", workspace, _U8, (GEMM_WORK_BYTES,), True).done())
+    args = (precision, G, r, M, heads, head_dim, K, _ptr(act_codes), _ptr(act_scales), float(act_global_scale),
+            _ptr(w_codes), _ptr(w_scales), float(w_global_scale), _ptr(xl1), _ptr(l2t), _ptr(bias), _ptr(norm_q),
+            _ptr(norm_k), float(eps), _ptr(rope), rope_rows, _ptr(y))
+    if workspace is None:
+        _check(lib().svdq_w4a4_gemm_qkv_norm_rope(*args, _stream(stream)))
+    else:
+        _check(lib().svdq_w4a4_gemm_qkv_norm_rope_ws(*args, _ptr(workspace), GEMM_WORK_BYTES, _stream(stream)))
     return y
 
 

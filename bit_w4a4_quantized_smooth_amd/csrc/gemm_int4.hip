@@ -138,7 +138,7 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
   // the launcher): its tile is one of the last tail/8 of its XCD's range, so
   // every slice of a tile runs on the same XCD as the tile's neighbours.
   int slice = -1, tail_idx = 0;
-  constexpr bool kTailSplit = MODE == 0 && SPLIT == 1;
+  constexpr bool kTailSplit = (MODE == 0 || MODE == 2) && SPLIT == 1;  // the Y-producing GEMMs
   if ((tiles & 7) == 0) t = split_tile_of(t, tiles, kTailSplit ? ts : TailSplit{}, slice, tail_idx);
   constexpr int kBandM = 12;
   const int band = t / (kBandM * n_tiles), in_band = t - band * (kBandM * n_tiles);
@@ -836,10 +836,12 @@ hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st) {
                        (const uint8_t*)a.act_codes, nullptr, (const uint8_t*)a.w_codes, nullptr, nullptr,
                        nullptr, nullptr, nullptr, (int32_t*)a.psums, qnone, mnone, tnone);
   } else if (a.qkv) {
-    hipLaunchKernelGGL(k2, dim3(blocks), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
+    const TailSplit ts = tail_split(blocks, (int)(a.K / 64), a.work);
+    const int grid = ts.parts > 0 ? ts.full + ts.tail * ts.parts : blocks;
+    hipLaunchKernelGGL(k2, dim3(grid), dim3(NT), LDS_BYTES, st, (int)a.M, (int)a.N, (int)a.K, a.rank,
                        (const uint8_t*)a.act_codes, (const uint16_t*)a.act_scales,
                        (const uint8_t*)a.w_codes, (const uint16_t*)a.w_scales, a.xl1,
-                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, *a.qkv, mnone, tnone);
+                       (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr, *a.qkv, mnone, ts);
   } else if (a.mlp) {
     const int nx = (int)(a.M * a.mlp->rank);
     if (nx > 0) hipLaunchKernelGGL(fill_zero_f32, dim3((nx + 255) / 256), dim3(256), 0, st, a.mlp->xl1, nx);

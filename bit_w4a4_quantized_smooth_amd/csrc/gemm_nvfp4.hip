@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   // the plain GEMM may run its grid's last partial round as K slices
   // (tail_split.h): slices are whole 16-step scale blocks of K
   int t = blockIdx.x, slice = -1, tail_idx = 0;
-  if ((tiles & 7) == 0) t = split_tile_of(t, tiles, MODE == 0 ? ts : TailSplit{}, slice, tail_idx);
+  if ((tiles & 7) == 0) t = split_tile_of(t, tiles, MODE == 0 || MODE == 2 ? ts : TailSplit{}, slice, tail_idx);
   constexpr int kBandM = 12;
   const int band = t / (kBandM * n_tiles), in_band = t - band * (kBandM * n_tiles);
   const int band_m0 = band * kBandM;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
   int steps = K >> 6, st0 = 0;  // this workgroup's steps: [st0, st0 + steps)
   const int G = K >> 4;
   const int rowb = K >> 1;
-  if (MODE == 0 && slice >= 0) {
+  if ((MODE == 0 || MODE == 2) && slice >= 0) {
     const int nb = steps >> 4;
     st0 = 16 * (slice * nb / ts.parts);
     steps = 16 * ((slice + 1) * nb / ts.parts) - st0;
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(
                std::make_integer_sequence<int, 15>{});
   }
 
-  if constexpr (MODE == 0) {
+  if constexpr (MODE == 0 || MODE == 2) {
     // a K slice: partials through the workspace; the tile's last slice
     // continues with the sum of all of them (4-float vector k of this lane:
     // acc[k / 8][(k / 4) % 2], elements 4 (k % 4) .. +3)
@@ -616,11 +616,13 @@ hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st) {
                        (const uint8_t*)a.w_codes, nullptr, nullptr, nullptr, nullptr, nullptr,
                        (float*)a.psums, none, mnone, tnone);
   } else if (a.qkv) {
-    hipLaunchKernelGGL(gemm_nvfp4_kernel<2>, dim3(blocks), dim3(256), 0, st, (int)a.M, (int)a.N,
+    const TailSplit ts = nvfp4_tail_split(blocks, (int)(a.K / 64), a.work);
+    const int grid = ts.parts > 0 ? ts.full + ts.tail * ts.parts : blocks;
+    hipLaunchKernelGGL(gemm_nvfp4_kernel<2>, dim3(grid), dim3(256), 0, st, (int)a.M, (int)a.N,
                        (int)a.K, a.rank, (const uint8_t*)a.act_codes, (const uint8_t*)a.act_scales,
                        a.alpha_a * a.alpha_w, (const uint8_t*)a.w_codes, (const uint8_t*)a.w_scales,
                        a.xl1, (const uint16_t*)a.l2t, (const uint16_t*)a.bias, (uint16_t*)a.y, nullptr,
-                       *a.qkv, mnone, tnone);
+                       *a.qkv, mnone, ts);
   } else if (a.mlp) {
     const int nx = (int)(a.M * a.mlp->rank);
     if (nx > 0) hipLaunchKernelGGL(fill_zero_f32, dim3((nx + 255) / 256), dim3(256), 0, st, a.mlp->xl1, nx);

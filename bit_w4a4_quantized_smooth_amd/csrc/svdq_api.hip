@@ -240,11 +240,12 @@ svdq_status svdq_w4a4_gemm(int precision, int group_size, int rank, int64_t M, i
 
 static_assert(SVDQ_GEMM_WORK_BYTES == svdq::kGemmWorkBytes, "workspace size of the header and the kernels");
 
-svdq_status svdq_w4a4_gemm_ws(int precision, int group_size, int rank, int64_t M, int64_t N,
-                              int64_t K, const void* act_codes, const void* act_scales,
-                              float act_global_scale, const void* w_codes, const void* w_scales,
-                              float w_global_scale, const float* xl1, const void* l2t,
-                              const void* bias, void* y, void* work, int64_t work_bytes, void* stream) {
+// The workspace of the split last round: NULL with work_bytes 0, or at least
+// SVDQ_GEMM_WORK_BYTES, 16-byte aligned, overlapping no other buffer of the call.
+static svdq_status check_work(void* work, int64_t work_bytes, int precision, int rank, int64_t M, int64_t N,
+                              int64_t K, const void* act_codes, const void* act_scales, const void* w_codes,
+                              const void* w_scales, const float* xl1, const void* l2t, const void* bias,
+                              const void* y) {
   if (work) {
     if (work_bytes < (int64_t)SVDQ_GEMM_WORK_BYTES)
       return fail(SVDQ_ERR_INVALID_ARG, "work_bytes=%lld below SVDQ_GEMM_WORK_BYTES=%lld", (long long)work_bytes,
@@ -262,18 +263,28 @@ svdq_status svdq_w4a4_gemm_ws(int precision, int group_size, int rank, int64_t M
   } else if (work_bytes != 0) {
     return fail(SVDQ_ERR_INVALID_ARG, "work_bytes=%lld given without work", (long long)work_bytes);
   }
+  return SVDQ_OK;
+}
+
+svdq_status svdq_w4a4_gemm_ws(int precision, int group_size, int rank, int64_t M, int64_t N,
+                              int64_t K, const void* act_codes, const void* act_scales,
+                              float act_global_scale, const void* w_codes, const void* w_scales,
+                              float w_global_scale, const float* xl1, const void* l2t,
+                              const void* bias, void* y, void* work, int64_t work_bytes, void* stream) {
+  svdq_status s;
+  if ((s = check_work(work, work_bytes, precision, rank, M, N, K, act_codes, act_scales, w_codes, w_scales, xl1,
+                      l2t, bias, y)) != SVDQ_OK)
+    return s;
   return gemm_y(precision, group_size, rank, M, N, K, act_codes, act_scales, act_global_scale, w_codes,
                 w_scales, w_global_scale, xl1, l2t, bias, y, stream, nullptr, 0, work);
 }
 
-svdq_status svdq_w4a4_gemm_qkv_norm_rope(int precision, int group_size, int rank, int64_t M,
-                                         int heads, int head_dim, int64_t K, const void* act_codes,
-                                         const void* act_scales, float act_global_scale,
-                                         const void* w_codes, const void* w_scales,
-                                         float w_global_scale, const float* xl1, const void* l2t,
-                                         const void* bias, const void* norm_q, const void* norm_k,
-                                         float eps, const float* rope, int64_t rope_rows, void* y,
-                                         void* stream) {
+static svdq_status qkv_common(int precision, int group_size, int rank, int64_t M, int heads, int head_dim,
+                              int64_t K, const void* act_codes, const void* act_scales, float act_global_scale,
+                              const void* w_codes, const void* w_scales, float w_global_scale, const float* xl1,
+                              const void* l2t, const void* bias, const void* norm_q, const void* norm_k, float eps,
+                              const float* rope, int64_t rope_rows, void* y, void* work, int64_t work_bytes,
+                              void* stream) {
   if (head_dim != 64 && head_dim != 128)
     return fail(SVDQ_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
   if (heads <= 0 || heads > (1 << 20)) return fail(SVDQ_ERR_INVALID_ARG, "bad head count %d", heads);
@@ -287,8 +298,42 @@ svdq_status svdq_w4a4_gemm_qkv_norm_rope(int precision, int group_size, int rank
   const svdq::QkvEpi q{(int)(heads * head_dim), head_dim, (const uint16_t*)norm_q, (const uint16_t*)norm_k,
                        eps, rope, rope ? (int)rope_rows : 1};
   const size_t rope_bytes = rope ? (size_t)rope_rows * head_dim * 4 : 0;
+  svdq_status s;
+  if ((s = check_work(work, work_bytes, precision, rank, M, N, K, act_codes, act_scales, w_codes, w_scales, xl1,
+                      l2t, bias, y)) != SVDQ_OK)
+    return s;
+  if (work && (overlaps(work, SVDQ_GEMM_WORK_BYTES, norm_q, (size_t)head_dim * 2) ||
+               overlaps(work, SVDQ_GEMM_WORK_BYTES, norm_k, (size_t)head_dim * 2) ||
+               overlaps(work, SVDQ_GEMM_WORK_BYTES, rope, rope_bytes)))
+    return fail(SVDQ_ERR_INVALID_ARG, "work must not overlap y or an input");
   return gemm_y(precision, group_size, rank, M, N, K, act_codes, act_scales, act_global_scale, w_codes,
-                w_scales, w_global_scale, xl1, l2t, bias, y, stream, &q, rope_bytes);
+                w_scales, w_global_scale, xl1, l2t, bias, y, stream, &q, rope_bytes, work);
+}
+
+svdq_status svdq_w4a4_gemm_qkv_norm_rope(int precision, int group_size, int rank, int64_t M,
+                                         int heads, int head_dim, int64_t K, const void* act_codes,
+                                         const void* act_scales, float act_global_scale,
+                                         const void* w_codes, const void* w_scales,
+                                         float w_global_scale, const float* xl1, const void* l2t,
+                                         const void* bias, const void* norm_q, const void* norm_k,
+                                         float eps, const float* rope, int64_t rope_rows, void* y,
+                                         void* stream) {
+  return qkv_common(precision, group_size, rank, M, heads, head_dim, K, act_codes, act_scales, act_global_scale,
+                    w_codes, w_scales, w_global_scale, xl1, l2t, bias, norm_q, norm_k, eps, rope, rope_rows, y,
+                    nullptr, 0, stream);
+}
+
+svdq_status svdq_w4a4_gemm_qkv_norm_rope_ws(int precision, int group_size, int rank, int64_t M,
+                                            int heads, int head_dim, int64_t K, const void* act_codes,
+                                            const void* act_scales, float act_global_scale,
+                                            const void* w_codes, const void* w_scales,
+                                            float w_global_scale, const float* xl1, const void* l2t,
+                                            const void* bias, const void* norm_q, const void* norm_k,
+                                            float eps, const float* rope, int64_t rope_rows, void* y,
+                                            void* work, int64_t work_bytes, void* stream) {
+  return qkv_common(precision, group_size, rank, M, heads, head_dim, K, act_codes, act_scales, act_global_scale,
+                    w_codes, w_scales, w_global_scale, xl1, l2t, bias, norm_q, norm_k, eps, rope, rope_rows, y,
+                    work, work_bytes, stream);
 }
 
 svdq_status svdq_w4a4_gemm_gelu_quant(int precision, int group_size, int rank, int64_t M, int64_t N,

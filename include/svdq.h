@@ -186,6 +186,22 @@ svdq_status svdq_w4a4_gemm_qkv_norm_rope(int precision, int group_size, int rank
                                          void* stream);
 
 /*
+ * svdq_w4a4_gemm_qkv_norm_rope_ws -- svdq_w4a4_gemm_qkv_norm_rope with the
+ * workspace of svdq_w4a4_gemm_ws: the grid's last partial round of tiles may
+ * run as K slices, and the last slice of a tile runs the norm and rotary
+ * epilogue on the summed tile.  work, work_bytes as for svdq_w4a4_gemm_ws;
+ * everything else as for svdq_w4a4_gemm_qkv_norm_rope.
+ */
+svdq_status svdq_w4a4_gemm_qkv_norm_rope_ws(int precision, int group_size, int rank, int64_t M,
+                                            int heads, int head_dim, int64_t K, const void* act_codes,
+                                            const void* act_scales, float act_global_scale,
+                                            const void* w_codes, const void* w_scales,
+                                            float w_global_scale, const float* xl1, const void* l2t,
+                                            const void* bias, const void* norm_q, const void* norm_k,
+                                            float eps, const float* rope, int64_t rope_rows, void* y,
+                                            void* work, int64_t work_bytes, void* stream);
+
+/*
  * svdq_w4a4_gemm_gelu_quant -- the fused MLP up-projection: the W4A4 GEMM of
  * the up projection, GELU, and the down projection's activation quantization
  * and low-rank input, all in the GEMM's epilogue, so the [M, N] hidden

@@ -287,3 +287,16 @@ def test_gemm_workspace_validation(L):
     assert gemm_ws(L, y=None) == INVALID                          # the plain GEMM's own checks still apply
     L.svdq_test_set_arch_override(b"gfx950")
     assert gemm_ws(L, M=0) == OK
+
+
+def test_qkv_workspace_validation(L):
+    def qkv_ws(work=64 * A, work_bytes=sq.GEMM_WORK_BYTES, y=8 * A):
+        return L.svdq_w4a4_gemm_qkv_norm_rope_ws(0, 64, 16, 256, 2, 128, 512, A, 2 * A, 1.0, 3 * A, 4 * A, 1.0,
+                                                 5 * A, 6 * A, 7 * A, 9 * A, 10 * A, 1e-6, 11 * A, 256, y,
+                                                 work, work_bytes, None)
+    assert qkv_ws() == UNSUPPORTED                                # valid: reaches the arch check
+    assert qkv_ws(work=None, work_bytes=0) == UNSUPPORTED
+    assert qkv_ws(work_bytes=4096) == INVALID
+    assert qkv_ws(work=64 * A + 4) == ALIGN
+    assert qkv_ws(work=10 * A - 4096) == INVALID                  # overlaps norm_k
+    assert qkv_ws(work=8 * A - 4096) == INVALID                   # overlaps y

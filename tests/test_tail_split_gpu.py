@@ -210,3 +210,47 @@ def test_split_tail_edges(prec, M, N, K):
     assert not bool((differ & ~in_split).any()), "outputs outside the split tiles differ"
     xl1 = oracle.lowrank_down(d["x"], d["l1t"])
     check_tiles(d, host(codes), host(scales), xl1, host(y_ws), tiles, 1, 9)
+
+
+@pytest.mark.parametrize("prec", [sq.SVDQ_INT4, sq.SVDQ_NVFP4])
+def test_split_tail_fused_attention_projection(prec):
+    # svdq_w4a4_gemm_qkv_norm_rope_ws on the 24-head x 128 QKV projection of the
+    # same size: the last slice of a split tile runs the per-head RMSNorm and
+    # rotary epilogue on the summed tile.  Outside the split tiles the output
+    # equals svdq_w4a4_gemm_qkv_norm_rope's bit for bit; whole token rows through
+    # the split tiles (the first row of each, every column, so every head whole)
+    # match the oracle's projection per Q, K and V block within 1e-2.
+    print(f"[tail split] fused attention projection prec {prec}", flush=True)
+    d = synth.qkv_layer(1002 if prec == sq.SVDQ_INT4 else 1004, 4608, 24, 128, 3072, 32, prec, 0.005, 30.0)
+    M, N, K, HD = 4608, 9216, 3072, 24 * 128
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = split_tiles(prec, M, N, K, cus)
+    if not tiles:
+        pytest.skip(f"no split on a {cus}-CU device for this grid")
+    sc = (lambda s: b16(s, torch.float16)) if prec == sq.SVDQ_INT4 else dev
+    codes, scales, xl1 = sq.quantize_act(prec, b16(d["x"]), b16(d["lam"]), b16(d["l1t"]), d["alpha_a"])
+    args = (prec, codes, scales, dev(d["w_codes"]), sc(d["w_scales"]), xl1, b16(d["l2t"]), b16(d["bias"]), 24, 128,
+            b16(d["norm_q"]), b16(d["norm_k"]), d["eps"], dev(d["rope"]), d["alpha_a"], d["alpha_w"])
+    work = sq.gemm_workspace()
+    y_plain = sq.w4a4_gemm_qkv_norm_rope(*args)
+    y_ws = sq.w4a4_gemm_qkv_norm_rope(*args, workspace=work)
+    torch.cuda.synchronize()
+    assert int(work[:PART_BYTES].count_nonzero()) > 0, "no partial tile written: no split ran"
+    assert int(work[PART_BYTES:].count_nonzero()) == 0
+    in_split = torch.zeros((M, N), dtype=torch.bool, device="cuda")
+    for m0, n0 in tiles:
+        in_split[m0:m0 + TILE, n0:n0 + TILE] = True
+    differ = y_ws.view(torch.int16) != y_plain.view(torch.int16)
+    assert not bool((differ & ~in_split).any()), "outputs outside the split tiles differ"
+    rows = np.unique([m0 for m0, _ in tiles])
+    oc, os_ = host(codes), host(scales)
+    ox = oracle.lowrank_down(d["x"], d["l1t"])
+    ref, _ = oracle.w4a4_linear_qkv(prec, oc, os_, d["w_codes"], d["w_scales"], ox, d["l2t"], d["bias"], 24, 128,
+                                    d["norm_q"], d["norm_k"], d["eps"], d["rope"], d["alpha_a"], d["alpha_w"],
+                                    rows=rows)
+    got = synth.bf16_bits_to_f64(host(y_ws)[rows])
+    for b, name in enumerate("QKV"):
+        g, r = got[:, b * HD:(b + 1) * HD], ref[:, b * HD:(b + 1) * HD]
+        err = np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-30)
+        print(f"[tail split] fused {name} block on {rows.size} rows through the split tiles: {err:.2e}", flush=True)
+        assert err <= Y_TOL, f"{name} block: max-abs-rel {err:.3g}"
