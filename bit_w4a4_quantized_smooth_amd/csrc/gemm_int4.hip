@@ -519,10 +519,19 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
     if (G > 32) load_ts(32, 1);
     if (rank > 0) load_lr(0);
 
-    // sum_g S = Sw . Sa^T on the matrix core (v_mfma_f32_16x16x32_f16, K = 32
-    // groups per instruction), then y = 2^18 * (acc - c0 * sum_g S)
+    // y = 2^18 (acc - c0 sum_g S), formed as (acc (-1/c0) + sum_g S) (-c0 2^18):
+    // the matrix core adds sum_g S = Sw . Sa^T (v_mfma_f32_16x16x32_f16, K = 32
+    // groups per instruction, exact fp16 products) into the accumulators
+    // themselves, so no vector instruction per group of 32 remains.  The one
+    // extra rounding, of acc (-1/c0), is 2^-24 of the offset c0 sum_g S.
     const float c0 = __int_as_float(kMagicBits);
-    const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+    const float neg_inv_c0 = -1.0f / c0;
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+#pragma unroll
+      for (int j = 0; j < BJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][v] *= neg_inv_c0;
     for (int kb = 0; kb < G; kb += 64) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -530,11 +539,8 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
 #pragma unroll
         for (int i = 0; i < BI; ++i)
 #pragma unroll
-          for (int j = 0; j < BJ; ++j) {
-            const v4f T = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[h][i], bx[h][j], zero4, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(-c0, T[v], acc[i][j][v]);
-          }
+          for (int j = 0; j < BJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[h][i], bx[h][j], acc[i][j], 0, 0, 0);
       }
       if (kb + 64 < G) load_ts(kb + 64, 0);
       if (kb + 96 < G) load_ts(kb + 96, 1);
@@ -549,12 +555,13 @@ __global__ __launch_bounds__(NT * SPLIT, 1) void gemm_int4_kernel(
           cs[i][j] = qe.rope ? *(const float4*)(qe.rope + (size_t)row[j] * qe.head_dim + qc0 + 16 * i + 4 * lg)
                              : float4{1.0f, 0.0f, 1.0f, 0.0f};
     }
+    const float out_scale = -c0 * kMagicScale;  // exact: c0 times a power of two
 #pragma unroll
     for (int i = 0; i < BI; ++i)
 #pragma unroll
       for (int j = 0; j < BJ; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[i][j][v] *= kMagicScale;
+        for (int v = 0; v < 4; ++v) acc[i][j][v] *= out_scale;
 
     // low-rank up-projection on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16):
     // acc += L2^T[n, :] . XL1[m, :]; lane = (row l16, rank entries 8*lg .. +8)
