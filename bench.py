@@ -1,7 +1,7 @@
 """Benchmark of the SVDQuant W4A4 linear + AWQ W4A16 GEMV hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-  1. svdq_quantize_act  on the DiT fused-QKV projection input X [4608, 3072]
+  1. svdq_quantize_act_ws on the DiT fused-QKV projection input X [4608, 3072]
      (smoothing, int4 group-64 codes and scales, fused X.L1 with rank 32),
   2. svdq_w4a4_gemm_ws  against W [9216, 3072] (int4 group 64) with the fused
      low-rank up-projection and bias, Y bf16 [4608, 9216] (with its workspace:
@@ -157,7 +157,9 @@ def main():
     SCALES = [torch.empty((M, K // 64), dtype=torch.float16, device=dev) for _ in range(C)]
     XL1 = [torch.empty((M, R), dtype=torch.float32, device=dev) for _ in range(C)]
     Y = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(2)]
-    WORK = sq.gemm_workspace(dev)  # the GEMM's split last round of tiles (svdq_w4a4_gemm_ws)
+    # one workspace for the stream: the quantizer's balanced split (svdq_quantize_act_ws)
+    # and the GEMM's split last round of tiles (svdq_w4a4_gemm_ws)
+    WORK = sq.gemm_workspace(dev)
 
     A = max(1, args.awq_copies)
     AX = bf(awq["x"])
@@ -175,7 +177,8 @@ def main():
         c = i % C
         if ev is not None:
             ev[0].record(stream)
-        sq.quantize_act(sq.SVDQ_INT4, X[c], LAM, L1T, out=(CODES[c], SCALES[c], XL1[c]), stream=stream)
+        sq.quantize_act(sq.SVDQ_INT4, X[c], LAM, L1T, out=(CODES[c], SCALES[c], XL1[c]), stream=stream,
+                        workspace=WORK)
         if ev is not None:
             ev[1].record(stream)
         if gemm_ev is not None:
@@ -317,14 +320,17 @@ def extras(args, torch, sq, synth, t, bf, f16, stream):
         xl1 = torch.empty((M, 32), dtype=torch.float32, device=dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         aa, aw = float(d["alpha_a"]), float(d["alpha_w"])
-        q_ms = median_ms(lambda i: sq.quantize_act(prec, x, lam, l1t, aa, out=(codes, scales, xl1), stream=stream),
-                         n, stream, torch)
+        q_ms = median_ms(lambda i: sq.quantize_act(prec, x, lam, l1t, aa, out=(codes, scales, xl1), stream=stream,
+                                                   workspace=work), n, stream, torch)
+        q0_ms = median_ms(lambda i: sq.quantize_act(prec, x, lam, l1t, aa, out=(codes, scales, xl1), stream=stream),
+                          n, stream, torch)
         g_ms = median_ms(lambda i: sq.w4a4_gemm(prec, codes, scales, wc, ws, xl1, l2t, bias, aa, aw, out=y,
                                                 stream=stream, workspace=work), n, stream, torch)
         ops = 2.0 * M * N * K
         tops = ops / (g_ms * 1e-3) / 1e12
         qb = M * K * 2 + K * 2 + 32 * K * 2 + M * K // 2 + M * (K // G) * (2 if prec == sq.SVDQ_INT4 else 1) + M * 32 * 4
         r = {"quantize_ms": round(q_ms, 5), "quantize_GBps": round(qb / (q_ms * 1e-3) / 1e9, 1),
+             "quantize_no_workspace_ms": round(q0_ms, 5),
              "gemm_ms": round(g_ms, 5), "gemm_TOPS": round(tops, 2),
              "linear_TOPS": round(ops / ((q_ms + g_ms) * 1e-3) / 1e12, 2)}
         if prec == sq.SVDQ_INT4:

@@ -33,7 +33,7 @@ _STATUS = {0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARG", 2: "SVDQ_ERR_UNSUPPORTED",
 # SVDQ_GEMM_WORK_BYTES: size of svdq_w4a4_gemm_ws's workspace
 GEMM_WORK_BYTES = 16 * 1024 * 1024 + 4096
 
-EXPORTS = ["svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_ws", "svdq_w4a4_gemm_qkv_norm_rope",
+EXPORTS = ["svdq_quantize_act", "svdq_quantize_act_ws", "svdq_w4a4_gemm", "svdq_w4a4_gemm_ws", "svdq_w4a4_gemm_qkv_norm_rope",
            "svdq_w4a4_gemm_qkv_norm_rope_ws", "svdq_w4a4_gemm_gelu_quant",
            "awq_w4a16_gemv", "svdq_calibrate_smooth", "svdq_lowrank_workspace_bytes", "svdq_lowrank_decompose",
            "svdq_lowrank_decompose_noalloc",
@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
         L.svdq_quantize_act.argtypes = [i32, i32, i32, i64, i64, vp, vp, vp, f32, vp, vp, vp, vp]
+        L.svdq_quantize_act_ws.argtypes = [i32, i32, i32, i64, i64, vp, vp, vp, f32, vp, vp, vp, vp, i64, vp]
         L.svdq_w4a4_gemm.argtypes = [i32, i32, i32, i64, i64, i64, vp, vp, f32, vp, vp, f32, vp, vp,
                                      vp, vp, vp]
         L.svdq_w4a4_gemm_ws.argtypes = [i32, i32, i32, i64, i64, i64, vp, vp, f32, vp, vp, f32, vp, vp,
@@ -80,7 +81,7 @@ def lib() -> ctypes.CDLL:
         L.svdq_quantize_weight.argtypes = [i32, i32, i64, i64, vp, f32, vp, vp, vp]
         L.awq_quantize_weight.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
         L.svdq_w4a4_group_psums.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp]
-        for f in ("svdq_quantize_act", "svdq_w4a4_gemm", "svdq_w4a4_gemm_ws", "svdq_w4a4_gemm_qkv_norm_rope",
+        for f in ("svdq_quantize_act", "svdq_quantize_act_ws", "svdq_w4a4_gemm", "svdq_w4a4_gemm_ws", "svdq_w4a4_gemm_qkv_norm_rope",
                   "svdq_w4a4_gemm_qkv_norm_rope_ws",
                   "svdq_w4a4_gemm_gelu_quant", "awq_w4a16_gemv", "svdq_w4a4_group_psums", "svdq_calibrate_smooth",
                   "svdq_lowrank_decompose", "svdq_lowrank_decompose_noalloc", "svdq_quantize_weight",
@@ -161,10 +162,11 @@ def _dims(fn, t, name, nd):
 
 
 def quantize_act(precision: int, x, smooth=None, l1t=None, act_global_scale: float = 1.0,
-                 out=None, stream=None):
-    """svdq_quantize_act.  x: bf16 [M, K]; smooth: bf16 [K] or None; l1t: bf16 [r, K]
-    or None.  Returns (codes u8 [M, K/2], scales, xl1 fp32 [M, r] or None); `out`
-    may supply that triple preallocated."""
+                 out=None, stream=None, workspace=None):
+    """svdq_quantize_act, or svdq_quantize_act_ws when `workspace` (see gemm_workspace;
+    the same one may serve the GEMMs of the stream) is given.  x: bf16 [M, K]; smooth:
+    bf16 [K] or None; l1t: bf16 [r, K] or None.  Returns (codes u8 [M, K/2], scales,
+    xl1 fp32 [M, r] or None); `out` may supply that triple preallocated."""
     M, K = _dims("quantize_act", x, "x", 2)
     G = GROUP.get(precision, 64)
     r = 0 if l1t is None else _dims("quantize_act", l1t, "l1t", 2)[0]
@@ -176,10 +178,14 @@ def quantize_act(precision: int, x, smooth=None, l1t=None, act_global_scale: flo
         codes, scales, xl1 = out
     (_Args("quantize_act").req("x", x, _BF16, (M, K)).req("smooth", smooth, _BF16, (K,), True)
      .req("l1t", l1t, _BF16, (r, K), True).req("codes", codes, _U8, (M, K // 2))
-     .req("scales", scales, _scale_dtype(precision), (M, K // G)).req("xl1", xl1, _F32, (M, r), r == 0).done())
-    _check(lib().svdq_quantize_act(precision, G, r, M, K, _ptr(x), _ptr(smooth), _ptr(l1t),
-                                   float(act_global_scale), _ptr(codes), _ptr(scales), _ptr(xl1),
-                                   _stream(stream)))
+     .req("scales", scales, _scale_dtype(precision), (M, K // G)).req("xl1", xl1, _F32, (M, r), r == 0)
+     .req("workspace", workspace, _U8, (GEMM_WORK_BYTES,), True).done())
+    args = (precision, G, r, M, K, _ptr(x), _ptr(smooth), _ptr(l1t), float(act_global_scale), _ptr(codes),
+            _ptr(scales), _ptr(xl1))
+    if workspace is None:
+        _check(lib().svdq_quantize_act(*args, _stream(stream)))
+    else:
+        _check(lib().svdq_quantize_act_ws(*args, _ptr(workspace), GEMM_WORK_BYTES, _stream(stream)))
     return codes, scales, xl1
 
 

@@ -30,6 +30,7 @@ struct QuantArgs {
   void* codes;
   void* scales;
   float* xl1;
+  void* work;  // svdq_quantize_act_ws: the GEMM workspace (counters zero), or null
 };
 
 // Epilogue of the fused attention projection: columns [Q | K | V], each hd =
@@ -79,6 +80,25 @@ constexpr int kTailMaxTiles = 64, kTailParts = 4;
 constexpr size_t kTailTileBytes = (size_t)128 * 128 * 4;  // fp32 accumulators of one 128 x 128 tile
 constexpr size_t kTailPartBytes = (size_t)kTailMaxTiles * kTailParts * kTailTileBytes;
 constexpr size_t kGemmWorkBytes = kTailPartBytes + 4096;
+
+// The balanced quantizer (svdq_quantize_act_ws): the grid of (32-row block,
+// 64-channel step) pairs cut into equal contiguous ranges of L steps, one per
+// workgroup, L <= steps per block, so a block is shared by workgroups only at
+// range ends.  The XL1 rows of a shared block are summed from the pieces'
+// fp32 partial tiles in part (two slots per workgroup) by the last piece to
+// arrive, counted in cnt[first workgroup of the block].  Both live in the
+// GEMM workspace: part in its partial-tile area (scratch), cnt in its counter
+// page above the GEMM's counters, zero between calls like those.
+struct QuantSplit {
+  int L, T;       // steps per workgroup (0: one block per workgroup), blocks * steps
+  float* part;    // [2 * workgroups][32 rows][rank]
+  unsigned* cnt;  // [workgroups]
+};
+constexpr int kQuantMaxGroups = 512;
+constexpr size_t kQuantCntOffset = kTailPartBytes + 1024;
+static_assert((size_t)kQuantMaxGroups * 2 * 32 * 32 * 4 <= kTailPartBytes, "quantizer partials fit the workspace");
+static_assert((size_t)kTailMaxTiles * 4 <= 1024 && 1024 + (size_t)kQuantMaxGroups * 4 <= 4096,
+              "GEMM and quantizer counters share the counter page without overlap");
 
 struct GemmArgs {
   int precision, rank;

@@ -272,11 +272,11 @@ __device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t res, uint8_t* dst,
 }
 }  // namespace dma
 
-template <int PREC, int RB, bool CH>
+template <int PREC, int RB, bool CH, bool BAL>
 __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
     int M, int K, const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
     const uint16_t* __restrict__ l1t, float alpha, uint8_t* __restrict__ codes,
-    void* __restrict__ scales, float* __restrict__ xl1) {
+    void* __restrict__ scales, float* __restrict__ xl1, QuantSplit sp) {
   using namespace dma;
   static_assert(RB == 1 || RB == 2, "LDS holds L1^T slices of 16 or 32 ranks");
   constexpr int LSL = RB * 2048;    // bytes of one step's L1^T slice (16*RB rows x 128 B)
@@ -293,14 +293,36 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
   __shared__ __align__(16) uint8_t lst[8][1024];            // the next chunk's lambda (bf16), waves 0-3
   __shared__ __align__(16) uint8_t xs0[8][2048], xs1[8][2048], xs2[8][2048], xs3[8][2048];  // X slices per wave
   __shared__ __align__(16) uint8_t ls0[4][LSL], ls1[4][LSL], ls2[4][LSL], ls3[4][LSL];     // L1^T slices per step lane
+  __shared__ unsigned xflag;                                // arrival count read by the whole workgroup
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rbk = wave >> 2, sl = wave & 3;  // row block, step lane
-  const int row0 = blockIdx.x * 32;
   const int r = lane & 15, c = lane >> 4;
   const int nsteps = K >> 6;
-  const int rounds = (nsteps + 3) >> 2;
+  // This workgroup's rounds nr (four steps each), its first 32-row block
+  // pair0 and first step st0 in it, and jb, the first round in the next block
+  // (past nr: none).  Balanced ranges start and end on whole rounds (L and
+  // the steps per block are multiples of four), so a round never straddles
+  // two blocks.
+  int nr, jb, pair0, st0;
+  if constexpr (BAL) {
+    const int s0 = (int)blockIdx.x * sp.L;
+    pair0 = s0 / nsteps;
+    st0 = s0 - pair0 * nsteps;
+    nr = min(sp.L, sp.T - s0) >> 2;
+    jb = (nsteps - st0) >> 2;
+  } else {
+    pair0 = blockIdx.x;
+    st0 = 0;
+    nr = (nsteps + 3) >> 2;
+    jb = nr;
+  }
+  const int row0 = pair0 * 32;
+  // first step (step lane 0) of round j
+  auto rstep = [&](int j) __attribute__((always_inline)) -> int {
+    return BAL ? (j < jb ? st0 + 4 * j : 4 * (j - jb)) : 4 * j;
+  };
 
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t lres = __builtin_amdgcn_make_buffer_rsrc((void*)l1t, (short)0, RB * 16 * K * 2, 0x00020000);
@@ -321,37 +343,42 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
     const int ri = 8 * (RB * rbk + i) + cr;  // L1^T row: this wave copies rows 8*RB*rbk .. +8*RB
     ldo[i] = (u32)ri * (u32)K * 2u + (u32)(((lane & 7) ^ rsw(ri)) << 4);
   }
-  // this lane's output row and its store offsets (rows past M: dropped)
+  // this lane's output row and its store offsets, in the first block and (BAL)
+  // the next one (rows past M: dropped)
   const int orow = row0 + 16 * rbk + r;
-  const bool rlive = orow < M;
+  const bool rlive = orow < M, rlive1 = orow + 32 < M;
   const int cbase = rlive ? orow * (K >> 1) + 8 * c : kOut;
   const int sbase = PREC == 0 ? (rlive && c == 0 ? orow * (K >> 6) * 2 : kOut) : (rlive ? orow * (K >> 4) + c : kOut);
+  const int cbase1 = BAL && rlive1 ? (orow + 32) * (K >> 1) + 8 * c : kOut;
+  const int sbase1 = !BAL ? kOut
+                     : PREC == 0 ? (rlive1 && c == 0 ? (orow + 32) * (K >> 6) * 2 : kOut)
+                                 : (rlive1 ? (orow + 32) * (K >> 4) + c : kOut);
 
-  v4f acc[RB];
+  v4f acc[RB], accA[RB];  // accA: the first block's sums once round jb starts the next
 #pragma unroll
-  for (int i = 0; i < RB; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < RB; ++i) acc[i] = accA[i] = v4f{0.f, 0.f, 0.f, 0.f};
   const float d6 = 6.0f * alpha;
 
   // copy the step of round j for this wave into slot buffers (xb, lb); steps
   // past the end use out-of-range offsets (zeros, no memory access), so every
   // wave issues the same copies in every round and the waits count exactly
   auto issue = [&](int j, uint8_t(*xb)[2048], uint8_t(*lb)[LSL]) __attribute__((always_inline)) {
-    const int st = 4 * j + sl;
-    const bool live = st < nsteps;
+    const int st = rstep(j) + sl;
+    const bool live = BAL ? j < nr : st < nsteps;
     const u32 sb = 128u * (u32)st;
+    const u32 xsb = sb + (BAL && j >= jb ? 64u * (u32)K : 0u);  // the next block: 32 rows further
 #pragma unroll
-    for (int i = 0; i < 2; ++i) copy16(xres, xb[wave] + 1024 * i, live ? (int)(xdo[i] + sb) : kOut);
+    for (int i = 0; i < 2; ++i) copy16(xres, xb[wave] + 1024 * i, live ? (int)(xdo[i] + xsb) : kOut);
 #pragma unroll
     for (int i = 0; i < RB; ++i) copy16(lres, lb[sl] + 1024 * (RB * rbk + i), live ? (int)(ldo[i] + sb) : kOut);
   };
   // the NSTO stores of a round, issued also for steps past the end (dropped)
-  auto store = [&](int st, u32 pk0, u32 pk1, u32 sbits) __attribute__((always_inline)) {
-    const bool live = st < nsteps;
-    __builtin_amdgcn_raw_buffer_store_b64(u2v{pk0, pk1}, cres, live ? cbase + 32 * st : kOut, 0, 0);
+  auto store = [&](bool live, int cb, int sbs, int st, u32 pk0, u32 pk1, u32 sbits) __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_buffer_store_b64(u2v{pk0, pk1}, cres, live ? cb + 32 * st : kOut, 0, 0);
     if constexpr (PREC == 0)
-      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)sbits, sres, live ? sbase + 2 * st : kOut, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)sbits, sres, live ? sbs + 2 * st : kOut, 0, 0);
     else
-      __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sbits, sres, live ? sbase + 4 * st : kOut, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sbits, sres, live ? sbs + 4 * st : kOut, 0, 0);
   };
   // lambda of a chunk: thread t < 256 loads channels 8t .. 8t+7 (16 bytes);
   // for the first chunk straight into registers, for the next ones by a copy
@@ -366,25 +393,26 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
     const int ch = q * KC + 8 * tid;
     copy16(lamres, lst[wave], wave < 4 && ch < K ? 2 * ch : kOut);
   };
-  auto lam_store = [&](int buf, uint4 lv) __attribute__((always_inline)) {
-    if (tid < KC / 8) {
-      const u32 w4[4] = {lv.x, lv.y, lv.z, lv.w};
-      float o[8];
+  // reciprocals of the eight lambda values in lv, to dst[0 .. 8)
+  auto lam_recip = [&](float* dst, uint4 lv) __attribute__((always_inline)) {
+    const u32 w4[4] = {lv.x, lv.y, lv.z, lv.w};
+    float o[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[2 * e] = lam ? 1.0f / bf16_bits_to_f32(w4[e] & 0xFFFFu) : 1.0f;
-        o[2 * e + 1] = lam ? 1.0f / bf16_bits_to_f32(w4[e] >> 16) : 1.0f;
-      }
-      *(float4*)&rl[buf][8 * tid] = float4{o[0], o[1], o[2], o[3]};
-      *(float4*)&rl[buf][8 * tid + 4] = float4{o[4], o[5], o[6], o[7]};
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = lam ? 1.0f / bf16_bits_to_f32(w4[e] & 0xFFFFu) : 1.0f;
+      o[2 * e + 1] = lam ? 1.0f / bf16_bits_to_f32(w4[e] >> 16) : 1.0f;
     }
+    *(float4*)dst = float4{o[0], o[1], o[2], o[3]};
+    *(float4*)(dst + 4) = float4{o[4], o[5], o[6], o[7]};
   };
 
   // quantize the step of round j from slot buffers (xb, lb), store its codes
   // and scale, and add its X.L1 share
   auto compute = [&](int j, uint8_t(*xb)[2048], uint8_t(*lb)[LSL]) __attribute__((always_inline)) {
-    const int st = 4 * j + sl;  // step within K
-    const float* rlc = CH ? &rl[(st >> 5) & 1][((st & 31) << 6) + (c << 4)] : &rl[0][0] + (st << 6) + (c << 4);
+    const int st = rstep(j) + sl;  // step within K
+    const bool nxt = BAL && j >= jb;
+    // a chunked table holds the chunk of rounds 8t .. 8t+7 in buffer t & 1
+    const float* rlc = CH ? &rl[(j >> 3) & 1][((st & 31) << 6) + (c << 4)] : &rl[0][0] + (st << 6) + (c << 4);
     const uint8_t* xrow = xb[wave] + r * 128;
     const uint4 va = *(const uint4*)(xrow + swz(r, 2 * c));
     const uint4 vb = *(const uint4*)(xrow + swz(r, 2 * c + 1));
@@ -423,7 +451,16 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
       pk0 = sf == 0.0f ? 0u : e2m1_codes8(xh, t);
       pk1 = sf == 0.0f ? 0u : e2m1_codes8(xh + 8, t);
     }
-    store(st, pk0, pk1, sbits);
+    store(BAL ? j < nr : st < nsteps, nxt ? cbase1 : cbase, nxt ? sbase1 : sbase, st, pk0, pk1, sbits);
+    if constexpr (BAL) {
+      if (j == jb && j < nr) {  // first round of the next block: set the first block's sums aside
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          accA[rb] = acc[rb];
+          acc[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
     // XL1 += X[16 rows, these 64 channels] . L1[these channels, 16*RB]
     const v8bf a0 = __builtin_bit_cast(v8bf, va);
     const v8bf a1 = __builtin_bit_cast(v8bf, vb);
@@ -438,43 +475,42 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
     }
   };
 
-  // Prologue: the reciprocals of lambda (K <= 2 KC: the whole table; else the
-  // first chunk), then rounds 0 .. 2 in flight, each followed by NSTO dropped
-  // stores so that every later round finds the same instruction pattern
-  // behind its copies (the waits below count it).
+  // Prologue: the load of lambda (the whole table for K <= 2 KC, else the
+  // first chunk) goes out first, then rounds 0 .. 2, each followed by NSTO
+  // dropped stores so that every later round finds the same instruction
+  // pattern behind its copies (the waits below count it); the reciprocals are
+  // formed once lambda has landed, while the copies are still in flight.
+  uint4 lv0;
   if constexpr (CH) {
-    lam_store(0, lam_load(0));
+    lv0 = lam_load(rstep(0) >> 5);
   } else {
     const int ch = 8 * tid;
-    const uint4 lv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lamres, ch < K ? 2 * ch : kOut, 0, 0));
-    const u32 w4[4] = {lv.x, lv.y, lv.z, lv.w};
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[2 * e] = lam ? 1.0f / bf16_bits_to_f32(w4[e] & 0xFFFFu) : 1.0f;
-      o[2 * e + 1] = lam ? 1.0f / bf16_bits_to_f32(w4[e] >> 16) : 1.0f;
-    }
-    *(float4*)(&rl[0][0] + ch) = float4{o[0], o[1], o[2], o[3]};
-    *(float4*)(&rl[0][0] + ch + 4) = float4{o[4], o[5], o[6], o[7]};
+    lv0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lamres, ch < K ? 2 * ch : kOut, 0, 0));
   }
   issue(0, xs0, ls0);
-  store(nsteps, 0u, 0u, 0u);
+  store(false, cbase, sbase, 0, 0u, 0u, 0u);
   issue(1, xs1, ls1);
-  store(nsteps, 0u, 0u, 0u);
+  store(false, cbase, sbase, 0, 0u, 0u, 0u);
   issue(2, xs2, ls2);
-  store(nsteps, 0u, 0u, 0u);
+  store(false, cbase, sbase, 0, 0u, 0u, 0u);
+  if constexpr (CH) {
+    if (tid < KC / 8) lam_recip(&rl[0][8 * tid], lv0);
+  } else {
+    lam_recip(&rl[0][0] + 8 * tid, lv0);
+  }
 
   // Round j = 8t + P: wait for this wave's copies of round j and its LDS
   // traffic, barrier (every wave's copies of round j have landed; every wave
   // is done with the slot of round j-1 and, at P = 0, with the reciprocal
   // buffer of the chunk before), then, with a chunked table, at P = 0 copy
-  // the next chunk's lambda (landed by the wait of round j+3, where the table
+  // the chunk of round j+8 (landed by the wait of round j+3, where the table
   // is filled; lst is rewritten only by the next chunk's P = 0, after that
   // round's barrier), refill the freed slot with round j+3, compute round j.
-  // Steps past the end (a partial last round, the rounds that pad the loop to
-  // whole unrolled blocks) are computed on the zeros their copies brought and
-  // their stores dropped: no branch, so the compiler keeps track of which copy
-  // fills which slot and adds no waits of its own.
+  // Steps past the end (the rounds that pad the loop to whole unrolled
+  // blocks, before the exit test stops it) are computed on the zeros their
+  // copies brought and their stores dropped: no branch inside a round, so the
+  // compiler keeps track of which copy fills which slot and adds no waits of
+  // its own.
   auto round = [&](int j, auto pc, uint8_t(*xa)[2048], uint8_t(*la)[LSL], uint8_t(*xc)[2048], uint8_t(*lc)[LSL])
       __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
@@ -482,10 +518,10 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if constexpr (CH && P == 0) lam_copy((j >> 3) + 1);
+    if constexpr (CH && P == 0) lam_copy(rstep(j + 8) >> 5);
     issue(j + 3, xc, lc);
     if constexpr (CH && P == 3) {
-      if (tid < KC / 8) lam_store(((j >> 3) + 1) & 1, *(const uint4*)&lst[tid >> 6][16 * (tid & 63)]);
+      if (tid < KC / 8) lam_recip(&rl[((j >> 3) + 1) & 1][8 * tid], *(const uint4*)&lst[tid >> 6][16 * (tid & 63)]);
     }
     compute(j, xa, la);
   };
@@ -498,21 +534,31 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
   using P6 = std::integral_constant<int, 6>;
   using P7 = std::integral_constant<int, 7>;
   if constexpr (CH) {
-    for (int j = 0; j < rounds; j += 8) {
+    for (int j = 0; j < nr; j += 8) {
       round(j, P0{}, xs0, ls0, xs3, ls3);
+      if (j + 1 >= nr) break;
       round(j + 1, P1{}, xs1, ls1, xs0, ls0);
+      if (j + 2 >= nr) break;
       round(j + 2, P2{}, xs2, ls2, xs1, ls1);
+      if (j + 3 >= nr) break;
       round(j + 3, P3{}, xs3, ls3, xs2, ls2);
+      if (j + 4 >= nr) break;
       round(j + 4, P4{}, xs0, ls0, xs3, ls3);
+      if (j + 5 >= nr) break;
       round(j + 5, P5{}, xs1, ls1, xs0, ls0);
+      if (j + 6 >= nr) break;
       round(j + 6, P6{}, xs2, ls2, xs1, ls1);
+      if (j + 7 >= nr) break;
       round(j + 7, P7{}, xs3, ls3, xs2, ls2);
     }
   } else {
-    for (int j = 0; j < rounds; j += 4) {
+    for (int j = 0; j < nr; j += 4) {
       round(j, P4{}, xs0, ls0, xs3, ls3);
+      if (j + 1 >= nr) break;
       round(j + 1, P5{}, xs1, ls1, xs0, ls0);
+      if (j + 2 >= nr) break;
       round(j + 2, P6{}, xs2, ls2, xs1, ls1);
+      if (j + 3 >= nr) break;
       round(j + 3, P7{}, xs3, ls3, xs2, ls2);
     }
   }
@@ -520,40 +566,131 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
   // per-wave partial XL1 tiles [16 rows][R] in slot xs0 (every copy has
   // landed and every wave is past its last read), summed over the four step
   // lanes of each row block in a fixed order; lane holds
-  // D[row 4*(lane/16) + v][col lane%16] of each 16x16 block
+  // D[row 4*(lane/16) + v][col lane%16] of each 16x16 block.  Thread t ends
+  // with the sums of tile entries t + NT k (row (t + NT k) / R), k < RB.
   constexpr int R = RB * 16;
+  constexpr int TILE = 32 * R;
+  static_assert(TILE == RB * NT, "RB tile entries per thread");
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
   __syncthreads();
   float* red = (float*)&xs0[0][0];
   static_assert(8 * 16 * R * 4 <= 8 * 2048, "partial XL1 tiles fit in one X slot");
+  float sums[RB];
+  auto reduce = [&](const v4f* a) __attribute__((always_inline)) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * c + v) * R + rb * 16 + r] = acc[rb][v];
-  __syncthreads();
-  for (int idx = tid; idx < 32 * R; idx += NT) {
-    const int rr = idx / R, col = idx - rr * R;  // row within the 32
-    const int b = rr >> 4, ri = rr & 15;
-    float sum = red[((4 * b) * 16 + ri) * R + col];
+      for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * c + v) * R + rb * 16 + r] = a[rb][v];
+    __syncthreads();
 #pragma unroll
-    for (int s2 = 1; s2 < 4; ++s2) sum += red[((4 * b + s2) * 16 + ri) * R + col];  // fixed order
-    if (row0 + rr < M) xl1[(size_t)(row0 + rr) * R + col] = sum;
+    for (int k = 0; k < RB; ++k) {
+      const int idx = tid + NT * k;
+      const int rr = idx / R, col = idx - rr * R;  // row within the 32
+      const int b = rr >> 4, ri = rr & 15;
+      float sum = red[((4 * b) * 16 + ri) * R + col];
+#pragma unroll
+      for (int s2 = 1; s2 < 4; ++s2) sum += red[((4 * b + s2) * 16 + ri) * R + col];  // fixed order
+      sums[k] = sum;
+    }
+  };
+  auto write_rows = [&](int rbase, const float* s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      const int idx = tid + NT * k;
+      const int rr = idx / R;
+      if (rbase + rr < M) xl1[(size_t)rbase * R + idx] = s[k];
+    }
+  };
+  if constexpr (!BAL) {
+    reduce(acc);
+    write_rows(row0, sums);
+  } else {
+    // A block shared with other workgroups: store this piece's tile with
+    // agent-coherent stores, wait until they are performed, count the piece
+    // in; the last piece to arrive resets the counter and writes the block's
+    // XL1 as the sum of all pieces in workgroup order (the same sum whichever
+    // arrives last).  No workgroup waits for another.
+    auto exchange = [&](int p, int seg) __attribute__((always_inline)) {
+      const int first = (int)(((long long)p * nsteps) / sp.L);
+      const int last = (int)(((long long)(p + 1) * nsteps - 1) / sp.L);
+      float* const mine = sp.part + (size_t)(2 * (int)blockIdx.x + seg) * TILE;
+#pragma unroll
+      for (int k = 0; k < RB; ++k) __hip_atomic_store(mine + tid + NT * k, sums[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);  // every store of this wave performed
+      __syncthreads();
+      if (tid == 0) xflag = __hip_atomic_fetch_add(sp.cnt + first, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const unsigned arrived = __builtin_amdgcn_readfirstlane(*(volatile unsigned*)&xflag);
+      if (arrived != (unsigned)(last - first)) return;
+      if (tid == 0) __hip_atomic_store(sp.cnt + first, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      float tot[RB];
+#pragma unroll
+      for (int k = 0; k < RB; ++k) tot[k] = 0.0f;
+      for (int w = first; w <= last; ++w) {
+        const int slot = 2 * w + (p - (int)(((long long)w * sp.L) / nsteps));
+        const float* src = sp.part + (size_t)slot * TILE;
+#pragma unroll
+        for (int k = 0; k < RB; ++k)
+          tot[k] += w == (int)blockIdx.x ? sums[k]
+                                         : __hip_atomic_load(src + tid + NT * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      write_rows(p * 32, tot);
+    };
+    const bool two = jb < nr;
+    if (two) reduce(accA);
+    else reduce(acc);
+    if (st0 == 0 && nr >= jb) write_rows(row0, sums);  // the whole block is this workgroup's
+    else exchange(pair0, 0);
+    if (two) {
+      __syncthreads();  // every wave is done with red and xflag
+      reduce(acc);
+      exchange(pair0 + 1, 1);
+    }
   }
+}
+
+template <int PREC, int RB, bool CH, bool BAL>
+static hipError_t launch_dma(const QuantArgs& a, int blocks, const QuantSplit& sp, hipStream_t st) {
+  hipLaunchKernelGGL((quant_act_dma_kernel<PREC, RB, CH, BAL>), dim3(blocks), dim3(dma::NT), 0, st, (int)a.M,
+                     (int)a.K, (const uint16_t*)a.x, (const uint16_t*)a.smooth, (const uint16_t*)a.l1t, a.alpha,
+                     (uint8_t*)a.codes, a.scales, a.xl1, sp);
+  return hipGetLastError();
+}
+
+// The balanced split of svdq_quantize_act_ws: ranges of L steps, L the even
+// share of the CUs rounded up to whole rounds (whole 2048-channel chunks of
+// the reciprocal table when K > 2 KC), used when L is below the steps of one
+// block (fewer blocks than CUs) and the blocks' steps are whole such units.
+// Returns false (sp untouched) where it does not apply.
+static bool balanced_split(const QuantArgs& a, QuantSplit& sp, int& blocks) {
+  if (!a.work || a.M <= 0) return false;
+  const int nsteps = (int)(a.K >> 6);
+  const int unit = a.K > 2 * dma::KC ? 32 : 4;
+  if (nsteps % unit != 0) return false;
+  const long long T = (long long)((a.M + 31) / 32) * nsteps;
+  const int cus = device_cu_count();
+  long long L = (T + cus - 1) / cus;
+  L = (L + unit - 1) / unit * unit;
+  if (L >= nsteps) return false;
+  const long long G = (T + L - 1) / L;
+  if (G > kQuantMaxGroups) return false;
+  sp.L = (int)L;
+  sp.T = (int)T;
+  sp.part = (float*)a.work;
+  sp.cnt = (unsigned*)((uint8_t*)a.work + kQuantCntOffset);
+  blocks = (int)G;
+  return true;
 }
 
 template <int PREC, int RB>
 static hipError_t launch_quant_dma(const QuantArgs& a, hipStream_t st) {
-  const int blocks = (int)((a.M + 31) / 32);
-  if (a.K <= 2 * dma::KC) {  // the whole reciprocal table in LDS
-    hipLaunchKernelGGL((quant_act_dma_kernel<PREC, RB, false>), dim3(blocks), dim3(dma::NT), 0, st, (int)a.M,
-                       (int)a.K, (const uint16_t*)a.x, (const uint16_t*)a.smooth, (const uint16_t*)a.l1t, a.alpha,
-                       (uint8_t*)a.codes, a.scales, a.xl1);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL((quant_act_dma_kernel<PREC, RB, true>), dim3(blocks), dim3(dma::NT), 0, st, (int)a.M, (int)a.K,
-                     (const uint16_t*)a.x, (const uint16_t*)a.smooth, (const uint16_t*)a.l1t,
-                     a.alpha, (uint8_t*)a.codes, a.scales, a.xl1);
-  return hipGetLastError();
+  QuantSplit sp{0, 0, nullptr, nullptr};
+  int blocks = (int)((a.M + 31) / 32);
+  const bool ch = a.K > 2 * dma::KC;  // else the whole reciprocal table in LDS
+  if (balanced_split(a, sp, blocks))
+    return ch ? launch_dma<PREC, RB, true, true>(a, blocks, sp, st) : launch_dma<PREC, RB, false, true>(a, blocks, sp, st);
+  return ch ? launch_dma<PREC, RB, true, false>(a, blocks, sp, st) : launch_dma<PREC, RB, false, false>(a, blocks, sp, st);
 }
 
 template <int PREC, int RB>
@@ -561,9 +698,12 @@ static hipError_t launch_quant(const QuantArgs& a, hipStream_t st) {
   // Ranks 16 / 32: once the 16-row workgroups of the kernel above no longer
   // fit one per CU, the LDS-staged kernel (32 rows per workgroup, coalesced
   // copies) is faster, for both precisions; below that the one-row-block
-  // workgroups keep every CU busy.
+  // workgroups keep every CU busy.  With a workspace, the LDS-staged kernel's
+  // balanced split applies at any M where it cuts the work per CU.
   if constexpr (RB == 1 || RB == 2) {
-    if ((a.M + 15) / 16 > device_cu_count()) return launch_quant_dma<PREC, RB>(a, st);
+    QuantSplit sp{0, 0, nullptr, nullptr};
+    int blocks = 0;
+    if ((a.M + 15) / 16 > device_cu_count() || balanced_split(a, sp, blocks)) return launch_quant_dma<PREC, RB>(a, st);
   }
   const size_t red = RB > 0 ? (size_t)QuantCfg<RB>::WAVES * 16 * RB * 16 : 0;
   const size_t lds = sizeof(float) * ((size_t)a.K > red ? (size_t)a.K : red);

@@ -121,10 +121,9 @@ void svdq_test_set_arch_override(const char* arch) {
 
 void svdq_test_set_no_ksplit(int on) { svdq::set_no_ksplit(on); }
 
-svdq_status svdq_quantize_act(int precision, int group_size, int rank, int64_t M, int64_t K,
-                              const void* x, const void* smooth, const void* l1t,
-                              float act_global_scale, void* act_codes, void* act_scales,
-                              float* xl1, void* stream) {
+static svdq_status quantize_act(int precision, int group_size, int rank, int64_t M, int64_t K, const void* x,
+                                const void* smooth, const void* l1t, float act_global_scale, void* act_codes,
+                                void* act_scales, float* xl1, void* stream, void* work, int64_t work_bytes) {
   svdq_status s;
   if ((s = check_precision(precision, group_size)) != SVDQ_OK) return s;
   if (!valid_rank(rank)) return fail(SVDQ_ERR_UNSUPPORTED, "rank %d not in {0, 16, ..., 128}", rank);
@@ -149,11 +148,40 @@ svdq_status svdq_quantize_act(int precision, int group_size, int rank, int64_t M
       overlaps(act_codes, nc, act_scales, ns) || overlaps(act_codes, nc, xl1, nl) ||
       overlaps(act_scales, ns, xl1, nl))
     return fail(SVDQ_ERR_INVALID_ARG, "outputs must not overlap each other or x");
+  if (work) {
+    if (work_bytes < (int64_t)SVDQ_GEMM_WORK_BYTES)
+      return fail(SVDQ_ERR_INVALID_ARG, "work_bytes=%lld below SVDQ_GEMM_WORK_BYTES=%lld", (long long)work_bytes,
+                  (long long)SVDQ_GEMM_WORK_BYTES);
+    if (!aligned16(work)) return fail(SVDQ_ERR_ALIGNMENT, "all buffers must be 16-byte aligned");
+    const size_t nw = (size_t)SVDQ_GEMM_WORK_BYTES;
+    if (overlaps(work, nw, x, nx) || overlaps(work, nw, act_codes, nc) || overlaps(work, nw, act_scales, ns) ||
+        overlaps(work, nw, xl1, nl) || overlaps(work, nw, smooth, (size_t)K * 2) ||
+        overlaps(work, nw, l1t, (size_t)rank * K * 2))
+      return fail(SVDQ_ERR_INVALID_ARG, "work must not overlap x, an input or an output");
+  } else if (work_bytes != 0) {
+    return fail(SVDQ_ERR_INVALID_ARG, "work_bytes=%lld given without work", (long long)work_bytes);
+  }
   if ((s = check_arch()) != SVDQ_OK) return s;
   if (M == 0) return ok();
   if ((s = check_sticky()) != SVDQ_OK) return s;
-  svdq::QuantArgs a{precision, rank, M, K, x, smooth, l1t, act_global_scale, act_codes, act_scales, xl1};
+  svdq::QuantArgs a{precision, rank, M, K, x, smooth, l1t, act_global_scale, act_codes, act_scales, xl1, work};
   return launched(svdq::launch_quantize_act(a, (hipStream_t)stream));
+}
+
+svdq_status svdq_quantize_act(int precision, int group_size, int rank, int64_t M, int64_t K,
+                              const void* x, const void* smooth, const void* l1t,
+                              float act_global_scale, void* act_codes, void* act_scales,
+                              float* xl1, void* stream) {
+  return quantize_act(precision, group_size, rank, M, K, x, smooth, l1t, act_global_scale, act_codes, act_scales,
+                      xl1, stream, nullptr, 0);
+}
+
+svdq_status svdq_quantize_act_ws(int precision, int group_size, int rank, int64_t M, int64_t K,
+                                 const void* x, const void* smooth, const void* l1t,
+                                 float act_global_scale, void* act_codes, void* act_scales,
+                                 float* xl1, void* work, int64_t work_bytes, void* stream) {
+  return quantize_act(precision, group_size, rank, M, K, x, smooth, l1t, act_global_scale, act_codes, act_scales,
+                      xl1, stream, work, work_bytes);
 }
 
 static svdq_status gemm_common(int precision, int group_size, int rank, int64_t M, int64_t N,

@@ -91,6 +91,38 @@ svdq_status svdq_quantize_act(int precision, int group_size, int rank, int64_t M
                               float* xl1, void* stream);
 
 /*
+ * svdq_quantize_act_ws -- svdq_quantize_act with the workspace of
+ * svdq_w4a4_gemm_ws (SVDQ_GEMM_WORK_BYTES, declared below): the same
+ * smoothing, quantization and fused down-projection (blog, "Background:
+ * SVDQuant and Nunchaku"), with the work of a call that has fewer 32-row
+ * blocks than the device has CUs spread evenly over all of them: the grid of
+ * (32-row block, 64-channel step) pairs is cut into equal contiguous ranges,
+ * one per workgroup, so a block can be shared by two or more workgroups.
+ * Codes and scales are those of svdq_quantize_act bit for bit.  The rows of
+ * a shared block get XL1 as the sum of the pieces' fp32 partial tiles, met
+ * in `work` and added in a fixed order by the last piece to finish, so their
+ * XL1 can differ from svdq_quantize_act's in the last bits (the same bits
+ * from call to call).  Where the split does not apply (ranks other than 16
+ * and 32, blocks >= CUs, K not a whole number of 256-channel rounds, or
+ * for K > 4096 of 2048-channel chunks), the call is svdq_quantize_act.
+ *
+ *   work        NULL (then exactly svdq_quantize_act; work_bytes must be 0), or
+ *               the workspace of svdq_w4a4_gemm_ws: at least
+ *               SVDQ_GEMM_WORK_BYTES bytes, 16-byte aligned, not overlapping
+ *               an input or output, zero-filled before its first use.  A call
+ *               leaves its counter words zero again (they sit apart from the
+ *               GEMM's), so one workspace serves the quantizer and the GEMMs of
+ *               one stream; calls that may run at the same time (other streams)
+ *               need workspaces of their own.
+ *   work_bytes  its size in bytes
+ *   the other arguments, limits and errors as for svdq_quantize_act
+ */
+svdq_status svdq_quantize_act_ws(int precision, int group_size, int rank, int64_t M, int64_t K,
+                                 const void* x, const void* smooth, const void* l1t,
+                                 float act_global_scale, void* act_codes, void* act_scales,
+                                 float* xl1, void* work, int64_t work_bytes, void* stream);
+
+/*
  * svdq_w4a4_gemm -- the 4-bit GEMM with per-group dequantization and the
  * low-rank up-projection and bias fused into its epilogue (blog, "Background:
  * SVDQuant and Nunchaku"):

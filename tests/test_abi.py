@@ -300,3 +300,19 @@ def test_qkv_workspace_validation(L):
     assert qkv_ws(work=64 * A + 4) == ALIGN
     assert qkv_ws(work=10 * A - 4096) == INVALID                  # overlaps norm_k
     assert qkv_ws(work=8 * A - 4096) == INVALID                   # overlaps y
+
+
+def test_quantize_workspace_validation(L):
+    def qws(work=64 * A, work_bytes=sq.GEMM_WORK_BYTES, M=256, codes=2 * A, x=A):
+        return L.svdq_quantize_act_ws(0, 64, 16, M, 512, x, None, 3 * A, 1.0, codes, 4 * A, 5 * A, work, work_bytes,
+                                      None)
+    assert qws() == UNSUPPORTED                                   # valid: reaches the arch check
+    assert qws(work=None, work_bytes=0) == UNSUPPORTED            # no workspace: the plain quantizer
+    assert qws(work=None, work_bytes=4096) == INVALID             # a size without a buffer
+    assert qws(work_bytes=sq.GEMM_WORK_BYTES - 1) == INVALID and b"SVDQ_GEMM_WORK_BYTES" in L.svdq_last_error()
+    assert qws(work=64 * A + 8) == ALIGN
+    assert qws(work=A - 4096) == INVALID                          # overlaps x
+    assert qws(work=2 * A - 4096) == INVALID                      # overlaps the codes
+    assert qws(codes=None) == INVALID                             # the plain quantizer's own checks still apply
+    L.svdq_test_set_arch_override(b"gfx950")
+    assert qws(M=0) == OK

@@ -61,15 +61,28 @@ QUANT = [(sq.SVDQ_INT4, 37, 320, 16), (sq.SVDQ_INT4, 4130, 2112, 32), (sq.SVDQ_I
          (sq.SVDQ_INT4, 21, 256, 64), (sq.SVDQ_NVFP4, 37, 320, 16), (sq.SVDQ_NVFP4, 4100, 1088, 32)]
 
 
-@pytest.mark.parametrize("prec,M,K,r", QUANT)
-def test_quantizer_guards(prec, M, K, r):
-    print(f"[guard] quantize prec {prec} {M}x{K} r{r}", flush=True)
+# the balanced split of svdq_quantize_act_ws (blocks shared by workgroups):
+# ragged last blocks, many-piece blocks, the chunked reciprocal table
+QUANT_WS = [(sq.SVDQ_INT4, 1000, 3072, 32), (sq.SVDQ_NVFP4, 33, 1024, 16), (sq.SVDQ_INT4, 200, 6144, 32),
+            (sq.SVDQ_NVFP4, 4100, 2048, 32)]
+_WORK = []
+
+
+def _work():
+    if not _WORK:
+        _WORK.append(sq.gemm_workspace())
+    return _WORK[0]
+
+
+@pytest.mark.parametrize("prec,M,K,r,ws", [q + (False,) for q in QUANT] + [q + (True,) for q in QUANT_WS])
+def test_quantizer_guards(prec, M, K, r, ws):
+    print(f"[guard] quantize prec {prec} {M}x{K} r{r} workspace {ws}", flush=True)
     d = synth.svdq_layer(50 + M, M, 128, K, r, prec, 0.02, 30.0)
     G = sq.GROUP[prec]
     out = (Guarded((M, K // 2), torch.uint8), Guarded((M, K // G), sdt(prec)),
            Guarded((M, r), torch.float32) if r else None)
     sq.quantize_act(prec, b16(d["x"]), b16(d["lam"]), b16(d["l1t"]) if r else None, d["alpha_a"],
-                    out=(out[0].t, out[1].t, out[2].t if r else None))
+                    out=(out[0].t, out[1].t, out[2].t if r else None), workspace=_work() if ws else None)
     torch.cuda.synchronize()
     for g in out:
         assert g is None or g.intact(), "a quantizer output's guard bytes were overwritten"

@@ -1,6 +1,7 @@
 """Parity of every svdq workload at its full size, through exactly the entry
-points and launch configurations the benchmark runs (svdq_quantize_act, then
-svdq_w4a4_gemm_ws with a workspace and the library's default kernel choice),
+points and launch configurations the benchmark runs (svdq_quantize_act_ws,
+then svdq_w4a4_gemm_ws, sharing one workspace, with the library's default
+kernel choice),
 on each workload's own seeded inputs:
 
   svdq_int4_256x512x512_r16               (also forced onto the one-copy GEMM instance)
@@ -97,9 +98,11 @@ class Run:
                         bias=b16(d["bias"]))
         g = self.gpu
         print(f"[workload] {name}: quantize + GEMM on the GPU", flush=True)
-        g["codes"], g["scales"], g["xl1"] = sq.quantize_act(prec, g["x"], g["lam"], g["l1t"], d["alpha_a"])
+        work = sq.gemm_workspace()
+        g["codes"], g["scales"], g["xl1"] = sq.quantize_act(prec, g["x"], g["lam"], g["l1t"], d["alpha_a"],
+                                                            workspace=work)
         g["y"] = sq.w4a4_gemm(prec, g["codes"], g["scales"], g["wc"], g["ws"], g["xl1"], g["l2t"], g["bias"],
-                              d["alpha_a"], d["alpha_w"], workspace=sq.gemm_workspace())
+                              d["alpha_a"], d["alpha_w"], workspace=work)
         torch.cuda.synchronize()
         self.codes, self.scales = host(g["codes"]), host(g["scales"])
         self.xl1 = None if g["xl1"] is None else g["xl1"].cpu().numpy()
