@@ -660,9 +660,12 @@ static hipError_t launch_dma(const QuantArgs& a, int blocks, const QuantSplit& s
 
 // The balanced split of svdq_quantize_act_ws: ranges of L steps, L the even
 // share of the CUs rounded up to whole rounds (whole 2048-channel chunks of
-// the reciprocal table when K > 2 KC), used when L is below the steps of one
-// block (fewer blocks than CUs) and the blocks' steps are whole such units.
-// Returns false (sp untouched) where it does not apply.
+// the reciprocal table when K > 2 KC), used when the blocks' steps are whole
+// such units and the split saves at least eight of a block's rounds (32
+// steps): it costs a few rounds' time in the exchange of the shared blocks'
+// XL1 and in the larger number of workgroups copying at once (measured by
+// kernel trace on a 4608 x 3072 input, where it saves five: 14.9 us against
+// 13.8 us unsplit).  Returns false (sp untouched) where it does not apply.
 static bool balanced_split(const QuantArgs& a, QuantSplit& sp, int& blocks) {
   if (!a.work || a.M <= 0) return false;
   const int nsteps = (int)(a.K >> 6);
@@ -672,7 +675,7 @@ static bool balanced_split(const QuantArgs& a, QuantSplit& sp, int& blocks) {
   const int cus = device_cu_count();
   long long L = (T + cus - 1) / cus;
   L = (L + unit - 1) / unit * unit;
-  if (L >= nsteps) return false;
+  if (nsteps - L < 32) return false;
   const long long G = (T + L - 1) / L;
   if (G > kQuantMaxGroups) return false;
   sp.L = (int)L;

@@ -102,9 +102,10 @@ svdq_status svdq_quantize_act(int precision, int group_size, int rank, int64_t M
  * a shared block get XL1 as the sum of the pieces' fp32 partial tiles, met
  * in `work` and added in a fixed order by the last piece to finish, so their
  * XL1 can differ from svdq_quantize_act's in the last bits (the same bits
- * from call to call).  Where the split does not apply (ranks other than 16
- * and 32, blocks >= CUs, K not a whole number of 256-channel rounds, or
- * for K > 4096 of 2048-channel chunks), the call is svdq_quantize_act.
+ * from call to call).  The split applies to ranks 16 and 32 where K is a
+ * whole number of 256-channel rounds (of 2048-channel chunks for K > 4096)
+ * and it shortens each workgroup's share by at least 2048 channels of a
+ * block (fewer blocks than CUs); elsewhere the call is svdq_quantize_act.
  *
  *   work        NULL (then exactly svdq_quantize_act; work_bytes must be 0), or
  *               the workspace of svdq_w4a4_gemm_ws: at least

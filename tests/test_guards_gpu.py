@@ -63,8 +63,8 @@ QUANT = [(sq.SVDQ_INT4, 37, 320, 16), (sq.SVDQ_INT4, 4130, 2112, 32), (sq.SVDQ_I
 
 # the balanced split of svdq_quantize_act_ws (blocks shared by workgroups):
 # ragged last blocks, many-piece blocks, the chunked reciprocal table
-QUANT_WS = [(sq.SVDQ_INT4, 1000, 3072, 32), (sq.SVDQ_NVFP4, 33, 1024, 16), (sq.SVDQ_INT4, 200, 6144, 32),
-            (sq.SVDQ_NVFP4, 4100, 2048, 32)]
+QUANT_WS = [(sq.SVDQ_INT4, 1000, 3072, 32), (sq.SVDQ_NVFP4, 2000, 3072, 32), (sq.SVDQ_INT4, 200, 6144, 32),
+            (sq.SVDQ_INT4, 3990, 4096, 32)]
 _WORK = []
 
 

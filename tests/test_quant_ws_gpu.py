@@ -25,14 +25,17 @@ pytestmark = pytest.mark.gpu
 
 XL1_TOL = 1e-4
 
-# (precision, M, K, rank): balanced with two-piece blocks (the DiT QKV input),
-# many-piece blocks, ragged last blocks, the chunked table (6144, 12288), and
-# fallbacks (K = 4608: 72 steps are not whole 2048-channel chunks; M = 8192:
-# as many blocks as CUs)
-CASES = [(sq.SVDQ_INT4, 4608, 3072, 32), (sq.SVDQ_NVFP4, 4608, 3072, 32), (sq.SVDQ_INT4, 1000, 3072, 32),
-         (sq.SVDQ_NVFP4, 33, 1024, 16), (sq.SVDQ_INT4, 200, 6144, 32), (sq.SVDQ_NVFP4, 4100, 2048, 32),
-         (sq.SVDQ_INT4, 4608, 12288, 32), (sq.SVDQ_INT4, 70, 4608, 32), (sq.SVDQ_INT4, 8192, 1024, 16),
-         (sq.SVDQ_INT4, 1, 256, 16)]
+# (precision, M, K, rank): split with two-piece blocks (3990 x 4096 with a
+# ragged last block; the MLP-down input 4608 x 12288 with the chunked
+# reciprocal table), many-piece blocks (1000 x 3072, 2000 x 3072 nvfp4 and
+# rank 16, 200 x 6144 chunked), and the cases where the split does not apply
+# and the call is the plain one (the QKV input 4608 x 3072: it would save
+# fewer than eight rounds; K = 4608: 72 steps are not whole 2048-channel
+# chunks; M = 8192: as many blocks as CUs; tiny calls)
+CASES = [(sq.SVDQ_INT4, 3990, 4096, 32), (sq.SVDQ_INT4, 4608, 12288, 32), (sq.SVDQ_INT4, 1000, 3072, 32),
+         (sq.SVDQ_NVFP4, 2000, 3072, 32), (sq.SVDQ_INT4, 2000, 3072, 16), (sq.SVDQ_INT4, 200, 6144, 32),
+         (sq.SVDQ_INT4, 4608, 3072, 32), (sq.SVDQ_NVFP4, 4608, 3072, 32), (sq.SVDQ_INT4, 70, 4608, 32),
+         (sq.SVDQ_INT4, 8192, 1024, 16), (sq.SVDQ_NVFP4, 33, 1024, 16), (sq.SVDQ_INT4, 1, 256, 16)]
 
 
 def b16(bits, dtype=torch.bfloat16):
