@@ -4,7 +4,7 @@ AWQ W4A16 linears can be traced whole by torch.compile (fullgraph=True).
 The pages say the quantized linear layers work under torch.compile ("Nunchaku
 Lite", section "torch.compile"; blog "Nunchaku 4-bit inference in Diffusers",
 "Benchmarks").  Here each library entry point becomes one opaque operator
-(`svdq::quantize_act`, `svdq::w4a4_gemm`, `svdq::w4a4_gemm_ws`,
+(`svdq::quantize_act`, `svdq::quantize_act_ws`, `svdq::w4a4_gemm`, `svdq::w4a4_gemm_ws`,
 `svdq::w4a4_gemm_qkv_norm_rope`, `svdq::w4a4_gemm_gelu_quant`, `svdq::awq_gemv`) with a fake
 (meta) implementation that only computes output shapes and dtypes, so the
 tracer never runs a kernel; the real implementation is the ctypes call into
@@ -16,8 +16,10 @@ layer tensors (as buffers) whose forward uses these operators; `SVDQMLP` is
 the DiT MLP with the fused up-projection ("Nunchaku Lite", "Fused kernels":
 the GELU-MLP fusion), three operators per call.  An SVDQLinear whose
 `workspace` attribute holds a workspace from `gemm_workspace()` (one may serve
-every layer that runs on the same stream) calls `svdq::w4a4_gemm_ws`, which
-runs the GEMM grid's last partial round of tiles as K slices.
+every layer that runs on the same stream) calls `svdq::quantize_act_ws` (a
+call with fewer 32-row blocks than CUs spread over all of them) and
+`svdq::w4a4_gemm_ws` (the GEMM grid's last partial round of tiles as K
+slices).
 """
 from __future__ import annotations
 
@@ -51,6 +53,32 @@ def _(x, smooth, l1t, precision, act_global_scale):
     return (x.new_empty((M, K // 2), dtype=torch.uint8),
             x.new_empty((M, K // GROUP[precision]), dtype=_SCALE_DTYPE[precision]),
             x.new_empty((M, r), dtype=torch.float32))
+
+
+@torch.library.custom_op("svdq::quantize_act_ws", mutates_args=("workspace",))
+def quantize_act_ws_op(x: Tensor, smooth: Optional[Tensor], l1t: Optional[Tensor], workspace: Tensor,
+                       precision: int, act_global_scale: float) -> Tuple[Tensor, Tensor, Tensor]:
+    """svdq_quantize_act_ws: the outputs of svdq::quantize_act; `workspace` (u8
+    [GEMM_WORK_BYTES], zero-filled once) is the one the stream's GEMMs use."""
+    codes, scales, xl1 = quantize_act(precision, x, smooth, l1t, act_global_scale, workspace=workspace)
+    if xl1 is None:
+        xl1 = x.new_empty((x.shape[0], 0), dtype=torch.float32)
+    return codes, scales, xl1
+
+
+@quantize_act_ws_op.register_fake
+def _(x, smooth, l1t, workspace, precision, act_global_scale):
+    M, K = x.shape
+    r = 0 if l1t is None else l1t.shape[0]
+    return (x.new_empty((M, K // 2), dtype=torch.uint8),
+            x.new_empty((M, K // GROUP[precision]), dtype=_SCALE_DTYPE[precision]),
+            x.new_empty((M, r), dtype=torch.float32))
+
+
+def _quant(x, smooth, l1t, precision, ags, workspace=None):
+    if workspace is None:
+        return torch.ops.svdq.quantize_act(x, smooth, l1t, precision, ags)
+    return torch.ops.svdq.quantize_act_ws(x, smooth, l1t, workspace, precision, ags)
 
 
 @torch.library.custom_op("svdq::w4a4_gemm", mutates_args=())
@@ -158,10 +186,10 @@ def svdq_linear(x: Tensor, smooth: Optional[Tensor], l1t: Optional[Tensor], w_co
                 act_global_scale: float = 1.0, w_global_scale: float = 1.0,
                 workspace: Optional[Tensor] = None) -> Tensor:
     """The SVDQuant linear as two traceable operators; x may have any leading shape.  With a
-    `workspace` (gemm_workspace()) the GEMM is svdq::w4a4_gemm_ws."""
+    `workspace` (gemm_workspace()) the operators are svdq::quantize_act_ws and svdq::w4a4_gemm_ws."""
     lead = x.shape[:-1]
     x2 = x.reshape(-1, x.shape[-1])
-    codes, scales, xl1 = torch.ops.svdq.quantize_act(x2, smooth, l1t, precision, act_global_scale)
+    codes, scales, xl1 = _quant(x2, smooth, l1t, precision, act_global_scale, workspace)
     y = _gemm(codes, scales, w_codes, w_scales, xl1, l2t, bias, precision, act_global_scale, w_global_scale,
               workspace)
     return y.reshape(*lead, w_codes.shape[0])
@@ -217,7 +245,7 @@ class SVDQMLP(torch.nn.Module):
         lead = x.shape[:-1]
         x2 = x.reshape(-1, x.shape[-1])
         up, down, p = self.up, self.down, self.precision
-        codes, scales, xl1 = torch.ops.svdq.quantize_act(x2, up.smooth, up.l1t, p, up.act_global_scale)
+        codes, scales, xl1 = _quant(x2, up.smooth, up.l1t, p, up.act_global_scale, up.workspace)
         hc, hs, hx = torch.ops.svdq.w4a4_gemm_gelu_quant(codes, scales, up.w_codes, up.w_scales, xl1, up.l2t,
                                                          up.bias, down.smooth, down.l1t, p, up.act_global_scale,
                                                          up.w_global_scale, down.act_global_scale)

@@ -60,6 +60,11 @@ def test_opcheck(prec):
     torch.library.opcheck(torch.ops.svdq.w4a4_gemm_ws.default,
                           (codes, scales, m.w_codes, m.w_scales, xl1, m.l2t, m.bias, sq.gemm_workspace(), prec,
                            d["alpha_a"], d["alpha_w"]))
+    # the balanced quantizer splits this one (1000 rows, 48 steps of a block, rank 32)
+    ds = synth.svdq_layer(34, 1000, 128, 3072, 32, prec, 0.01, 20.0)
+    torch.library.opcheck(torch.ops.svdq.quantize_act_ws.default,
+                          (_t(ds["x"], torch.bfloat16), _t(ds["lam"], torch.bfloat16), _t(ds["l1t"], torch.bfloat16),
+                           sq.gemm_workspace(), prec, ds["alpha_a"]))
     qd = synth.qkv_layer(33, 96, 2, 128, 256, 16, prec)
     qc, qs, qx = torch.ops.svdq.quantize_act(_t(qd["x"], torch.bfloat16), _t(qd["lam"], torch.bfloat16),
                                              _t(qd["l1t"], torch.bfloat16), prec, qd["alpha_a"])
@@ -185,6 +190,35 @@ def test_module_with_workspace(prec):
     assert n_diff <= 32 * 128 * 128
     rel = float((y_ws.float() - y_plain.float()).abs().max() / y_plain.float().abs().max())
     print(f"[ops] {n_diff} outputs differ from the layer without a workspace, max-abs-rel {rel:.1e}", flush=True)
+    assert rel <= 1e-2
+    torch._dynamo.reset()
+    compiled = torch.compile(m, fullgraph=True, backend="aot_eager")
+    for _ in range(2):
+        y_comp = compiled(x)
+        torch.cuda.synchronize()
+        assert torch.equal(y_comp.view(torch.int16), y_ws.view(torch.int16))
+    assert int(m.workspace[16 << 20:].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("prec", [sq.SVDQ_INT4, sq.SVDQ_NVFP4])
+def test_module_with_workspace_split_quantizer(prec):
+    # 1000 tokens (31 full 32-row blocks and a ragged one, fewer than the CUs):
+    # the quantizer splits each block over several workgroups.  Against the
+    # same layer without a workspace: codes and scales are the same, XL1 of
+    # the shared blocks differs in its last bits, so Y stays within the int4
+    # conversion noise; compiled equals eager bit for bit; counters zero.
+    print(f"[ops] SVDQLinear 1000 tokens with a workspace, prec {prec}", flush=True)
+    d = synth.svdq_layer(72, 1000, 1024, 3072, 32, prec, 0.005, 30.0)
+    m = _svdq_module(d)
+    x = _t(d["x"], torch.bfloat16)
+    y_plain = m(x)
+    m.workspace = ops.gemm_workspace()
+    y_ws = m(x)
+    torch.cuda.synchronize()
+    assert int(m.workspace[:16 << 20].count_nonzero()) > 0, "no partial tile written: no split ran"
+    assert int(m.workspace[16 << 20:].count_nonzero()) == 0
+    rel = float((y_ws.float() - y_plain.float()).abs().max() / y_plain.float().abs().max())
+    print(f"[ops] max-abs-rel against the layer without a workspace {rel:.1e}", flush=True)
     assert rel <= 1e-2
     torch._dynamo.reset()
     compiled = torch.compile(m, fullgraph=True, backend="aot_eager")

@@ -123,11 +123,22 @@ def test_fake_gemm_ws():
         assert (y.shape, y.dtype) == ((96, 384), torch.bfloat16)
 
 
+def test_fake_quantize_ws():
+    with FakeTensorMode():
+        x = torch.empty(96, 512, dtype=torch.bfloat16)
+        work = torch.empty(sq.GEMM_WORK_BYTES, dtype=torch.uint8)
+        for prec, sdt in ((sq.SVDQ_INT4, torch.float16), (sq.SVDQ_NVFP4, torch.uint8)):
+            c, s, xl1 = torch.ops.svdq.quantize_act_ws(x, None, torch.empty(32, 512, dtype=torch.bfloat16), work,
+                                                       prec, 1.0)
+            assert c.shape == (96, 256) and s.dtype == sdt and s.shape == (96, 512 // sq.GROUP[prec])
+            assert xl1.shape == (96, 32) and xl1.dtype == torch.float32
+
+
 def test_export_with_workspace():
-    # a layer given a workspace traces to quantize_act + w4a4_gemm_ws, the
+    # a layer given a workspace traces to quantize_act_ws + w4a4_gemm_ws, the
     # workspace a constant tensor of the graph
     m = ops.SVDQLinear(256, 384, rank=16)
     m.workspace = torch.zeros(sq.GEMM_WORK_BYTES, dtype=torch.uint8)
     ep = torch.export.export(m, (torch.zeros(2, 48, 256, dtype=torch.bfloat16),), strict=True)
     svdq_ops = [str(n.target) for n in ep.graph.nodes if n.op == "call_function" and "svdq" in str(n.target)]
-    assert svdq_ops == ["svdq.quantize_act.default", "svdq.w4a4_gemm_ws.default"]
+    assert svdq_ops == ["svdq.quantize_act_ws.default", "svdq.w4a4_gemm_ws.default"]
