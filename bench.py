@@ -1,12 +1,16 @@
 """Benchmark of the SVDQuant W4A4 linear + AWQ W4A16 GEMV hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-  1. svdq_quantize_act_ws on the DiT fused-QKV projection input X [4608, 3072]
+  1. the quantizer on the DiT fused-QKV projection input X [4608, 3072]
      (smoothing, int4 group-64 codes and scales, fused X.L1 with rank 32),
   2. svdq_w4a4_gemm_ws  against W [9216, 3072] (int4 group 64) with the fused
      low-rank up-projection and bias, Y bf16 [4608, 9216] (with its workspace:
      the grid's last partial round of tiles runs as K slices),
-  3. awq_w4a16_gemv     on the modulation projection x [2, 3072] x W [18432, 3072].
+  3. the AWQ GEMV on the modulation projection x [2, 3072] x W [18432, 3072].
+Steps 1 and 3 do not depend on each other and go out as one launch,
+svdq_quantize_act_awq_gemv (the GEMV's workgroups run on the CUs the
+quantizer's 144 workgroups leave idle), then step 2; --no-fuse launches the
+three separately (svdq_quantize_act_ws, svdq_w4a4_gemm_ws, awq_w4a16_gemv).
 Inputs are resident in HBM before timing starts; several copies of every input
 are cycled so that the 256 MB Infinity Cache cannot serve a step from the
 previous one.  `value` is whole-step throughput in tera-ops per second,
@@ -61,6 +65,8 @@ def parse():
     p.add_argument("--calls", type=int, default=20, help="timed calls per extra workload")
     p.add_argument("--no-extras", action="store_true", help="time only the step")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-fuse", action="store_true",
+                   help="launch the quantizer and the AWQ GEMV separately in the timed steps")
     p.add_argument("--cpu-rows", type=int, default=1152, help="rows of X in the oracle's timed sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of the benchmark, copy MIB MiB device-to-device a few times (the known-size "
@@ -170,11 +176,30 @@ def main():
     AY = torch.empty((2, 18432), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    def step(i, ev=None, gemm_ev=None):
-        # ev: events around all three kernels (component timing, untimed pass);
+    def step(i, ev=None, gemm_ev=None, fused=not args.no_fuse):
+        # ev: events around every launch (component timing, untimed passes);
         # gemm_ev: events around the GEMM only (the timed steps: each event
-        # record adds a small gap to the stream, so the timed steps carry two)
+        # record adds a small gap to the stream, so the timed steps carry two).
+        # fused: the quantizer and the AWQ GEMV (independent of each other) go
+        # out as one launch (svdq_quantize_act_awq_gemv), then the GEMM.
         c = i % C
+        a = i % A
+        if fused:
+            if ev is not None:
+                ev[0].record(stream)
+            sq.quantize_act_awq_gemv(sq.SVDQ_INT4, X[c], LAM, L1T, 1.0, AX, AWC[a], AWS[a], AWZ[a], ABIAS,
+                                     out=(CODES[c], SCALES[c], XL1[c]), awq_out=AY, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            if gemm_ev is not None:
+                gemm_ev[0].record(stream)
+            sq.w4a4_gemm(sq.SVDQ_INT4, CODES[c], SCALES[c], WC[c], WS[c], XL1[c], L2T, BIAS, out=Y[i % 2],
+                         stream=stream, workspace=WORK)
+            if gemm_ev is not None:
+                gemm_ev[1].record(stream)
+            if ev is not None:
+                ev[2].record(stream)
+            return
         if ev is not None:
             ev[0].record(stream)
         sq.quantize_act(sq.SVDQ_INT4, X[c], LAM, L1T, out=(CODES[c], SCALES[c], XL1[c]), stream=stream,
@@ -189,7 +214,6 @@ def main():
             ev[2].record(stream)
         if gemm_ev is not None:
             gemm_ev[1].record(stream)
-        a = i % A
         sq.awq_gemv(AX, AWC[a], AWS[a], AWZ[a], ABIAS, out=AY, stream=stream)
         if ev is not None:
             ev[3].record(stream)
@@ -215,15 +239,26 @@ def main():
     wall_s = time.perf_counter() - t0
     t_gemm = np.array([e[0].elapsed_time(e[1]) for e in gevs])
 
-    # component durations: a further untimed pass with events around every kernel
+    # component durations: further untimed passes with events around every
+    # launch, one with the three kernels launched separately, one fused
     nc = min(args.steps, 50)
+    base_i = settle_steps + args.warmup + args.steps
+    for i in range(5):  # the kernels of the other mode load on their first launch: keep that out
+        step(base_i + i, fused=args.no_fuse)
+    torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nc)]
     for i in range(nc):
-        step(settle_steps + args.warmup + args.steps + i, evs[i])
+        step(settle_steps + args.warmup + args.steps + i, evs[i], fused=False)
     torch.cuda.synchronize()
     t_quant = np.array([e[0].elapsed_time(e[1]) for e in evs])
     t_awq = np.array([e[2].elapsed_time(e[3]) for e in evs])
     t_step = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    fevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nc)]
+    for i in range(nc):
+        step(settle_steps + args.warmup + args.steps + nc + i, fevs[i], fused=True)
+    torch.cuda.synchronize()
+    t_fused = np.array([e[0].elapsed_time(e[1]) for e in fevs])
+    t_fstep = np.array([e[0].elapsed_time(e[2]) for e in fevs])
     ms_step = float(wall_s * 1e3 / args.steps)
 
     ops = 2.0 * M * N * K
@@ -242,6 +277,10 @@ def main():
         "awq_GBps": round(awq_bytes / (t_awq.mean() * 1e-3) / 1e9, 1),
         "awq_frac_hbm": round(awq_bytes / (t_awq.mean() * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "event_step_ms": round(float(t_step.mean()), 5),
+        "quantize_awq_fused_ms": round(float(t_fused.mean()), 5),
+        "event_step_fused_ms": round(float(t_fstep.mean()), 5),
+        "step_launches": ("quantize+awq fused (svdq_quantize_act_awq_gemv), gemm" if not args.no_fuse
+                          else "quantize, gemm, awq"),
     }
     if not args.no_extras:
         components.update(extras(args, torch, sq, synth, t, bf, f16, stream))

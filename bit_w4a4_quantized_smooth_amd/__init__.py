@@ -33,10 +33,10 @@ _STATUS = {0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARG", 2: "SVDQ_ERR_UNSUPPORTED",
 # SVDQ_GEMM_WORK_BYTES: size of svdq_w4a4_gemm_ws's workspace
 GEMM_WORK_BYTES = 16 * 1024 * 1024 + 4096
 
-EXPORTS = ["svdq_quantize_act", "svdq_quantize_act_ws", "svdq_w4a4_gemm", "svdq_w4a4_gemm_ws", "svdq_w4a4_gemm_qkv_norm_rope",
-           "svdq_w4a4_gemm_qkv_norm_rope_ws", "svdq_w4a4_gemm_gelu_quant",
-           "awq_w4a16_gemv", "svdq_calibrate_smooth", "svdq_lowrank_workspace_bytes", "svdq_lowrank_decompose",
-           "svdq_lowrank_decompose_noalloc",
+EXPORTS = ["svdq_quantize_act", "svdq_quantize_act_ws", "svdq_w4a4_gemm", "svdq_w4a4_gemm_ws",
+           "svdq_w4a4_gemm_qkv_norm_rope", "svdq_w4a4_gemm_qkv_norm_rope_ws", "svdq_w4a4_gemm_gelu_quant",
+           "awq_w4a16_gemv", "svdq_quantize_act_awq_gemv", "svdq_calibrate_smooth",
+           "svdq_lowrank_workspace_bytes", "svdq_lowrank_decompose", "svdq_lowrank_decompose_noalloc",
            "svdq_quantize_weight", "awq_quantize_weight",
            "svdq_w4a4_group_psums", "svdq_last_error", "svdq_abi_version", "svdq_test_set_arch_override",
            "svdq_test_set_no_ksplit"]
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.svdq_w4a4_gemm_gelu_quant.argtypes = [i32, i32, i32, i64, i64, i64, vp, vp, f32, vp, vp, f32, vp, vp,
                                                 vp, vp, vp, i32, f32, vp, vp, vp, vp]
         L.awq_w4a16_gemv.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        L.svdq_quantize_act_awq_gemv.argtypes = [i32, i32, i32, i64, i64, vp, vp, vp, f32, vp, vp, vp,
+                                                 i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.svdq_calibrate_smooth.argtypes = [i64, i64, i64, vp, vp, vp, vp]
         L.svdq_lowrank_workspace_bytes.argtypes = [i64, i64, i32, i32]
         L.svdq_lowrank_workspace_bytes.restype = i64
@@ -83,7 +85,8 @@ def lib() -> ctypes.CDLL:
         L.svdq_w4a4_group_psums.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp]
         for f in ("svdq_quantize_act", "svdq_quantize_act_ws", "svdq_w4a4_gemm", "svdq_w4a4_gemm_ws", "svdq_w4a4_gemm_qkv_norm_rope",
                   "svdq_w4a4_gemm_qkv_norm_rope_ws",
-                  "svdq_w4a4_gemm_gelu_quant", "awq_w4a16_gemv", "svdq_w4a4_group_psums", "svdq_calibrate_smooth",
+                  "svdq_w4a4_gemm_gelu_quant", "awq_w4a16_gemv", "svdq_quantize_act_awq_gemv",
+                  "svdq_w4a4_group_psums", "svdq_calibrate_smooth",
                   "svdq_lowrank_decompose", "svdq_lowrank_decompose_noalloc", "svdq_quantize_weight",
                   "awq_quantize_weight"):
             getattr(L, f).restype = i32
@@ -371,6 +374,37 @@ def awq_gemv(x, w_codes, w_scales, w_zeros, bias=None, out=None, stream=None, gr
     _check(lib().awq_w4a16_gemv(group_size, M, N, K, _ptr(x), _ptr(w_codes), _ptr(w_scales),
                                 _ptr(w_zeros), _ptr(bias), _ptr(y), _stream(stream)))
     return y
+
+
+def quantize_act_awq_gemv(precision: int, x, smooth, l1t, act_global_scale: float, awq_x, w_codes, w_scales,
+                          w_zeros, bias=None, out=None, awq_out=None, stream=None):
+    """svdq_quantize_act_awq_gemv: quantize_act(precision, x, smooth, l1t, act_global_scale)
+    and awq_gemv(awq_x, w_codes, w_scales, w_zeros, bias) in one launch where the shapes
+    allow it.  Returns ((codes, scales, xl1), y); `out` / `awq_out` may supply the
+    quantizer's triple and the AWQ output preallocated."""
+    M, K = _dims("quantize_act_awq_gemv", x, "x", 2)
+    G = GROUP.get(precision, 64)
+    r = 0 if l1t is None else _dims("quantize_act_awq_gemv", l1t, "l1t", 2)[0]
+    aM, aK = _dims("quantize_act_awq_gemv", awq_x, "awq_x", 2)
+    aN = _dims("quantize_act_awq_gemv", w_codes, "w_codes", 2)[0]
+    if out is None:
+        codes = torch.empty((M, K // 2), dtype=_U8, device=x.device)
+        scales = torch.empty((M, K // G), dtype=_scale_dtype(precision), device=x.device)
+        xl1 = torch.empty((M, r), dtype=_F32, device=x.device) if r else None
+    else:
+        codes, scales, xl1 = out
+    y = awq_out if awq_out is not None else torch.empty((aM, aN), dtype=_BF16, device=awq_x.device)
+    (_Args("quantize_act_awq_gemv").req("x", x, _BF16, (M, K)).req("smooth", smooth, _BF16, (K,), True)
+     .req("l1t", l1t, _BF16, (r, K), True).req("codes", codes, _U8, (M, K // 2))
+     .req("scales", scales, _scale_dtype(precision), (M, K // G)).req("xl1", xl1, _F32, (M, r), r == 0)
+     .req("awq_x", awq_x, _BF16, (aM, aK)).req("w_codes", w_codes, _U8, (aN, aK // 2))
+     .req("w_scales", w_scales, _F16, (aN, aK // 64)).req("w_zeros", w_zeros, _F16, (aN, aK // 64))
+     .req("bias", bias, _BF16, (aN,), True).req("y", y, _BF16, (aM, aN)).done())
+    _check(lib().svdq_quantize_act_awq_gemv(precision, G, r, M, K, _ptr(x), _ptr(smooth), _ptr(l1t),
+                                            float(act_global_scale), _ptr(codes), _ptr(scales), _ptr(xl1), 64,
+                                            aM, aN, aK, _ptr(awq_x), _ptr(w_codes), _ptr(w_scales),
+                                            _ptr(w_zeros), _ptr(bias), _ptr(y), _stream(stream)))
+    return (codes, scales, xl1), y
 
 
 def svdq_linear(precision: int, x, smooth, l1t, w_codes, w_scales, l2t, bias,

@@ -157,5 +157,10 @@ hipError_t launch_gemm_int4(const GemmArgs& a, hipStream_t st);
 void set_no_ksplit(int v);
 hipError_t launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st);
 hipError_t launch_awq(const AwqArgs& a, hipStream_t st);
+// The quantizer and an independent AWQ GEMV (either may be null): one fused
+// launch where both shapes allow it (quant_awq_fusable), else the two
+// launches in that order.
+bool quant_awq_fusable(const QuantArgs& q, const AwqArgs& w, int* sx);
+hipError_t launch_quant_awq(const QuantArgs* q, const AwqArgs* w, hipStream_t st);
 
 }  // namespace svdq

@@ -26,6 +26,7 @@
 
 #include <type_traits>
 
+#include "awq_small.h"
 #include "common.h"
 #include "launch.h"
 
@@ -272,11 +273,24 @@ __device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t res, uint8_t* dst,
 }
 }  // namespace dma
 
+// The kernel's LDS, one object so that a fused launch (quant_awq_kernel)
+// can hand the same space to another job's workgroups.
+template <int RB>
+struct DmaLds {
+  float rl[2][dma::KC];             // lambda reciprocals, two chunks
+  uint8_t lst[8][1024];             // the next chunk's lambda (bf16), waves 0-3
+  uint8_t xs[4][8][2048];           // X slices per ring slot and wave
+  uint8_t ls[4][4][RB * 2048];      // L1^T slices per ring slot and step lane
+  unsigned xflag;                   // arrival count read by the whole workgroup
+};
+
+// The body of quant_act_dma_kernel for workgroup `bid` (of a grid of the
+// kernel's own size), with its LDS in S.
 template <int PREC, int RB, bool CH, bool BAL>
-__global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
-    int M, int K, const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
+__device__ __forceinline__ void quant_dma_body(
+    DmaLds<RB>& S, int bid, int M, int K, const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
     const uint16_t* __restrict__ l1t, float alpha, uint8_t* __restrict__ codes,
-    void* __restrict__ scales, float* __restrict__ xl1, QuantSplit sp) {
+    void* __restrict__ scales, float* __restrict__ xl1, const QuantSplit& sp) {
   using namespace dma;
   static_assert(RB == 1 || RB == 2, "LDS holds L1^T slices of 16 or 32 ranks");
   constexpr int LSL = RB * 2048;    // bytes of one step's L1^T slice (16*RB rows x 128 B)
@@ -289,11 +303,17 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
   // in flight is everything issued after them.
   constexpr int kAfter = 2 * NDMA + 3 * NSTO;
   constexpr int kOut = 0x7FFFFFF0;  // offset past num_records: zeros / dropped, no memory access
-  __shared__ __align__(16) float rl[2][KC];                 // lambda reciprocals, two chunks
-  __shared__ __align__(16) uint8_t lst[8][1024];            // the next chunk's lambda (bf16), waves 0-3
-  __shared__ __align__(16) uint8_t xs0[8][2048], xs1[8][2048], xs2[8][2048], xs3[8][2048];  // X slices per wave
-  __shared__ __align__(16) uint8_t ls0[4][LSL], ls1[4][LSL], ls2[4][LSL], ls3[4][LSL];     // L1^T slices per step lane
-  __shared__ unsigned xflag;                                // arrival count read by the whole workgroup
+  float(&rl)[2][KC] = S.rl;
+  uint8_t(&lst)[8][1024] = S.lst;
+  uint8_t(*const xs0)[2048] = S.xs[0];
+  uint8_t(*const xs1)[2048] = S.xs[1];
+  uint8_t(*const xs2)[2048] = S.xs[2];
+  uint8_t(*const xs3)[2048] = S.xs[3];
+  uint8_t(*const ls0)[LSL] = S.ls[0];
+  uint8_t(*const ls1)[LSL] = S.ls[1];
+  uint8_t(*const ls2)[LSL] = S.ls[2];
+  uint8_t(*const ls3)[LSL] = S.ls[3];
+  unsigned& xflag = S.xflag;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -307,13 +327,13 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
   // two blocks.
   int nr, jb, pair0, st0;
   if constexpr (BAL) {
-    const int s0 = (int)blockIdx.x * sp.L;
+    const int s0 = bid * sp.L;
     pair0 = s0 / nsteps;
     st0 = s0 - pair0 * nsteps;
     nr = min(sp.L, sp.T - s0) >> 2;
     jb = (nsteps - st0) >> 2;
   } else {
-    pair0 = blockIdx.x;
+    pair0 = bid;
     st0 = 0;
     nr = (nsteps + 3) >> 2;
     jb = nr;
@@ -613,7 +633,7 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
     auto exchange = [&](int p, int seg) __attribute__((always_inline)) {
       const int first = (int)(((long long)p * nsteps) / sp.L);
       const int last = (int)(((long long)(p + 1) * nsteps - 1) / sp.L);
-      float* const mine = sp.part + (size_t)(2 * (int)blockIdx.x + seg) * TILE;
+      float* const mine = sp.part + (size_t)(2 * bid + seg) * TILE;
 #pragma unroll
       for (int k = 0; k < RB; ++k) __hip_atomic_store(mine + tid + NT * k, sums[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -632,7 +652,7 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
         const float* src = sp.part + (size_t)slot * TILE;
 #pragma unroll
         for (int k = 0; k < RB; ++k)
-          tot[k] += w == (int)blockIdx.x ? sums[k]
+          tot[k] += w == bid ? sums[k]
                                          : __hip_atomic_load(src + tid + NT * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       write_rows(p * 32, tot);
@@ -648,6 +668,15 @@ __global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
       exchange(pair0 + 1, 1);
     }
   }
+}
+
+template <int PREC, int RB, bool CH, bool BAL>
+__global__ __launch_bounds__(dma::NT) void quant_act_dma_kernel(
+    int M, int K, const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
+    const uint16_t* __restrict__ l1t, float alpha, uint8_t* __restrict__ codes,
+    void* __restrict__ scales, float* __restrict__ xl1, QuantSplit sp) {
+  __shared__ __align__(16) DmaLds<RB> S;
+  quant_dma_body<PREC, RB, CH, BAL>(S, (int)blockIdx.x, M, K, x, lam, l1t, alpha, codes, scales, xl1, sp);
 }
 
 template <int PREC, int RB, bool CH, bool BAL>
@@ -740,6 +769,92 @@ static hipError_t dispatch_rank(const QuantArgs& a, hipStream_t st) {
 
 hipError_t launch_quantize_act(const QuantArgs& a, hipStream_t st) {
   return a.precision == 0 ? dispatch_rank<0>(a, st) : dispatch_rank<1>(a, st);
+}
+
+// One launch of two independent jobs (svdq_quantize_act_awq_gemv): workgroups
+// [0, qblocks) run the LDS-staged quantizer exactly as quant_act_dma_kernel
+// (unsplit), the others the small-M AWQ GEMV with eight waves (awq_gemv_body,
+// 32 weight rows per workgroup) in the same LDS.  On a DiT-sized call the
+// quantizer's 32-row workgroups hold one CU each and leave the rest idle (144
+// of 256 CUs at 4608 rows) for ~15 us; the GEMV's workgroups, dispatched after
+// them, stream the 4-bit weights there meanwhile, and its own launch, ramp
+// and tail are gone.  Each job computes what its own launch computes.
+template <int PREC, int RB, int MR, int SX>
+__global__ __launch_bounds__(dma::NT) void quant_awq_kernel(
+    int qblocks, int M, int K, const uint16_t* __restrict__ x, const uint16_t* __restrict__ lam,
+    const uint16_t* __restrict__ l1t, float alpha, uint8_t* __restrict__ codes, void* __restrict__ scales,
+    float* __restrict__ xl1, int aM, int aN, int aK, const uint16_t* __restrict__ ax,
+    const uint8_t* __restrict__ wc, const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wz,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ ay) {
+  static_assert(dma::NT == 64 * 8, "the GEMV's workgroups take the quantizer's eight waves");
+  __shared__ __align__(16) DmaLds<RB> S;
+  const int b = (int)blockIdx.x;
+  if (b < qblocks) {
+    const QuantSplit none{0, 0, nullptr, nullptr};
+    quant_dma_body<PREC, RB, false, false>(S, b, M, K, x, lam, l1t, alpha, codes, scales, xl1, none);
+  } else {
+    awq_gemv_body<MR, SX, 8>((uint4*)&S, b - qblocks, aM, aN, aK, ax, wc, ws, wz, bias, ay);
+  }
+}
+
+namespace {
+// The fused launch applies where each job would take that kernel on its own
+// launch: the quantizer's LDS-staged kernel with one reciprocal table and no
+// split (ranks 16 and 32, more 16-row blocks than CUs, K <= 4096), and the
+// small-M GEMV (M <= 4, K % 512 == 0, K <= 8192) with eight-wave workgroups
+// (N % 32 == 0) whose LDS fits the quantizer's.
+template <int PREC, int RB, int MR>
+hipError_t launch_quant_awq_sx(const QuantArgs& q, const AwqArgs& w, int sx, hipStream_t st) {
+  typedef void (*F)(int, int, int, const uint16_t*, const uint16_t*, const uint16_t*, float, uint8_t*, void*, float*,
+                    int, int, int, const uint16_t*, const uint8_t*, const uint16_t*, const uint16_t*,
+                    const uint16_t*, uint16_t*);
+  static const F table[4] = {quant_awq_kernel<PREC, RB, MR, 1>, quant_awq_kernel<PREC, RB, MR, 2>,
+                             quant_awq_kernel<PREC, RB, MR, 4>, quant_awq_kernel<PREC, RB, MR, 8>};
+  const int si = sx <= 1 ? 0 : sx <= 2 ? 1 : sx <= 4 ? 2 : 3;
+  const int qblocks = (int)((q.M + 31) / 32);
+  const int ablocks = (int)(w.N / 32);
+  hipLaunchKernelGGL(table[si], dim3(qblocks + ablocks), dim3(dma::NT), 0, st, qblocks, (int)q.M, (int)q.K,
+                     (const uint16_t*)q.x, (const uint16_t*)q.smooth, (const uint16_t*)q.l1t, q.alpha,
+                     (uint8_t*)q.codes, q.scales, q.xl1, (int)w.M, (int)w.N, (int)w.K, (const uint16_t*)w.x,
+                     (const uint8_t*)w.w_codes, (const uint16_t*)w.w_scales, (const uint16_t*)w.w_zeros,
+                     (const uint16_t*)w.bias, (uint16_t*)w.y);
+  return hipGetLastError();
+}
+
+template <int PREC, int RB>
+hipError_t launch_quant_awq_mr(const QuantArgs& q, const AwqArgs& w, int sx, hipStream_t st) {
+  return w.M <= 1 ? launch_quant_awq_sx<PREC, RB, 1>(q, w, sx, st)
+       : w.M <= 2 ? launch_quant_awq_sx<PREC, RB, 2>(q, w, sx, st)
+                  : launch_quant_awq_sx<PREC, RB, 4>(q, w, sx, st);
+}
+}  // namespace
+
+bool quant_awq_fusable(const QuantArgs& q, const AwqArgs& w, int* sx) {
+  if (q.M <= 0 || w.M <= 0) return false;
+  if (!(q.rank == 16 || q.rank == 32) || (q.M + 15) / 16 <= device_cu_count() || q.K > 2 * dma::KC) return false;
+  if (w.M > 4 || w.K % 512 != 0 || w.K / 512 > AWQ_TBMAX || w.N % 32 != 0) return false;
+  const int MR = w.M <= 1 ? 1 : w.M <= 2 ? 2 : 4;
+  const AwqLds L = awq_lds((int)w.K, MR, 32);
+  const int items = (L.nx + dma::NT - 1) / dma::NT;  // x staging items per thread
+  const size_t lds = q.rank == 16 ? sizeof(DmaLds<1>) : sizeof(DmaLds<2>);
+  if ((size_t)L.total > lds || items > 8) return false;
+  *sx = items;
+  return true;
+}
+
+hipError_t launch_quant_awq(const QuantArgs* q, const AwqArgs* w, hipStream_t st) {
+  int sx = 0;
+  if (q && w && quant_awq_fusable(*q, *w, &sx)) {
+    const bool r16 = q->rank == 16;
+    if (q->precision == 0)
+      return r16 ? launch_quant_awq_mr<0, 1>(*q, *w, sx, st) : launch_quant_awq_mr<0, 2>(*q, *w, sx, st);
+    return r16 ? launch_quant_awq_mr<1, 1>(*q, *w, sx, st) : launch_quant_awq_mr<1, 2>(*q, *w, sx, st);
+  }
+  if (q) {
+    const hipError_t e = launch_quantize_act(*q, st);
+    if (e != hipSuccess) return e;
+  }
+  return w ? launch_awq(*w, st) : hipSuccess;
 }
 
 }  // namespace svdq

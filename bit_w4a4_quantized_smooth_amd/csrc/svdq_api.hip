@@ -121,9 +121,12 @@ void svdq_test_set_arch_override(const char* arch) {
 
 void svdq_test_set_no_ksplit(int on) { svdq::set_no_ksplit(on); }
 
+// Validates a quantizer call; launches it, or with `prep` only fills *prep
+// (left untouched for an empty call).
 static svdq_status quantize_act(int precision, int group_size, int rank, int64_t M, int64_t K, const void* x,
                                 const void* smooth, const void* l1t, float act_global_scale, void* act_codes,
-                                void* act_scales, float* xl1, void* stream, void* work, int64_t work_bytes) {
+                                void* act_scales, float* xl1, void* stream, void* work, int64_t work_bytes,
+                                svdq::QuantArgs* prep = nullptr) {
   svdq_status s;
   if ((s = check_precision(precision, group_size)) != SVDQ_OK) return s;
   if (!valid_rank(rank)) return fail(SVDQ_ERR_UNSUPPORTED, "rank %d not in {0, 16, ..., 128}", rank);
@@ -161,10 +164,13 @@ static svdq_status quantize_act(int precision, int group_size, int rank, int64_t
   } else if (work_bytes != 0) {
     return fail(SVDQ_ERR_INVALID_ARG, "work_bytes=%lld given without work", (long long)work_bytes);
   }
-  if ((s = check_arch()) != SVDQ_OK) return s;
-  if (M == 0) return ok();
-  if ((s = check_sticky()) != SVDQ_OK) return s;
   svdq::QuantArgs a{precision, rank, M, K, x, smooth, l1t, act_global_scale, act_codes, act_scales, xl1, work};
+  if (prep) {  // the caller checks the device once for both of its jobs
+    *prep = a;
+    return ok();
+  }
+  if ((s = check_arch()) != SVDQ_OK) return s;
+  if ((s = check_sticky()) != SVDQ_OK) return s;
   return launched(svdq::launch_quantize_act(a, (hipStream_t)stream));
 }
 
@@ -573,9 +579,13 @@ svdq_status awq_quantize_weight(int group_size, int64_t N, int64_t K, const void
   return launched(svdq::launch_awq_quantize(N, K, w, codes, scales, zeros, (hipStream_t)stream));
 }
 
-svdq_status awq_w4a16_gemv(int group_size, int64_t M, int64_t N, int64_t K, const void* x,
-                           const void* w_codes, const void* w_scales, const void* w_zeros,
-                           const void* bias, void* y, void* stream) {
+}  // extern "C"
+
+// Validates an AWQ call; launches it, or with `prep` only fills *prep (left
+// untouched for an empty call).
+static svdq_status awq_gemv(int group_size, int64_t M, int64_t N, int64_t K, const void* x, const void* w_codes,
+                            const void* w_scales, const void* w_zeros, const void* bias, void* y, void* stream,
+                            svdq::AwqArgs* prep = nullptr) {
   if (group_size != 64)
     return fail(SVDQ_ERR_UNSUPPORTED, "awq_w4a16 supports int4 with group 64; got group %d", group_size);
   if (M < 0 || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
@@ -595,12 +605,65 @@ svdq_status awq_w4a16_gemv(int group_size, int64_t M, int64_t N, int64_t K, cons
   if (overlaps(y, ny, x, (size_t)M * K * 2) || overlaps(y, ny, w_codes, (size_t)N * K / 2) ||
       overlaps(y, ny, w_scales, ng) || overlaps(y, ny, w_zeros, ng) || overlaps(y, ny, bias, (size_t)N * 2))
     return fail(SVDQ_ERR_INVALID_ARG, "y must not overlap an input");
+  svdq::AwqArgs a{M, N, K, x, w_codes, w_scales, w_zeros, bias, y};
+  if (prep) {  // the caller checks the device once for both of its jobs
+    *prep = a;
+    return ok();
+  }
   svdq_status s;
   if ((s = check_arch()) != SVDQ_OK) return s;
-  if (M == 0) return ok();
   if ((s = check_sticky()) != SVDQ_OK) return s;
-  svdq::AwqArgs a{M, N, K, x, w_codes, w_scales, w_zeros, bias, y};
   return launched(svdq::launch_awq(a, (hipStream_t)stream));
+}
+
+extern "C" {
+
+svdq_status awq_w4a16_gemv(int group_size, int64_t M, int64_t N, int64_t K, const void* x,
+                           const void* w_codes, const void* w_scales, const void* w_zeros,
+                           const void* bias, void* y, void* stream) {
+  return awq_gemv(group_size, M, N, K, x, w_codes, w_scales, w_zeros, bias, y, stream);
+}
+
+svdq_status svdq_quantize_act_awq_gemv(int precision, int group_size, int rank, int64_t M, int64_t K,
+                                       const void* x, const void* smooth, const void* l1t,
+                                       float act_global_scale, void* act_codes, void* act_scales, float* xl1,
+                                       int awq_group_size, int64_t awq_M, int64_t awq_N, int64_t awq_K,
+                                       const void* awq_x, const void* w_codes, const void* w_scales,
+                                       const void* w_zeros, const void* bias, void* y, void* stream) {
+  svdq::QuantArgs q{};
+  svdq::AwqArgs w{};
+  q.M = -1;
+  w.M = -1;
+  svdq_status s;
+  if ((s = quantize_act(precision, group_size, rank, M, K, x, smooth, l1t, act_global_scale, act_codes, act_scales,
+                        xl1, stream, nullptr, 0, &q)) != SVDQ_OK)
+    return s;
+  if ((s = awq_gemv(awq_group_size, awq_M, awq_N, awq_K, awq_x, w_codes, w_scales, w_zeros, bias, y, stream, &w)) !=
+      SVDQ_OK)
+    return s;
+  const bool hq = q.M > 0, hw = w.M > 0;
+  if (hq && hw) {  // the two jobs must not touch each other's outputs
+    const size_t nc = (size_t)M * K / 2, nl = (size_t)M * rank * 4;
+    const size_t ns = precision == SVDQ_INT4 ? (size_t)M * (K / 64) * 2 : (size_t)M * (K / 16);
+    const size_t ny = (size_t)awq_M * awq_N * 2, ng = (size_t)awq_N * (awq_K / 64) * 2;
+    const void* qin[3] = {x, smooth, l1t};
+    const size_t qin_n[3] = {(size_t)M * K * 2, (size_t)K * 2, (size_t)rank * K * 2};
+    const void* qout[3] = {act_codes, act_scales, xl1};
+    const size_t qout_n[3] = {nc, ns, nl};
+    const void* win[5] = {awq_x, w_codes, w_scales, w_zeros, bias};
+    const size_t win_n[5] = {(size_t)awq_M * awq_K * 2, (size_t)awq_N * awq_K / 2, ng, ng, (size_t)awq_N * 2};
+    for (int i = 0; i < 3; ++i)
+      if (overlaps(y, ny, qin[i], qin_n[i]) || overlaps(y, ny, qout[i], qout_n[i]))
+        return fail(SVDQ_ERR_INVALID_ARG, "the AWQ output must not overlap the quantizer's buffers");
+    for (int i = 0; i < 3; ++i)
+      for (int j = 0; j < 5; ++j)
+        if (overlaps(qout[i], qout_n[i], win[j], win_n[j]))
+          return fail(SVDQ_ERR_INVALID_ARG, "the quantizer's outputs must not overlap the AWQ inputs");
+  }
+  if ((s = check_arch()) != SVDQ_OK) return s;
+  if (!hq && !hw) return ok();
+  if ((s = check_sticky()) != SVDQ_OK) return s;
+  return launched(svdq::launch_quant_awq(hq ? &q : nullptr, hw ? &w : nullptr, (hipStream_t)stream));
 }
 
 }  // extern "C"

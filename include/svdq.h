@@ -293,6 +293,37 @@ svdq_status awq_w4a16_gemv(int group_size, int64_t M, int64_t N, int64_t K, cons
                            const void* w_codes, const void* w_scales, const void* w_zeros,
                            const void* bias, void* y, void* stream);
 
+/*
+ * svdq_quantize_act_awq_gemv -- svdq_quantize_act and an independent
+ * awq_w4a16_gemv in one launch where the shapes allow it: the smoothing,
+ * quantization and fused down-projection of one layer's activations (blog,
+ * "Background: SVDQuant and Nunchaku") beside a memory-bound AWQ projection
+ * (blog, "Introducing Nunchaku Lite": the modulation projections are
+ * weight-only), for a step that has both at hand, e.g. a DiT block's
+ * attention input and a later block's modulation, which depends only on the
+ * timestep embedding.  The quantizer of a DiT-sized call holds a part of the
+ * CUs (one 32-row workgroup each); the GEMV's workgroups run on the others
+ * meanwhile.  Every output is bit-identical to the two separate calls.
+ *
+ *   the first twelve arguments   as for svdq_quantize_act (no workspace)
+ *   awq_group_size .. y          as for awq_w4a16_gemv (awq_M, awq_N, awq_K,
+ *                                awq_x are its M, N, K, x)
+ * The AWQ output must not overlap any quantizer buffer, nor a quantizer
+ * output any AWQ input.  Either job may be empty (M == 0 / awq_M == 0).
+ * One launch when the quantizer runs its LDS-staged kernel unsplit (ranks 16
+ * and 32, more 16-row blocks than CUs, K <= 4096) and the GEMV its small-M
+ * kernel (awq_M <= 4, awq_K % 512 == 0, awq_K <= 8192, awq_N % 32 == 0);
+ * otherwise the two launches, quantizer first, on the same stream.  Limits
+ * and errors as for the two calls; nothing is enqueued unless both
+ * validate.
+ */
+svdq_status svdq_quantize_act_awq_gemv(int precision, int group_size, int rank, int64_t M, int64_t K,
+                                       const void* x, const void* smooth, const void* l1t,
+                                       float act_global_scale, void* act_codes, void* act_scales, float* xl1,
+                                       int awq_group_size, int64_t awq_M, int64_t awq_N, int64_t awq_K,
+                                       const void* awq_x, const void* w_codes, const void* w_scales,
+                                       const void* w_zeros, const void* bias, void* y, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Offline weight side (blog "Nunchaku 4-bit inference in Diffusers",
  * "Background: SVDQuant and Nunchaku": activation outliers move into the

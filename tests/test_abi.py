@@ -316,3 +316,17 @@ def test_quantize_workspace_validation(L):
     assert qws(codes=None) == INVALID                             # the plain quantizer's own checks still apply
     L.svdq_test_set_arch_override(b"gfx950")
     assert qws(M=0) == OK
+
+
+def test_quantize_awq_entry_validation(L):
+    def qa(codes=2 * A, y=9 * A, awq_x=5 * A, aM=2, rank=16, l1t=3 * A, xl1=4 * A, M=256, ag=64):
+        return L.svdq_quantize_act_awq_gemv(0, 64, rank, M, 512, A, None, l1t, 1.0, codes, 6 * A, xl1,
+                                            ag, aM, 512, 512, awq_x, 7 * A, 8 * A, 10 * A, None, y, None)
+    assert qa() == UNSUPPORTED                                    # valid: reaches the arch check
+    assert qa(ag=128) == UNSUPPORTED and b"group 64" in L.svdq_last_error()   # the AWQ call's own checks
+    assert qa(codes=None) == INVALID                              # the quantizer's own checks
+    assert qa(y=A) == INVALID and b"AWQ output" in L.svdq_last_error()        # y over the quantizer's x
+    assert qa(y=2 * A) == INVALID                                 # y over the codes
+    assert qa(awq_x=2 * A) == INVALID and b"AWQ inputs" in L.svdq_last_error()  # codes over the AWQ x
+    L.svdq_test_set_arch_override(b"gfx950")
+    assert qa(M=0, aM=0) == OK                                    # both jobs empty: nothing enqueued
