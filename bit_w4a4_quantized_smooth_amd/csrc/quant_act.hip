@@ -393,12 +393,15 @@ __device__ __forceinline__ void quant_dma_body(
     for (int i = 0; i < RB; ++i) copy16(lres, lb[sl] + 1024 * (RB * rbk + i), live ? (int)(ldo[i] + sb) : kOut);
   };
   // the NSTO stores of a round, issued also for steps past the end (dropped)
-  auto store = [&](bool live, int cb, int sbs, int st, u32 pk0, u32 pk1, u32 sbits) __attribute__((always_inline)) {
-    __builtin_amdgcn_raw_buffer_store_b64(u2v{pk0, pk1}, cres, live ? cb + 32 * st : kOut, 0, 0);
+  // (dead: the out-of-range offset of a dropped store; distinct ones keep the
+  // compiler from merging the prologue's dropped stores into one)
+  auto store = [&](bool live, int cb, int sbs, int st, u32 pk0, u32 pk1, u32 sbits, int dead = kOut)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_buffer_store_b64(u2v{pk0, pk1}, cres, live ? cb + 32 * st : dead, 0, 0);
     if constexpr (PREC == 0)
-      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)sbits, sres, live ? sbs + 2 * st : kOut, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)sbits, sres, live ? sbs + 2 * st : dead, 0, 0);
     else
-      __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sbits, sres, live ? sbs + 4 * st : kOut, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sbits, sres, live ? sbs + 4 * st : dead, 0, 0);
   };
   // lambda of a chunk: thread t < 256 loads channels 8t .. 8t+7 (16 bytes);
   // for the first chunk straight into registers, for the next ones by a copy
@@ -507,12 +510,21 @@ __device__ __forceinline__ void quant_dma_body(
     const int ch = 8 * tid;
     lv0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lamres, ch < K ? 2 * ch : kOut, 0, 0));
   }
+  // The round waits count memory instructions, so all three pairs of dropped
+  // stores must be emitted, each after its copies: they go to distinct
+  // out-of-range offsets (identical ones were merged into one pair, which left
+  // round 0's wait short of round 0's copies) and each group is fenced.
+  // tests/test_quant_asm.py checks the emitted order in the gfx950 assembly.
+  asm volatile("" ::: "memory");
   issue(0, xs0, ls0);
-  store(false, cbase, sbase, 0, 0u, 0u, 0u);
+  store(false, cbase, sbase, 0, 0u, 0u, 0u, kOut);
+  asm volatile("" ::: "memory");
   issue(1, xs1, ls1);
-  store(false, cbase, sbase, 0, 0u, 0u, 0u);
+  store(false, cbase, sbase, 0, 0u, 0u, 0u, kOut - 256);
+  asm volatile("" ::: "memory");
   issue(2, xs2, ls2);
-  store(false, cbase, sbase, 0, 0u, 0u, 0u);
+  store(false, cbase, sbase, 0, 0u, 0u, 0u, kOut - 512);
+  asm volatile("" ::: "memory");
   if constexpr (CH) {
     if (tid < KC / 8) lam_recip(&rl[0][8 * tid], lv0);
   } else {
