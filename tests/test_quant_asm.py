@@ -11,7 +11,10 @@ fused quantizer + GEMV kernel, that before the first barrier
 
   * every round's copies are followed by its two stores (three pairs), and
   * the wait in front of that barrier leaves in flight no more operations
-    than were issued after round 0's copies.
+    than were issued after round 0's copies;
+
+and that every later round (barrier to barrier) issues its copies (one more
+where the next reciprocal chunk is copied) and then exactly its two stores.
 
 CPU only (the compiler runs here; nothing is launched)."""
 import os
@@ -76,3 +79,26 @@ def test_ring_prologue_order(asm):
         after0 = len(ops) - ndma  # operations issued after round 0's copies
         waits = [x[1] for x in seq if isinstance(x, tuple)]
         assert waits and waits[-1] <= after0, (name, "round 0 wait", waits[-1], "after", after0)
+
+
+def test_ring_rounds_order(asm):
+    names = re.findall(r"^(_ZN4svdq(?:20quant_act_dma_kernel|16quant_awq_kernel)\S+):", asm, re.M)
+    for name in names:
+        i = asm.index(name + ":")
+        body = asm[i:asm.index(".Lfunc_end", i)].split("\n")
+        ndma = [x for x in prologue(body) if not isinstance(x, tuple)].index("S")
+        blocks, cur, seen = [], [], False
+        for line in body:
+            t = line.strip()
+            if t.startswith("buffer_load") and " lds" in t:
+                seen = True
+                cur.append("C")
+            elif t.startswith("buffer_store") and seen:
+                cur.append("S")
+            elif t.startswith("s_barrier") and seen:
+                blocks.append("".join(cur))
+                cur = []
+        rounds = [b for b in blocks[1:] if "C" in b]  # after the prologue, up to the epilogue
+        assert rounds, name
+        ok = {"C" * ndma + "SS", "C" * (ndma + 1) + "SS"}
+        assert all(b in ok for b in rounds), (name, sorted(set(rounds)))
