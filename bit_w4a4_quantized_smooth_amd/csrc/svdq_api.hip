@@ -660,8 +660,8 @@ svdq_status svdq_quantize_act_awq_gemv(int precision, int group_size, int rank, 
         if (overlaps(qout[i], qout_n[i], win[j], win_n[j]))
           return fail(SVDQ_ERR_INVALID_ARG, "the quantizer's outputs must not overlap the AWQ inputs");
   }
+  if (!hq && !hw) return ok();  // both empty: nothing to read or write (as for the two calls)
   if ((s = check_arch()) != SVDQ_OK) return s;
-  if (!hq && !hw) return ok();
   if ((s = check_sticky()) != SVDQ_OK) return s;
   return launched(svdq::launch_quant_awq(hq ? &q : nullptr, hw ? &w : nullptr, (hipStream_t)stream));
 }

@@ -328,5 +328,4 @@ def test_quantize_awq_entry_validation(L):
     assert qa(y=A) == INVALID and b"AWQ output" in L.svdq_last_error()        # y over the quantizer's x
     assert qa(y=2 * A) == INVALID                                 # y over the codes
     assert qa(awq_x=2 * A) == INVALID and b"AWQ inputs" in L.svdq_last_error()  # codes over the AWQ x
-    L.svdq_test_set_arch_override(b"gfx950")
     assert qa(M=0, aM=0) == OK                                    # both jobs empty: nothing enqueued
